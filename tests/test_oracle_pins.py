@@ -1,0 +1,416 @@
+"""Pins the fp64 oracle to facts that do not come from the oracle itself.
+
+Each pin is a function of the oracle's callables so that the mutation tests at
+the bottom can show that a plausible mistake (a dropped scale, a transposed
+operand, a lost term, a flipped sign convention) fails at least one pin.
+Sources: hand-worked fixtures and the pages' printed storage figures under
+tests/golden/, closed forms, scipy's Hadamard matrix, brute-force loops.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+class _Ad:
+    def __init__(self, S1, S2, alpha, beta, gamma):
+        self.S1, self.S2, self.alpha, self.beta, self.gamma = S1, S2, alpha, beta, gamma
+
+
+def _rand_layer(seed, N, R, M, ell, T, integer=False):
+    kind = "int3" if integer else "normal"
+    sc = "ones" if integer else "small_plus"
+    return synth.make_layer(N, R, M, ell, T, seed, sc, sc, sc, kind)
+
+
+# ----------------------------------------------------------------- pins ----
+
+def pin_hand_example(fwd, dw_fn):
+    """Hand-worked 2x2x3 example, one and two terms, and its dense dW."""
+    g = _load("tiny_hand.json")
+    S1, S2 = np.array(g["S1"]), np.array(g["S2"])
+    a, b, c = np.array(g["alpha"]), np.array(g["beta"]), np.array(g["gamma"])
+    x = np.array(g["x"])
+    ok = np.array_equal(fwd(x, S1, S2, a[:1], b[:1], c[:1]), np.array(g["y_term1"]))
+    ok &= np.array_equal(fwd(x, S1, S2, a, b, c), np.array(g["y_both_terms"]))
+    ok &= np.array_equal(dw_fn(S1, S2, a[:1], b[:1], c[:1]), np.array(g["delta_w_term1"]))
+    return bool(ok)
+
+
+def pin_hadamard4_fixture(fwd):
+    g = _load("hadamard4.json")
+    H = np.array(g["H4"])
+    y = fwd(np.array(g["x"]), H, H, np.array([g["alpha"]]), np.array([g["beta"]]),
+            np.array([g["gamma"]]))
+    return bool(np.array_equal(y, np.array(g["y"])))
+
+
+def pin_hadamard_closed_form(fwd, k=6, seed=1):
+    """S1 = H P, S2 = P^T H with H Sylvester-Hadamard (scipy) and P a random
+    permutation: S1 S2 = 2^k I, so with beta = 1, y = 2^k alpha*gamma*x."""
+    n = 2 ** k
+    rng = np.random.default_rng(seed)
+    H = scipy.linalg.hadamard(n).astype(np.int8)
+    P = np.eye(n, dtype=np.int8)[rng.permutation(n)]
+    S1 = (H @ P).astype(np.int8)
+    S2 = (P.T @ H).astype(np.int8)
+    x = rng.integers(-3, 4, size=(5, n)).astype(np.float64)
+    alpha = rng.integers(1, 4, size=(1, n)).astype(np.float64)
+    gamma = rng.integers(-2, 3, size=(1, n)).astype(np.float64)
+    beta = np.ones((1, n))
+    y = fwd(x, S1, S2, alpha, beta, gamma)
+    return bool(np.array_equal(y, n * alpha * gamma * x))
+
+
+def pin_all_ones(fwd, seed=2):
+    """S1 = 1, S2 = 1: y_n = alpha_n (sum_r beta_r)(sum_m gamma_m x_m)."""
+    rng = np.random.default_rng(seed)
+    N, R, M = 7, 5, 9
+    a, b, c = (rng.integers(1, 5, size=(1, d)).astype(float) for d in (N, R, M))
+    x = rng.integers(-3, 4, size=(3, M)).astype(float)
+    y = fwd(x, np.ones((N, R), np.int8), np.ones((R, M), np.int8), a, b, c)
+    want = a[0][None, :] * b.sum() * (x * c[0][None, :]).sum(axis=1)[:, None]
+    return bool(np.array_equal(y, want))
+
+
+def pin_rank_one(fwd, seed=3):
+    """R = 1: y = alpha * s1 * beta * (s2 . (gamma * x))."""
+    rng = np.random.default_rng(seed)
+    N, M = 6, 11
+    s1 = synth.make_signs(rng, N, 1)
+    s2 = synth.make_signs(rng, 1, M)
+    a = rng.integers(1, 4, size=(1, N)).astype(float)
+    b = np.array([[3.0]])
+    c = rng.integers(1, 4, size=(1, M)).astype(float)
+    x = rng.integers(-3, 4, size=(4, M)).astype(float)
+    inner = (x * c[0] * s2[0]).sum(axis=1)
+    want = a[0][None, :] * s1[:, 0][None, :] * 3.0 * inner[:, None]
+    return bool(np.array_equal(fwd(x, s1, s2, a, b, c), want))
+
+
+def pin_brute_force(fwd, seed=4):
+    """Explicit loops (no library routine) agree exactly on integer data,
+    including sizes that are not multiples of 32 and two terms."""
+    ok = True
+    for (N, R, M, ell, T) in [(5, 7, 33, 1, 3), (9, 3, 4, 2, 2), (1, 1, 1, 1, 1)]:
+        L = _rand_layer(seed, N, R, M, ell, T, integer=True)
+        rng = np.random.default_rng(seed)
+        a = rng.integers(-2, 3, size=(ell, N)).astype(float)
+        b = rng.integers(-2, 3, size=(ell, R)).astype(float)
+        c = rng.integers(-2, 3, size=(ell, M)).astype(float)
+        y = fwd(L.x, L.S1, L.S2, a, b, c)
+        ok &= np.array_equal(y, np.array(oracle.forward_loops(L.x, L.S1, L.S2, a, b, c)))
+    return bool(ok)
+
+
+def pin_dense(fwd, dw_fn, seed=5):
+    """Two-stage order ([DBF] inference) equals X dW^T with dW from the
+    [LoRDBA] equation; exact on integers, 1e-12 relative on fp16 data."""
+    Li = _rand_layer(seed, 24, 10, 40, 2, 6, integer=True)
+    rng = np.random.default_rng(seed)
+    a = rng.integers(-3, 4, size=(2, 24)).astype(float)
+    ok = np.array_equal(fwd(Li.x, Li.S1, Li.S2, a, Li.beta, Li.gamma),
+                        Li.x.astype(float) @ dw_fn(Li.S1, Li.S2, a, Li.beta, Li.gamma).T)
+    Lf = _rand_layer(seed + 1, 24, 10, 40, 2, 6)
+    y = fwd(Lf.x, Lf.S1, Lf.S2, Lf.alpha, Lf.beta, Lf.gamma)
+    yd = Lf.x.astype(float) @ dw_fn(Lf.S1, Lf.S2, Lf.alpha, Lf.beta, Lf.gamma).T
+    ok &= oracle.max_norm_error(y, yd) < 1e-12
+    return bool(ok)
+
+
+def pin_basis_probe(fwd, dw_fn, seed=6):
+    """X = I (T = M) returns dW^T, entry by entry a brute-force sum."""
+    L = _rand_layer(seed, 6, 4, 5, 1, 0, integer=True)
+    rng = np.random.default_rng(seed)
+    a = rng.integers(-3, 4, size=(1, 6)).astype(float)
+    b = rng.integers(-3, 4, size=(1, 4)).astype(float)
+    c = rng.integers(-3, 4, size=(1, 5)).astype(float)
+    y = fwd(np.eye(5), L.S1, L.S2, a, b, c)
+    bf = np.zeros((6, 5))
+    for n in range(6):
+        for m in range(5):
+            bf[n, m] = sum(a[0, n] * L.S1[n, r] * b[0, r] * L.S2[r, m] * c[0, m] for r in range(4))
+    return bool(np.array_equal(y, bf.T) and np.array_equal(dw_fn(L.S1, L.S2, a, b, c), bf))
+
+
+def pin_linearity(fwd, seed=7):
+    """Linear in x; the ell-term result is the sum of single-term results."""
+    L = _rand_layer(seed, 16, 8, 24, 3, 4, integer=True)
+    rng = np.random.default_rng(seed)
+    a = rng.integers(-3, 4, size=(3, 16)).astype(float)
+    b = rng.integers(-3, 4, size=(3, 8)).astype(float)
+    c = rng.integers(-3, 4, size=(3, 24)).astype(float)
+    x1 = L.x.astype(float)
+    x2 = rng.integers(-3, 4, size=x1.shape).astype(float)
+    lhs = fwd(2 * x1 - 3 * x2, L.S1, L.S2, a, b, c)
+    rhs = 2 * fwd(x1, L.S1, L.S2, a, b, c) - 3 * fwd(x2, L.S1, L.S2, a, b, c)
+    ok = np.array_equal(lhs, rhs)
+    per_term = sum(fwd(x1, L.S1, L.S2, a[i:i + 1], b[i:i + 1], c[i:i + 1]) for i in range(3))
+    ok &= np.array_equal(fwd(x1, L.S1, L.S2, a, b, c), per_term)
+    return bool(ok)
+
+
+def pin_gauges(fwd, seed=8):
+    """Sign flip of column r of S1 with row r of S2, a permutation of the R
+    channels, and a power of two moved between the scales leave y unchanged."""
+    L = _rand_layer(seed, 12, 9, 20, 2, 5, integer=True)
+    rng = np.random.default_rng(seed)
+    a = rng.integers(1, 4, size=(2, 12)).astype(float)
+    b = rng.integers(1, 4, size=(2, 9)).astype(float)
+    c = rng.integers(1, 4, size=(2, 20)).astype(float)
+    y0 = fwd(L.x, L.S1, L.S2, a, b, c)
+    S1f, S2f = L.S1.copy(), L.S2.copy()
+    flip = rng.random(9) < 0.5
+    S1f[:, flip] *= -1
+    S2f[flip, :] *= -1
+    ok = np.array_equal(fwd(L.x, S1f, S2f, a, b, c), y0)
+    p = rng.permutation(9)
+    ok &= np.array_equal(fwd(L.x, L.S1[:, p], L.S2[p, :], a, b[:, p], c), y0)
+    ok &= np.array_equal(fwd(L.x, L.S1, L.S2, a * 4, b / 4, c), y0)
+    ok &= np.array_equal(fwd(L.x, L.S1, L.S2, a, b * 8, c / 8), y0)
+    return bool(ok)
+
+
+def pin_adjoint(fwd, fwd_t, seed=9):
+    """<g, dW x> = <dW^T g, x> in fp64."""
+    L = _rand_layer(seed, 33, 17, 41, 2, 3)
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((3, 33))
+    lhs = np.sum(g * fwd(L.x, L.S1, L.S2, L.alpha, L.beta, L.gamma))
+    rhs = np.sum(fwd_t(g, L.S1, L.S2, L.alpha, L.beta, L.gamma) * L.x.astype(float))
+    return abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def pin_sign_convention(sign_fn):
+    """sign(H) agrees with numpy's sign away from zero; zero (either sign)
+    and NaN give +1 (the reading for the undefined case)."""
+    rng = np.random.default_rng(10)
+    h = rng.standard_normal(1000)
+    h = h[h != 0]
+    ok = np.array_equal(sign_fn(h), np.sign(h).astype(np.int8))
+    ok &= np.array_equal(sign_fn(np.array([0.0, -0.0, np.nan])), np.array([1, 1, 1], np.int8))
+    ok &= sign_fn(np.array([-1e-30]))[0] == -1
+    return bool(ok)
+
+
+# ------------------------------------------------------ the pins pass ------
+
+def test_hand_example():
+    assert pin_hand_example(oracle.forward, oracle.delta_w)
+
+
+def test_hand_example_loops():
+    g = _load("tiny_hand.json")
+    y = oracle.forward_loops(g["x"], np.array(g["S1"]), np.array(g["S2"]), np.array(g["alpha"]),
+                             np.array(g["beta"]), np.array(g["gamma"]))
+    assert y == g["y_both_terms"]
+
+
+def test_hadamard4_fixture():
+    assert pin_hadamard4_fixture(oracle.forward)
+
+
+@pytest.mark.parametrize("k", [2, 5, 7])
+def test_hadamard_closed_form(k):
+    assert pin_hadamard_closed_form(oracle.forward, k=k)
+
+
+def test_all_ones():
+    assert pin_all_ones(oracle.forward)
+
+
+def test_rank_one():
+    assert pin_rank_one(oracle.forward)
+
+
+def test_brute_force():
+    assert pin_brute_force(oracle.forward)
+
+
+def test_dense():
+    assert pin_dense(oracle.forward, oracle.delta_w)
+
+
+def test_basis_probe():
+    assert pin_basis_probe(oracle.forward, oracle.delta_w)
+
+
+def test_linearity():
+    assert pin_linearity(oracle.forward)
+
+
+def test_gauges():
+    assert pin_gauges(oracle.forward)
+
+
+def test_adjoint():
+    assert pin_adjoint(oracle.forward, oracle.forward_transposed)
+
+
+def test_sign_convention():
+    assert pin_sign_convention(oracle.sign_of_latent)
+
+
+def test_forward_rows_matches_full():
+    L = _rand_layer(11, 40, 20, 70, 2, 5)
+    y = oracle.forward(L.x, L.S1, L.S2, L.alpha, L.beta, L.gamma)
+    idx = np.array([0, 3, 39, 17])
+    ys = oracle.forward_rows(L.x[[1, 4]], L.S1, L.S2, L.alpha, L.beta, L.gamma, idx)
+    assert np.array_equal(ys, y[[1, 4]][:, idx])
+
+
+def test_multi_adapter_routing():
+    """Each token's row equals the single-adapter result of its adapter; ids
+    outside [0, A) give 0, or keep the base output when one is given."""
+    B = synth.make_multi_adapter(num_adapters=3, N=10, R=4, M=12, ell=2, T=9, seed=12, sort=False)
+    ids = B.ids.copy()
+    ids[2] = -1
+    ids[5] = 3
+    y = oracle.forward_multi_adapter(B.x, ids, B.adapters)
+    for t in range(9):
+        if 0 <= ids[t] < 3:
+            ad = B.adapters[ids[t]]
+            want = oracle.forward(B.x[t:t + 1], ad.S1, ad.S2, ad.alpha, ad.beta, ad.gamma)[0]
+            assert np.array_equal(y[t], want)
+        else:
+            assert np.all(y[t] == 0)
+    base = np.arange(90, dtype=float).reshape(9, 10)
+    y2 = oracle.forward_multi_adapter(B.x, ids, B.adapters, y_old=base)
+    assert np.array_equal(y2, y + base)
+
+
+def test_accumulate_adds_base():
+    L = _rand_layer(13, 8, 4, 8, 1, 3, integer=True)
+    base = np.full((3, 8), 5.0)
+    assert np.array_equal(oracle.forward(L.x, L.S1, L.S2, L.alpha, L.beta, L.gamma, y_old=base),
+                          oracle.forward(L.x, L.S1, L.S2, L.alpha, L.beta, L.gamma) + 5.0)
+
+
+def test_integer_bound_fits_fp32():
+    """Integer variant of the tiny layer: |u| <= 3M, |y| <= 3 M R < 2^24,
+    so fp32 accumulation is exact and |u| <= 2048 is exact in fp16."""
+    L = synth.make_config_layer(1, 4, integer=True)
+    y = oracle.forward(L.x, L.S1, L.S2, L.alpha, L.beta, L.gamma)
+    z = oracle.stage1(L.x, L.S2, L.beta[0], L.gamma[0])
+    assert np.max(np.abs(z)) <= 3 * L.M <= 2048
+    assert np.max(np.abs(y)) <= 3 * L.M * L.R < 2 ** 24
+    assert np.array_equal(y, np.round(y))
+
+
+def test_fp16_rne():
+    # 2049 is halfway between fp16 neighbours 2048 and 2050: ties to even.
+    assert oracle.fp16_rne(np.array([2049.0]))[0] == 2048.0
+    assert oracle.fp16_rne(np.array([2051.0]))[0] == 2052.0
+    assert np.isinf(oracle.fp16_rne(np.array([70000.0]))[0])
+
+
+# ---------------------------------------------- storage: the pages' figures --
+
+def test_storage_closed_form_and_claims():
+    c = _load("storage_claims.json")
+    N = M = 4096
+    # one bit per sign entry, fp16 scales
+    assert c["sign_bits_per_entry"]["value"] == 1 and c["scale_bits"]["value"] == 16
+    assert oracle.sign_bits(4096, 2048, 4096) == 2048 * 8192
+    assert oracle.scale_bytes(4096, 2048, 4096, 1) == 2 * (4096 + 2048 + 4096)
+    # about 1 and 2 bits per weight at the attention and MLP shapes
+    assert abs(oracle.bits_per_weight(4096, 2048, 4096) - 1.009765625) < 1e-12
+    assert abs(oracle.bits_per_weight(14336, 6368, 4096) - 117771776 / 58720256) < 1e-12
+    assert [round(oracle.bits_per_weight(14336, 6368, 4096))] == [2]
+    # >10x at equal rank holds from R = 27 on (N = M = 4096)
+    thr = c["compression_equal_rank_gt"]["value"]
+    assert oracle.compression_vs_fp16_lora(N, 26, M) < thr < oracle.compression_vs_fp16_lora(N, 27, M)
+    # the printed 10.6x: R = 16 gives 7.99x, R = 32 gives 10.65x (reading: rank mislabelled)
+    assert abs(oracle.compression_vs_fp16_lora(N, 16, M) - 2097152 / 262400) < 1e-12
+    r32 = oracle.compression_vs_fp16_lora(N, 32, M)
+    assert math.floor(r32 * 10) / 10 == c["footprint_reduction_rq2"]["value"]
+    assert abs(oracle.compression_vs_fp16_lora(N, 64, M) - 8388608 / 656384) < 1e-12
+    # at most 4 bits per factor entry from R = 6 on
+    per_entry = lambda R: 1 + 16 * (N + R + M) / (R * (N + M))  # noqa: E731
+    assert per_entry(5) > c["max_bits_per_weight"]["value"] >= per_entry(6)
+    # a fractional rate such as 1.5 bits/weight is reachable by choosing R
+    target = c["fractional_bits_example"]["value"]
+    R15 = min(range(1, 4096), key=lambda R: abs(oracle.bits_per_weight(N, R, M) - target))
+    assert abs(oracle.bits_per_weight(N, R15, M) - target) < 1e-3
+
+
+def test_storage_counts_exactly():
+    """Brute force: count bits of actual arrays of the stated types."""
+    L = _rand_layer(14, 30, 7, 50, 2, 1)
+    n_signs = L.S1.size + L.S2.size
+    n_scale_bytes = L.alpha.nbytes + L.beta.nbytes + L.gamma.nbytes
+    assert oracle.sign_bits(30, 7, 50) == n_signs
+    assert oracle.scale_bytes(30, 7, 50, 2) == n_scale_bytes
+
+
+# ---------------------------------------------------------- mutations ------
+# Each mutant is a plausible slip; at least one pin must reject it.
+
+def _mut_drop_beta(x, S1, S2, a, b, c, y_old=None):
+    return oracle.forward(x, S1, S2, a, np.ones_like(np.asarray(b, float)), c)
+
+
+def _mut_transpose_s2(x, S1, S2, a, b, c, y_old=None):
+    S2 = np.asarray(S2)
+    if S2.shape[0] == S2.shape[1]:
+        S2 = S2.T
+    else:  # same shape, wrong element placement
+        S2 = S2[::-1, ::-1]
+    return oracle.forward(x, S1, S2, a, b, c)
+
+
+def _mut_swap_alpha_gamma(x, S1, S2, a, b, c, y_old=None):
+    a, c = np.asarray(a, float), np.asarray(c, float)
+    if a.shape == c.shape:
+        a, c = c, a
+    else:
+        a = a[:, ::-1]
+    return oracle.forward(x, S1, S2, a, b, c)
+
+
+def _mut_first_term_only(x, S1, S2, a, b, c, y_old=None):
+    a, b, c = (np.atleast_2d(np.asarray(v, float)) for v in (a, b, c))
+    return oracle.forward(x, S1, S2, a[:1], b[:1], c[:1])
+
+
+def _mut_sign_flip(x, S1, S2, a, b, c, y_old=None):
+    return oracle.forward(x, -np.asarray(S1), S2, a, b, c)
+
+
+def _mut_term_index_shift(x, S1, S2, a, b, c, y_old=None):
+    a, b, c = (np.atleast_2d(np.asarray(v, float)) for v in (a, b, c))
+    return oracle.forward(x, S1, S2, a, np.roll(b, 1, axis=0), c)
+
+
+@pytest.mark.parametrize("mutant", [_mut_drop_beta, _mut_transpose_s2, _mut_swap_alpha_gamma,
+                                    _mut_first_term_only, _mut_sign_flip, _mut_term_index_shift])
+def test_pins_reject_mutants(mutant):
+    results = [
+        pin_hand_example(mutant, oracle.delta_w),
+        pin_hadamard4_fixture(mutant),
+        pin_hadamard_closed_form(mutant),
+        pin_all_ones(mutant),
+        pin_rank_one(mutant),
+        pin_brute_force(mutant),
+        pin_dense(mutant, oracle.delta_w),
+        pin_basis_probe(mutant, oracle.delta_w),
+        pin_linearity(mutant),
+    ]
+    assert not all(results)
+
+
+def test_pins_reject_sign_convention_mutant():
+    assert not pin_sign_convention(lambda h: np.where(np.asarray(h) <= 0, -1, 1).astype(np.int8))
