@@ -1,0 +1,196 @@
+"""Thin PyTorch-side binding of the C ABI (include/dbf.h).
+
+Argument marshalling only: tensors supply device pointers, strides and the
+current HIP stream; every step of the product runs in the HIP library.
+Function names follow the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import check, lib
+
+__all__ = [
+    "dbf_abi_version",
+    "dbf_status_string",
+    "dbf_packed_bytes",
+    "dbf_pack_signs",
+    "dbf_unpack_signs",
+    "dbf_workspace_bytes",
+    "dbf_forward",
+    "dbf_forward_multi_adapter",
+    "PackedLayer",
+    "pointer_table",
+]
+
+_DTYPE = {torch.int8: _lib.DBF_I8, torch.float16: _lib.DBF_F16, torch.float32: _lib.DBF_F32}
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _row_major(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit inner stride")
+    return t.stride(0)
+
+
+def dbf_abi_version() -> int:
+    return _lib.abi_version()
+
+
+def dbf_status_string(status: int) -> str:
+    return _lib.status_string(status)
+
+
+def dbf_packed_bytes(rows: int, cols: int) -> int:
+    return _lib.packed_bytes(rows, cols)
+
+
+def dbf_workspace_bytes(N: int, R: int, M: int, ell: int, T: int) -> int:
+    return _lib.workspace_bytes(N, R, M, ell, T)
+
+
+def dbf_pack_signs(src: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Pack sign(src) (rows x cols, packed along cols).  Returns a uint8
+    device tensor of dbf_packed_bytes(rows, cols) bytes (16-byte aligned)."""
+    rows, cols = src.shape
+    ld = _row_major(src, "src")
+    nbytes = dbf_packed_bytes(rows, cols)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=src.device)
+    check(lib.dbf_pack_signs(_ptr(src), _DTYPE[src.dtype], rows, cols, ld, _ptr(out),
+                             _stream(stream)), "dbf_pack_signs")
+    return out
+
+
+def dbf_unpack_signs(packed: torch.Tensor, rows: int, cols: int, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.int8, device=packed.device)
+    ld = _row_major(out, "out")
+    check(lib.dbf_unpack_signs(_ptr(packed), rows, cols, _ptr(out), ld, _stream(stream)),
+          "dbf_unpack_signs")
+    return out
+
+
+def _flags(accumulate: bool, path: str | None) -> int:
+    f = _lib.DBF_ACCUMULATE if accumulate else 0
+    if path == "gemv":
+        f |= _lib.DBF_PATH_GEMV
+    elif path == "mfma":
+        f |= _lib.DBF_PATH_MFMA
+    elif path not in (None, "auto"):
+        raise ValueError(f"unknown path {path!r}")
+    return f
+
+
+def _out(y, T, N, y_dtype, device):
+    if y is None:
+        y = torch.empty((T, N), dtype=y_dtype, device=device)
+    return y, _row_major(y, "y")
+
+
+def _ws(ws, N, R, M, ell, T, device):
+    need = dbf_workspace_bytes(N, R, M, ell, T)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return ws
+
+
+def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torch.Tensor,
+                beta: torch.Tensor, gamma: torch.Tensor, N: int, R: int, M: int, *,
+                y: torch.Tensor | None = None, y_dtype=torch.float16, accumulate: bool = False,
+                path: str | None = None, ws: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """y = sum_i diag(alpha_i) B1 diag(beta_i) B2 diag(gamma_i) x per token row.
+
+    x [T][M] fp16; B1, B2 packed (dbf_pack_signs); alpha [ell][N],
+    beta [ell][R], gamma [ell][M] fp16 contiguous."""
+    T = x.shape[0]
+    ell = alpha.shape[0] if alpha.dim() == 2 else 1
+    ldx = _row_major(x, "x")
+    y, ldy = _out(y, T, N, y_dtype, x.device)
+    ws = _ws(ws, N, R, M, ell, T, x.device)
+    yt = _DTYPE[y.dtype]
+    check(lib.dbf_forward(_ptr(x), ldx, _ptr(B1), _ptr(B2), _ptr(alpha), _ptr(beta), _ptr(gamma),
+                          N, R, M, ell, T, _ptr(y), ldy, yt, _flags(accumulate, path), _ptr(ws),
+                          ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward")
+    return y
+
+
+def pointer_table(tensors, device) -> torch.Tensor:
+    """Device int64 array of the tensors' device addresses."""
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+
+
+def dbf_forward_multi_adapter(x: torch.Tensor, ids: torch.Tensor, B1s: torch.Tensor,
+                              B2s: torch.Tensor, alphas: torch.Tensor, betas: torch.Tensor,
+                              gammas: torch.Tensor, num_adapters: int, N: int, R: int, M: int,
+                              ell: int, *, y: torch.Tensor | None = None, y_dtype=torch.float16,
+                              accumulate: bool = False, path: str | None = None,
+                              ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Token t uses adapter ids[t]; the five tables are device int64 arrays
+    of per-adapter device pointers (see ``pointer_table``)."""
+    T = x.shape[0]
+    ldx = _row_major(x, "x")
+    y, ldy = _out(y, T, N, y_dtype, x.device)
+    ws = _ws(ws, N, R, M, ell, T, x.device)
+    yt = _DTYPE[y.dtype]
+    check(lib.dbf_forward_multi_adapter(
+        _ptr(x), ldx, T, _ptr(ids), num_adapters, _ptr(B1s), _ptr(B2s), _ptr(alphas), _ptr(betas),
+        _ptr(gammas), N, R, M, ell, _ptr(y), ldy, yt, _flags(accumulate, path), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward_multi_adapter")
+    return y
+
+
+@dataclass
+class PackedLayer:
+    """One layer's factors resident on the device: packed B1 (N x R) and
+    B2 (R x M) plus fp16 scales [ell][*]."""
+
+    B1: torch.Tensor
+    B2: torch.Tensor
+    alpha: torch.Tensor
+    beta: torch.Tensor
+    gamma: torch.Tensor
+    N: int
+    R: int
+    M: int
+
+    @property
+    def ell(self) -> int:
+        return self.alpha.shape[0]
+
+    @classmethod
+    def from_signs(cls, S1, S2, alpha, beta, gamma, device="cuda") -> "PackedLayer":
+        """S1 [N][R], S2 [R][M] sign (or latent) arrays; scales [ell][*] fp16.
+        Host arrays are uploaded, then packed on the device."""
+        def dev(a, dtype=None):
+            t = torch.as_tensor(a)
+            if dtype is not None:
+                t = t.to(dtype)
+            return t.to(device).contiguous()
+
+        s1, s2 = dev(S1), dev(S2)
+        a, b, g = (dev(v, torch.float16) for v in (alpha, beta, gamma))
+        if a.dim() == 1:
+            a, b, g = a[None], b[None], g[None]
+        B1 = dbf_pack_signs(s1)
+        B2 = dbf_pack_signs(s2)
+        return cls(B1, B2, a.contiguous(), b.contiguous(), g.contiguous(), s1.shape[0],
+                   s1.shape[1], s2.shape[1])
+
+    def forward(self, x: torch.Tensor, **kw) -> torch.Tensor:
+        return dbf_forward(x, self.B1, self.B2, self.alpha, self.beta, self.gamma, self.N, self.R,
+                           self.M, **kw)

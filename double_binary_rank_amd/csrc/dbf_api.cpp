@@ -1,0 +1,180 @@
+// C ABI of the library: synchronous argument validation, then launches on
+// the caller's stream.  No allocation, no global mutable state.
+#include "../../include/dbf.h"
+
+#include <hip/hip_runtime.h>
+
+#include "dbf_launch.h"
+
+using dbf::cdiv;
+
+namespace {
+
+inline bool aligned16(const void* p) { return (((uintptr_t)p) & 15u) == 0; }
+
+dbf_status hip_status(hipError_t e) { return e == hipSuccess ? DBF_OK : DBF_ERR_HIP; }
+
+bool valid_dtype_out(dbf_dtype t) { return t == DBF_F16 || t == DBF_F32; }
+
+constexpr uint32_t kKnownFlags = DBF_ACCUMULATE | DBF_PATH_GEMV | DBF_PATH_MFMA;
+
+// Checks shared by dbf_forward and dbf_forward_multi_adapter.
+dbf_status check_common(const void* x, int64_t ldx, int64_t N, int64_t R, int64_t M, int32_t ell,
+                        int64_t T, void* y, int64_t ldy, dbf_dtype y_type, uint32_t flags,
+                        void* ws, size_t ws_bytes) {
+  if (N <= 0 || R <= 0 || M <= 0 || ell < 1 || T < 0) return DBF_ERR_INVALID_ARG;
+  if (!valid_dtype_out(y_type)) return DBF_ERR_INVALID_ARG;
+  if (flags & ~kKnownFlags) return DBF_ERR_INVALID_ARG;
+  if ((flags & DBF_PATH_GEMV) && (flags & DBF_PATH_MFMA)) return DBF_ERR_INVALID_ARG;
+  if (T == 0) return DBF_OK;
+  if (x == nullptr || y == nullptr) return DBF_ERR_INVALID_ARG;
+  if (ldx < M || ldy < N) return DBF_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || (ldx % 8) != 0) return DBF_ERR_ALIGNMENT;
+  if ((ldy % (y_type == DBF_F16 ? 8 : 4)) != 0) return DBF_ERR_ALIGNMENT;
+  const size_t need = dbf::workspace_bytes(N, R, M, ell, T);
+  if (ws == nullptr || ws_bytes < need) return DBF_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DBF_ERR_ALIGNMENT;
+  return DBF_OK;
+}
+
+dbf::Path pick_path(uint32_t flags, int64_t per_segment, int64_t T) {
+  if (flags & DBF_PATH_GEMV) return dbf::Path::Gemv;
+  if (flags & DBF_PATH_MFMA) return dbf::Path::Mfma;
+  return dbf::choose_path(T, per_segment);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dbf_abi_version(void) { return DBF_ABI_VERSION; }
+
+const char* dbf_status_string(dbf_status s) {
+  switch (s) {
+    case DBF_OK:
+      return "DBF_OK";
+    case DBF_ERR_INVALID_ARG:
+      return "DBF_ERR_INVALID_ARG: null pointer, non-positive size, bad stride, dtype or flag";
+    case DBF_ERR_ALIGNMENT:
+      return "DBF_ERR_ALIGNMENT: a pointer or stride is not aligned as required";
+    case DBF_ERR_WORKSPACE:
+      return "DBF_ERR_WORKSPACE: workspace missing or smaller than dbf_workspace_bytes";
+    case DBF_ERR_HIP:
+      return "DBF_ERR_HIP: the HIP runtime refused a launch";
+    default:
+      return "unknown dbf_status";
+  }
+}
+
+dbf_status dbf_packed_bytes(int64_t rows, int64_t cols, size_t* bytes) {
+  if (rows <= 0 || cols <= 0 || bytes == nullptr) return DBF_ERR_INVALID_ARG;
+  *bytes = (size_t)cdiv(rows, dbf::kRowTile) * (size_t)cdiv(cols, dbf::kColBlock) *
+           (size_t)dbf::kBlockWords * 4u;
+  return DBF_OK;
+}
+
+dbf_status dbf_pack_signs(const void* src, dbf_dtype src_type, int64_t rows, int64_t cols,
+                          int64_t ld_src, uint32_t* dst, void* stream) {
+  if (src == nullptr || dst == nullptr || rows <= 0 || cols <= 0 || ld_src < cols)
+    return DBF_ERR_INVALID_ARG;
+  if (src_type != DBF_I8 && src_type != DBF_F16 && src_type != DBF_F32) return DBF_ERR_INVALID_ARG;
+  if (!aligned16(dst)) return DBF_ERR_ALIGNMENT;
+  return hip_status(
+      dbf::launch_pack(src, (int)src_type, rows, cols, ld_src, dst, (hipStream_t)stream));
+}
+
+dbf_status dbf_unpack_signs(const uint32_t* src, int64_t rows, int64_t cols, int8_t* dst,
+                            int64_t ld_dst, void* stream) {
+  if (src == nullptr || dst == nullptr || rows <= 0 || cols <= 0 || ld_dst < cols)
+    return DBF_ERR_INVALID_ARG;
+  if (!aligned16(src)) return DBF_ERR_ALIGNMENT;
+  return hip_status(dbf::launch_unpack(src, rows, cols, dst, ld_dst, (hipStream_t)stream));
+}
+
+dbf_status dbf_workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T,
+                               size_t* bytes) {
+  if (N <= 0 || R <= 0 || M <= 0 || ell < 1 || T < 0 || bytes == nullptr)
+    return DBF_ERR_INVALID_ARG;
+  *bytes = dbf::workspace_bytes(N, R, M, ell, T);
+  return DBF_OK;
+}
+
+dbf_status dbf_forward(const void* x, int64_t ldx, const uint32_t* B1, const uint32_t* B2,
+                       const void* alpha, const void* beta, const void* gamma, int64_t N,
+                       int64_t R, int64_t M, int32_t ell, int64_t T, void* y, int64_t ldy,
+                       dbf_dtype y_type, uint32_t flags, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (B1 == nullptr || B2 == nullptr || alpha == nullptr || beta == nullptr || gamma == nullptr)
+    return DBF_ERR_INVALID_ARG;
+  dbf_status st = check_common(x, ldx, N, R, M, ell, T, y, ldy, y_type, flags, ws, ws_bytes);
+  if (st != DBF_OK || T == 0) return st;
+  if (!aligned16(B1) || !aligned16(B2)) return DBF_ERR_ALIGNMENT;
+  if ((((uintptr_t)alpha) | ((uintptr_t)beta) | ((uintptr_t)gamma)) & 1u) return DBF_ERR_ALIGNMENT;
+
+  dbf::ForwardArgs a{};
+  a.x = (const dbf::half_t*)x;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.y_f32 = (y_type == DBF_F32);
+  a.accumulate = (flags & DBF_ACCUMULATE) != 0;
+  a.N = N;
+  a.R = R;
+  a.M = M;
+  a.T = T;
+  a.ell = ell;
+  a.single = dbf::Factors{B1, B2, (const dbf::half_t*)alpha, (const dbf::half_t*)beta,
+                          (const dbf::half_t*)gamma};
+  a.multi = false;
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  a.path = pick_path(flags, T, T);
+  return hip_status(dbf::launch_forward(a, (hipStream_t)stream));
+}
+
+dbf_status dbf_forward_multi_adapter(const void* x, int64_t ldx, int64_t T, const int32_t* ids,
+                                     int32_t num_adapters, const uint32_t* const* B1s,
+                                     const uint32_t* const* B2s, const void* const* alphas,
+                                     const void* const* betas, const void* const* gammas,
+                                     int64_t N, int64_t R, int64_t M, int32_t ell, void* y,
+                                     int64_t ldy, dbf_dtype y_type, uint32_t flags, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (num_adapters < 1 || B1s == nullptr || B2s == nullptr || alphas == nullptr ||
+      betas == nullptr || gammas == nullptr)
+    return DBF_ERR_INVALID_ARG;
+  dbf_status st = check_common(x, ldx, N, R, M, ell, T, y, ldy, y_type, flags, ws, ws_bytes);
+  if (st != DBF_OK || T == 0) return st;
+  if (ids == nullptr) return DBF_ERR_INVALID_ARG;
+  if ((((uintptr_t)B1s) | ((uintptr_t)B2s) | ((uintptr_t)alphas) | ((uintptr_t)betas) |
+       ((uintptr_t)gammas)) & 7u)
+    return DBF_ERR_ALIGNMENT;
+  if (((uintptr_t)ids) & 3u) return DBF_ERR_ALIGNMENT;
+
+  dbf::ForwardArgs a{};
+  a.x = (const dbf::half_t*)x;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.y_f32 = (y_type == DBF_F32);
+  a.accumulate = (flags & DBF_ACCUMULATE) != 0;
+  a.N = N;
+  a.R = R;
+  a.M = M;
+  a.T = T;
+  a.ell = ell;
+  a.multi = true;
+  a.ids = ids;
+  a.num_adapters = num_adapters;
+  a.B1s = B1s;
+  a.B2s = B2s;
+  a.alphas = (const dbf::half_t* const*)alphas;
+  a.betas = (const dbf::half_t* const*)betas;
+  a.gammas = (const dbf::half_t* const*)gammas;
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  const int64_t per = T / (num_adapters < T ? num_adapters : T);
+  a.path = pick_path(flags, per, T);
+  return hip_status(dbf::launch_forward(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

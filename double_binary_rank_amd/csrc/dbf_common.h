@@ -1,0 +1,60 @@
+// Shared definitions of the HIP path (device and host).  Not part of the
+// public ABI: the packed layout and the launch structures are internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dbf {
+
+typedef _Float16 half_t;
+typedef half_t v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Packed sign layout (one bit per sign; bit value 1 means -1).
+//
+// A rows x cols sign matrix is packed along cols (the reduction dimension of
+// its product).  Rows are grouped in tiles of 16, cols in blocks of 128.  Each
+// (row tile, col block) pair is one 256-byte block; blocks are stored row-tile
+// major: block (rt, kb) starts at word (rt * nkb + kb) * 64.  Inside a block,
+// row rho (0..15) owns words 4*rho .. 4*rho+3; word q covers cols
+// kb*128 + 32*q + s for s = 0..31.  Inside a word, slot s sits at bit
+//     b(s) = 4 * (s % 8) + s / 8
+// so that slots 8d..8d+7 occupy bits d, d+4, ..., d+28.  This order lets a
+// lane turn a word into matrix-core operands with a shift and a mask per
+// register (fp4: (w << (3-d)) & 0x88888888 gives the sign bits of 8 slots).
+// A 64-lane wave reading one block reads 256 contiguous bytes.
+// ---------------------------------------------------------------------------
+constexpr int kRowTile = 16;
+constexpr int kColBlock = 128;
+constexpr int kBlockWords = 64;
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int slot_bit(int s) { return 4 * (s & 7) + (s >> 3); }
+
+// One adapter's factors (device pointers).
+struct Factors {
+  const uint32_t* B1;
+  const uint32_t* B2;
+  const half_t* alpha;
+  const half_t* beta;
+  const half_t* gamma;
+};
+
+// A run of consecutive tokens [t0, t1) served by one adapter (adapter < 0:
+// tokens that contribute nothing).
+struct ColBlock {
+  int32_t t0, t1, adapter, pad;
+};
+
+// Workspace header written by the segmentation kernel.
+struct WsHeader {
+  int32_t n_colblocks;
+  int32_t pad[63];
+};
+
+}  // namespace dbf

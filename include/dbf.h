@@ -1,0 +1,158 @@
+/*
+ * dbf.h -- C ABI of the MI355X (gfx950) double-binary-factorised product.
+ *
+ * The operation (LoRDBA summary, section 2 "Arquitectura Central", update
+ * equation; DBF summary, section 2 "Calculo en la inferencia", operation
+ * order):
+ *
+ *     y[t] = sum_{i<ell} diag(alpha_i) . B1 . diag(beta_i) . B2 . diag(gamma_i) . x[t]
+ *
+ * evaluated as  scale by gamma_i -> accumulate signs of B2 -> scale by beta_i
+ * -> accumulate signs of B1 -> scale by alpha_i -> sum over i.
+ *
+ *   x      [T][M]  fp16, row stride ldx elements (token rows)
+ *   B1     N x R   signs in {-1,+1}, packed (dbf_pack_signs, cols = R)
+ *   B2     R x M   signs in {-1,+1}, packed (dbf_pack_signs, cols = M)
+ *   alpha  [ell][N], beta [ell][R], gamma [ell][M]   fp16, contiguous
+ *   y      [T][N]  fp16 or fp32, row stride ldy elements
+ *
+ * The signs are shared by the ell terms; only the scales carry the term
+ * index (the LoRDBA update indexes only alpha, beta, gamma).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates or frees memory and keeps no per-call state.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream).  Buffers must stay valid until the stream reaches the work.
+ *    Calls are re-entrant; concurrent calls must not share a workspace.
+ *  - Arguments are validated synchronously on the host before any launch;
+ *    a failed check returns an error and enqueues nothing.
+ *  - Sizes are element counts unless stated otherwise.
+ */
+#ifndef DBF_H_
+#define DBF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dbf_status;
+#define DBF_OK 0
+#define DBF_ERR_INVALID_ARG (-1) /* null pointer, bad size/stride/dtype/flag */
+#define DBF_ERR_ALIGNMENT (-2)   /* pointer or stride misaligned            */
+#define DBF_ERR_WORKSPACE (-3)   /* workspace missing or too small          */
+#define DBF_ERR_HIP (-4)         /* the HIP runtime refused a launch        */
+
+typedef int32_t dbf_dtype;
+#define DBF_I8 1
+#define DBF_F16 2
+#define DBF_F32 3
+
+/* flags for dbf_forward / dbf_forward_multi_adapter */
+#define DBF_ACCUMULATE 1u /* y += product (unmerged adapter branch added onto
+                             a base output, LoRDBA summary section 1); the
+                             default overwrites y                            */
+#define DBF_PATH_GEMV 2u  /* force the small-T (decode) kernels  (tuning/tests) */
+#define DBF_PATH_MFMA 4u  /* force the large-T (prefill) kernels (tuning/tests) */
+
+#define DBF_ABI_VERSION 1
+
+/* ABI version of the loaded library (DBF_ABI_VERSION it was built with). */
+int32_t dbf_abi_version(void);
+
+/* Static, human-readable text for a status code. */
+const char* dbf_status_string(dbf_status s);
+
+/*
+ * Bytes of the packed form of a rows x cols sign matrix, packed along cols
+ * (the reduction dimension of its product).  One bit per sign (LoRDBA
+ * summary, section 2 "Eficiencia de Almacenamiento"); rows are padded to a
+ * multiple of 16 and cols to a multiple of 128, so the size is
+ * ceil(rows/16) * ceil(cols/128) * 256.  The layout itself is internal.
+ * Errors: INVALID_ARG if rows <= 0, cols <= 0 or bytes == NULL.
+ */
+dbf_status dbf_packed_bytes(int64_t rows, int64_t cols, size_t* bytes);
+
+/*
+ * Binarise and pack: sign(h) per entry of the rows x cols source (row stride
+ * ld_src elements) into `dst` (dbf_packed_bytes bytes, 16-byte aligned).
+ * sign(h) = -1 for h < 0, +1 otherwise (+-0 and NaN give +1); this is the
+ * forward binarisation B = sign(H) of the LoRDBA training pipeline
+ * (summary section 2 "Pipeline de Entrenamiento", step 2).  An int8 source
+ * is read the same way, so +-1 int8 matrices pack exactly.
+ *   src_type: DBF_I8, DBF_F16 or DBF_F32.
+ * Padding entries are written as +1.
+ * Errors: INVALID_ARG (null pointer, rows/cols <= 0, ld_src < cols, bad
+ * dtype), ALIGNMENT (dst not 16-byte aligned), HIP.
+ */
+dbf_status dbf_pack_signs(const void* src, dbf_dtype src_type, int64_t rows, int64_t cols,
+                          int64_t ld_src, uint32_t* dst, void* stream);
+
+/*
+ * Inverse of dbf_pack_signs for inspection and tests: writes int8 +-1 into
+ * dst [rows][ld_dst].  Errors as for dbf_pack_signs (ld_dst < cols is
+ * INVALID_ARG; src must be 16-byte aligned).
+ */
+dbf_status dbf_unpack_signs(const uint32_t* src, int64_t rows, int64_t cols, int8_t* dst,
+                            int64_t ld_dst, void* stream);
+
+/*
+ * Workspace bytes needed by dbf_forward and dbf_forward_multi_adapter for
+ * these sizes (the same bound serves both).  T may be 0 (returns 0 bytes
+ * needed beyond a small header).
+ * Errors: INVALID_ARG if N, R, M <= 0, ell < 1, T < 0 or bytes == NULL.
+ */
+dbf_status dbf_workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T,
+                               size_t* bytes);
+
+/*
+ * y = sum_i diag(alpha_i) B1 diag(beta_i) B2 diag(gamma_i) x   for T tokens
+ * (with DBF_ACCUMULATE: y += ...).  Inputs as described at the top.
+ * Precision: fp32 accumulation.  On the small-T path gamma_i*x (exact in
+ * fp32) and the R-vector beta_i*u stay fp32 up to the matrix-core operand
+ * encoding (see the design notes); on the large-T path the matrix-core
+ * operands gamma_i*x and beta_i*u are rounded to fp16.  The fp16 output is
+ * rounded to nearest-even and overflows to +-inf.
+ * Alignment: x, y, B1, B2 and ws 16-byte aligned; ldx a multiple of 8;
+ * ldy a multiple of 8 (fp16 y) or 4 (fp32 y).
+ * T == 0 is a successful no-op (x, y and ws may then be NULL).
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE (ws_bytes below
+ * dbf_workspace_bytes), HIP.
+ */
+dbf_status dbf_forward(const void* x, int64_t ldx, const uint32_t* B1, const uint32_t* B2,
+                       const void* alpha, const void* beta, const void* gamma, int64_t N,
+                       int64_t R, int64_t M, int32_t ell, int64_t T, void* y, int64_t ldy,
+                       dbf_dtype y_type, uint32_t flags, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * Batched adapter serving (LoRDBA summary, section 1: many unmerged adapters
+ * served together, as in S-LoRA / Punica).  Token t uses adapter ids[t]:
+ *   y[t] = DBF_{ids[t]}(x[t])      (with DBF_ACCUMULATE: y[t] += ...)
+ * Tokens whose id is outside [0, num_adapters) contribute nothing: their row
+ * of y is written as 0, or left unchanged under DBF_ACCUMULATE.
+ *   ids      device int32 [T]; any order is correct, runs of equal ids are
+ *            processed together (sorted ids are fastest)
+ *   B1s, B2s, alphas, betas, gammas   DEVICE arrays of num_adapters device
+ *            pointers, each as in dbf_forward; every adapter has the same
+ *            N, R, M and ell.
+ * Errors as for dbf_forward, plus INVALID_ARG for num_adapters < 1 or a
+ * null table.  Adapter pointers inside the tables are not checked (they live
+ * on the device).
+ */
+dbf_status dbf_forward_multi_adapter(const void* x, int64_t ldx, int64_t T, const int32_t* ids,
+                                     int32_t num_adapters, const uint32_t* const* B1s,
+                                     const uint32_t* const* B2s, const void* const* alphas,
+                                     const void* const* betas, const void* const* gammas,
+                                     int64_t N, int64_t R, int64_t M, int32_t ell, void* y,
+                                     int64_t ldy, dbf_dtype y_type, uint32_t flags, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBF_H_ */

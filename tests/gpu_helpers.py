@@ -1,0 +1,64 @@
+"""Helpers for the GPU tests: upload seeded inputs, run the HIP path through
+the C ABI, and a host-side model of the documented packed layout."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import double_binary_rank_amd as dbf
+
+
+def pack_ref(S: np.ndarray) -> np.ndarray:
+    """The packed words of sign(S) under the layout the library documents:
+    16-row tiles x 128-col blocks of 256 bytes, row-tile major; row rho of a
+    block owns words 4*rho..4*rho+3; slot s of a word at bit 4*(s%8)+s//8;
+    bit 1 means -1."""
+    rows, cols = S.shape
+    nrt, nkb = -(-rows // 16), -(-cols // 128)
+    words = np.zeros(nrt * nkb * 64, dtype=np.uint64)
+    r, k = np.nonzero(np.asarray(S) < 0)
+    idx = ((r // 16) * nkb + k // 128) * 64 + 4 * (r % 16) + (k % 128) // 32
+    s = k % 32
+    bit = 4 * (s % 8) + s // 8
+    np.bitwise_or.at(words, idx, (np.uint64(1) << bit.astype(np.uint64)))
+    return words.astype(np.uint32)
+
+
+def to_dev(a, dtype=None):
+    t = torch.as_tensor(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def upload(L) -> dbf.PackedLayer:
+    return dbf.PackedLayer.from_signs(L.S1, L.S2, L.alpha, L.beta, L.gamma, device="cuda")
+
+
+def run_layer(L, path=None, y_dtype=torch.float16, accumulate=False, y_init=None, pl=None):
+    pl = pl or upload(L)
+    x = to_dev(L.x)
+    y = None if y_init is None else to_dev(y_init)
+    out = pl.forward(x, path=path, y_dtype=y_dtype, accumulate=accumulate, y=y)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+class DeviceAdapters:
+    """Per-adapter packed factors plus the device pointer tables."""
+
+    def __init__(self, adapters):
+        self.layers = [upload(a) for a in adapters]
+        dev = "cuda"
+        self.B1s = dbf.pointer_table([p.B1 for p in self.layers], dev)
+        self.B2s = dbf.pointer_table([p.B2 for p in self.layers], dev)
+        self.alphas = dbf.pointer_table([p.alpha for p in self.layers], dev)
+        self.betas = dbf.pointer_table([p.beta for p in self.layers], dev)
+        self.gammas = dbf.pointer_table([p.gamma for p in self.layers], dev)
+        p0 = self.layers[0]
+        self.N, self.R, self.M, self.ell = p0.N, p0.R, p0.M, p0.ell
+
+    def forward(self, x, ids, **kw):
+        return dbf.dbf_forward_multi_adapter(
+            x, ids, self.B1s, self.B2s, self.alphas, self.betas, self.gammas, len(self.layers),
+            self.N, self.R, self.M, self.ell, **kw)

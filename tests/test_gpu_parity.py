@@ -1,0 +1,268 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Bars: bit-exact on integer-valued inputs with unit scales (fp32 output equals
+float32 of the exact value; fp16 output equals its nearest-even rounding);
+max|y - y_ref| / max|y_ref| <= 2e-3 on fp16 inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+PATHS = ["gemv", "mfma"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    torch.manual_seed(0)
+
+
+def H():
+    import gpu_helpers
+    return gpu_helpers
+
+
+def ref(L, y_old=None):
+    return oracle.forward(L.x, L.S1, L.S2, L.alpha, L.beta, L.gamma, y_old=y_old)
+
+
+# ------------------------------------------------------------ packing ----
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (37, 300), (16, 128), (64, 4096), (5, 33)])
+def test_pack_layout_int8(rows, cols):
+    rng = np.random.default_rng(rows * 1000 + cols)
+    S = synth.make_signs(rng, rows, cols)
+    packed = H().dbf.dbf_pack_signs(H().to_dev(S))
+    torch.cuda.synchronize()
+    got = packed.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, H().pack_ref(S))
+
+
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_pack_latent_sign(dtype):
+    rng = np.random.default_rng(7)
+    h = rng.standard_normal((40, 200)).astype(dtype)
+    h[0, :5] = [0.0, -0.0, np.nan, -np.inf, np.inf]
+    h[3, 7] = -np.finfo(dtype).tiny
+    packed = H().dbf.dbf_pack_signs(H().to_dev(h))
+    torch.cuda.synchronize()
+    want = H().pack_ref(oracle.sign_of_latent(h))
+    assert np.array_equal(packed.cpu().numpy().view(np.uint32), want)
+
+
+@pytest.mark.parametrize("rows,cols", [(37, 300), (128, 64), (3, 1)])
+def test_unpack_roundtrip(rows, cols):
+    rng = np.random.default_rng(rows + cols)
+    S = synth.make_signs(rng, rows, cols)
+    d = H().dbf
+    back = d.dbf_unpack_signs(d.dbf_pack_signs(H().to_dev(S)), rows, cols)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().numpy(), S)
+
+
+# -------------------------------------------------- single layer parity ----
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("y_dtype", [torch.float32, torch.float16])
+def test_tiny_integer_bitexact(path, y_dtype):
+    L = synth.make_config_layer(1, 4, integer=True)
+    y = H().run_layer(L, path=path, y_dtype=y_dtype)
+    want = ref(L)
+    if y_dtype == torch.float32:
+        assert np.array_equal(y, want.astype(np.float32).astype(np.float64))
+    else:
+        assert np.array_equal(y, oracle.fp16_rne(want).astype(np.float64))
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("cfg,T", [(1, 4), (2, 1), (2, 8), (3, 1)])
+def test_config_parity(cfg, T, path):
+    L = synth.make_config_layer(cfg, T)
+    err = oracle.max_norm_error(H().run_layer(L, path=path), ref(L))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("path", [None, "gemv", "mfma"])
+def test_attn_T256_full(path):
+    """4096 x 4096, R = 2048 at T = 256 (the prefill case the benchmark times)."""
+    L = synth.make_config_layer(3, 256)
+    err = oracle.max_norm_error(H().run_layer(L, path=path), ref(L))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("cfg", [4, 40])
+@pytest.mark.parametrize("T", [1, 16, 256])
+def test_mlp_sampled(cfg, T):
+    """MLP up (14336 x 4096) and down (4096 x 14336), R = 6368: sampled
+    tokens and outputs computed one by one by the oracle."""
+    L = synth.make_config_layer(cfg, T)
+    y = H().run_layer(L)
+    rng = np.random.default_rng(T)
+    toks = np.unique(rng.choice(T, size=min(T, 6), replace=False))
+    cols = np.sort(rng.choice(L.N, size=384, replace=False))
+    want = oracle.forward_rows(L.x[toks], L.S1, L.S2, L.alpha, L.beta, L.gamma, cols)
+    err = oracle.max_norm_error(y[toks][:, cols], want)
+    assert err <= TOL, err
+    assert np.all(np.isfinite(y))
+
+
+RAGGED = [(5, 7, 33, 1, 3), (300, 130, 260, 1, 37), (17, 129, 127, 2, 5), (64, 16, 8, 3, 70),
+          (1, 1, 1, 1, 1), (33, 200, 520, 2, 130)]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("shape", RAGGED)
+def test_ragged_integer_bitexact(shape, path):
+    N, R, M, ell, T = shape
+    L = synth.make_layer(N, R, M, ell, T, seed=sum(shape), alpha="ones", beta="ones", gamma="ones",
+                         x_kind="int3")
+    y = H().run_layer(L, path=path, y_dtype=torch.float32)
+    assert np.array_equal(y, ref(L).astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("shape", RAGGED)
+def test_ragged_fp16(shape, path):
+    N, R, M, ell, T = shape
+    L = synth.make_layer(N, R, M, ell, T, seed=sum(shape) + 1)
+    err = oracle.max_norm_error(H().run_layer(L, path=path), ref(L))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_accumulate(path):
+    L = synth.make_config_layer(1, 4, integer=True)
+    rng = np.random.default_rng(3)
+    base = rng.integers(-50, 50, size=(4, L.N)).astype(np.float16)
+    y = H().run_layer(L, path=path, y_dtype=torch.float16, accumulate=True, y_init=base)
+    assert np.array_equal(y, oracle.fp16_rne(ref(L, y_old=base)).astype(np.float64))
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_sign_flip_gauge_bitwise(path):
+    """Negating column r of B1 together with row r of B2 leaves y bit-identical
+    (fp16 data: every step is sign-symmetric)."""
+    L = synth.make_config_layer(1, 4)
+    y0 = H().run_layer(L, path=path)
+    rng = np.random.default_rng(5)
+    flip = rng.random(L.R) < 0.5
+    L.S1[:, flip] *= -1
+    L.S2[flip, :] *= -1
+    assert np.array_equal(H().run_layer(L, path=path), y0)
+
+
+def test_paths_agree_on_integers():
+    L = synth.make_layer(96, 200, 300, 2, 20, seed=9, alpha="ones", beta="ones", gamma="ones",
+                         x_kind="int3")
+    a = H().run_layer(L, path="gemv", y_dtype=torch.float32)
+    b = H().run_layer(L, path="mfma", y_dtype=torch.float32)
+    assert np.array_equal(a, b)
+
+
+def test_determinism_and_stream():
+    L = synth.make_config_layer(3, 1)
+    pl = H().upload(L)
+    x = H().to_dev(L.x)
+    outs = []
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(20):
+            outs.append(pl.forward(x).clone())
+    s.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    err = oracle.max_norm_error(outs[0].float().cpu().numpy(), ref(L))
+    assert err <= TOL
+
+
+def test_guard_bands_untouched():
+    L = synth.make_layer(40, 24, 72, 1, 7, seed=11)
+    pl = H().upload(L)
+    x = H().to_dev(L.x)
+    canary = -12345.0
+    big = torch.full((7 + 4, 64 + 16), canary, dtype=torch.float32, device="cuda")
+    y = big[2:9, 8:48]  # ldy = 80, 40 columns written
+    pl.forward(x, y=y, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    b = big.cpu().numpy()
+    mask = np.ones_like(b, dtype=bool)
+    mask[2:9, 8:48] = False
+    assert np.all(b[mask] == canary)
+    err = oracle.max_norm_error(b[2:9, 8:48], ref(L))
+    assert err <= TOL
+
+
+def test_T0_noop():
+    L = synth.make_layer(16, 8, 32, 1, 0, seed=1)
+    pl = H().upload(L)
+    x = torch.empty((0, 32), dtype=torch.float16, device="cuda")
+    y = pl.forward(x)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 16)
+
+
+# ------------------------------------------------------- multi-adapter ----
+
+def _multi_ref(B, ids, y_old=None):
+    return oracle.forward_multi_adapter(B.x, ids, B.adapters, y_old=y_old)
+
+
+@pytest.mark.parametrize("path", [None, "gemv", "mfma"])
+def test_multi_adapter_config5(path):
+    B = synth.make_multi_adapter()  # 64 adapters, 4096^2, R=64, ell=2, T=2048, Zipf ids
+    D = H().DeviceAdapters(B.adapters)
+    y = D.forward(H().to_dev(B.x), H().to_dev(B.ids), path=path)
+    torch.cuda.synchronize()
+    err = oracle.max_norm_error(y.float().cpu().numpy(), _multi_ref(B, B.ids))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_multi_adapter_integer_unsorted_invalid(path):
+    B = synth.make_multi_adapter(num_adapters=5, N=72, R=40, M=136, ell=2, T=77, seed=21,
+                                 alpha="ones", beta="ones", gamma="ones", x_kind="int3",
+                                 sort=False)
+    ids = B.ids.copy()
+    ids[[0, 9, 10, 40]] = [-1, 5, 1000, -7]
+    D = H().DeviceAdapters(B.adapters)
+    y = D.forward(H().to_dev(B.x), H().to_dev(ids), path=path, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64),
+                          _multi_ref(B, ids).astype(np.float32).astype(np.float64))
+    # accumulate: rows of invalid ids keep the base output
+    base = np.random.default_rng(2).integers(-9, 9, size=(77, 72)).astype(np.float32)
+    y2 = D.forward(H().to_dev(B.x), H().to_dev(ids), path=path, y=H().to_dev(base),
+                   accumulate=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.cpu().numpy().astype(np.float64),
+                          _multi_ref(B, ids, y_old=base).astype(np.float32).astype(np.float64))
+
+
+def test_multi_adapter_permutation_invariance():
+    B = synth.make_multi_adapter(num_adapters=8, N=256, R=64, M=256, ell=2, T=300, seed=33)
+    D = H().DeviceAdapters(B.adapters)
+    x, ids = H().to_dev(B.x), H().to_dev(B.ids)
+    y = D.forward(x, ids)
+    perm = torch.as_tensor(np.random.default_rng(4).permutation(300)).cuda()
+    yp = D.forward(x[perm].contiguous(), ids[perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y[perm])
+
+
+def test_multi_equals_single():
+    """A batch routed entirely to adapter k equals dbf_forward of adapter k."""
+    B = synth.make_multi_adapter(num_adapters=3, N=128, R=32, M=192, ell=1, T=40, seed=44)
+    D = H().DeviceAdapters(B.adapters)
+    x = H().to_dev(B.x)
+    ids = torch.full((40,), 2, dtype=torch.int32, device="cuda")
+    ym = D.forward(x, ids, path="gemv")
+    ys = D.layers[2].forward(x, path="gemv")
+    torch.cuda.synchronize()
+    assert torch.equal(ym, ys)
