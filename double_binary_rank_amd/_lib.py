@@ -46,12 +46,31 @@ class DbfError(RuntimeError):
         self.status = status
 
 
+def _hip_runtimes() -> set:
+    """Paths of every libamdhip64 mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    except OSError:  # pragma: no cover
+        return set()
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m double_binary_rank_amd.build`"
         )
-    return ctypes.CDLL(LIB_PATH)
+    # PyTorch ships its own HIP runtime.  Load it first: the library then
+    # binds to that same runtime (same soname), so stream handles and device
+    # pointers from torch are valid in our launches.  Two runtimes in one
+    # process would not share streams or contexts.
+    import torch  # noqa: F401
+
+    lib_ = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError(f"more than one HIP runtime mapped into the process: {sorted(runtimes)}")
+    return lib_
 
 
 lib = _load()

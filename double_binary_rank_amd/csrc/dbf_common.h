@@ -14,21 +14,28 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+// Global-address-space views: loads through these compile to global_load
+// (tracked by vmcnt alone) instead of flat loads.
+#define DBF_GLOBAL __attribute__((address_space(1)))
+typedef const DBF_GLOBAL uint32_t* gu32p;
+typedef const DBF_GLOBAL v8i* gv8ip;
+
 // ---------------------------------------------------------------------------
 // Packed sign layout (one bit per sign; bit value 1 means -1).
 //
 // A rows x cols sign matrix is packed along cols (the reduction dimension of
 // its product).  Rows are grouped in tiles of 16, cols in blocks of 128.  Each
 // (row tile, col block) pair is one 256-byte block; blocks are stored row-tile
-// major: block (rt, kb) starts at word (rt * nkb + kb) * 64.  Inside a block,
-// row rho (0..15) owns words 4*rho .. 4*rho+3; word q covers cols
-// kb*128 + 32*q + s for s = 0..31.  Inside a word, slot s sits at bit
+// major: block (rt, kb) starts at word (rt * nkb + kb) * 64.  Inside a block
+// the 64 words are in matrix-core lane order: word lam = 16*q + rho holds
+// row rho (0..15) of the tile and cols kb*128 + 32*q + s, s = 0..31, which
+// is what lane lam of a 16x16x128 MFMA holds as its A operand.  Inside a
+// word, slot s sits at bit
 //     b(s) = 4 * (s % 8) + s / 8
 // so that slots 8d..8d+7 occupy bits d, d+4, ..., d+28.  This order lets a
-// lane turn a word into matrix-core operands with a shift and a mask per
-// register (fp4: (w << (3-d)) & 0x88888888 gives the sign bits of 8 slots).
+// lane turn a word into fp4 operands with a shift and a mask per register:
+// ((w << (3-d)) & 0x88888888) | 0x22222222 is +-1.0 in e2m1 for 8 slots.
 // A 64-lane wave reading one block reads 256 contiguous bytes.
-// ---------------------------------------------------------------------------
 constexpr int kRowTile = 16;
 constexpr int kColBlock = 128;
 constexpr int kBlockWords = 64;

@@ -8,6 +8,7 @@
 // z lives in the caller's workspace as fp32 [ell][T][ldz].
 #include <climits>
 
+#include "dbf_device.h"
 #include "dbf_launch.h"
 
 namespace dbf {
@@ -20,7 +21,7 @@ __global__ void k_pack(const void* __restrict__ src, int dtype, int64_t rows, in
   if (gid >= total_words) return;
   const int64_t blk = gid / kBlockWords;
   const int w = (int)(gid % kBlockWords);
-  const int rho = w >> 2, q = w & 3;
+  const int rho = w & 15, q = w >> 4;
   const int64_t row = (blk / nkb) * kRowTile + rho;
   const int64_t k0 = (blk % nkb) * kColBlock + 32 * q;
   uint32_t word = 0;
@@ -48,8 +49,8 @@ __global__ void k_unpack(const uint32_t* __restrict__ src, int64_t rows, int64_t
   if (gid >= total_words) return;
   const int64_t blk = gid / kBlockWords;
   const int w = (int)(gid % kBlockWords);
-  const int64_t row = (blk / nkb) * kRowTile + (w >> 2);
-  const int64_t k0 = (blk % nkb) * kColBlock + 32 * (w & 3);
+  const int64_t row = (blk / nkb) * kRowTile + (w & 15);
+  const int64_t k0 = (blk % nkb) * kColBlock + 32 * (w >> 4);
   if (row >= rows) return;
   const uint32_t word = src[gid];
   for (int s = 0; s < 32; ++s) {
@@ -169,38 +170,6 @@ struct StageParams {
   const half_t* const* gammas;
 };
 
-__device__ inline void store4(void* y, int64_t ldy, bool f32, int64_t t, int64_t r, int64_t rows,
-                              const float v[4]) {
-  if (f32) {
-    float* p = (float*)y + t * ldy + r;
-    if (r + 4 <= rows) {
-      *(v4f*)p = v4f{v[0], v[1], v[2], v[3]};
-    } else {
-      for (int e = 0; e < 4; ++e)
-        if (r + e < rows) p[e] = v[e];
-    }
-  } else {
-    half_t* p = (half_t*)y + t * ldy + r;
-    if (r + 4 <= rows) {
-      typedef half_t v4h __attribute__((ext_vector_type(4)));
-      *(v4h*)p = v4h{(half_t)v[0], (half_t)v[1], (half_t)v[2], (half_t)v[3]};
-    } else {
-      for (int e = 0; e < 4; ++e)
-        if (r + e < rows) p[e] = (half_t)v[e];
-    }
-  }
-}
-
-__device__ inline void load4(const void* y, int64_t ldy, bool f32, int64_t t, int64_t r,
-                             int64_t rows, float v[4]) {
-  for (int e = 0; e < 4; ++e) {
-    if (r + e < rows)
-      v[e] = f32 ? ((const float*)y)[t * ldy + r + e] : (float)((const half_t*)y)[t * ldy + r + e];
-    else
-      v[e] = 0.0f;
-  }
-}
-
 // Wave tile: (16*RW rows) x (16*CW tokens).  The four waves of a workgroup
 // compute the same tile over four quarters of K and are summed in a fixed
 // order through LDS (deterministic).  MFMA: A = signs (rows), B = activations
@@ -276,8 +245,9 @@ __global__ __launch_bounds__(256) void k_stage_f16(StageParams p) {
 #pragma unroll
         for (int rt = 0; rt < RW; ++rt) {
           const int64_t tile = row0 / 16 + rt;
-          wd[rt] = tile < p.nrt ? *(const v4u*)(S + (tile * p.nkb + kb) * kBlockWords + 4 * c16)
-                                : v4u{0u, 0u, 0u, 0u};
+          const uint32_t* blk = S + (tile * p.nkb + kb) * kBlockWords + c16;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) wd[rt][q] = tile < p.nrt ? blk[16 * q] : 0u;
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -446,20 +416,21 @@ __global__ __launch_bounds__(1024) void k_segment(const int32_t* __restrict__ id
 
 // ============================================================ launching ====
 
-static inline int64_t ldz_of(int64_t R) { return cdiv(R, 8) * 8; }
-static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
-static inline int64_t max_colblocks(int64_t T) { return T + cdiv(T, 16) + 1; }
-
 size_t workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T) {
-  (void)N;
-  (void)M;
-  return sizeof(WsHeader) + align256((size_t)max_colblocks(T) * sizeof(ColBlock)) +
-         align256((size_t)ell * (size_t)T * (size_t)ldz_of(R) * sizeof(float));
+  return ws_layout(N, R, M, ell, T).total;
 }
 
 Path choose_path(int64_t T, int64_t per_seg) {
   (void)T;
   return per_seg <= 16 ? Path::Gemv : Path::Mfma;
+}
+
+hipError_t launch_segment(const ForwardArgs& a, int chunk, hipStream_t s) {
+  const WsLayout L = ws_layout(a.N, a.R, a.M, a.ell, a.T);
+  char* ws = (char*)a.ws;
+  hipLaunchKernelGGL(k_segment, dim3(1), dim3(1024), 0, s, a.ids, a.T, a.num_adapters, chunk,
+                     (ColBlock*)(ws + L.cbl), (WsHeader*)ws);
+  return hipGetLastError();
 }
 
 template <int STAGE, int RW, int CW>
@@ -484,13 +455,22 @@ static hipError_t run_stages(StageParams p1, StageParams p2, bool multi, int64_t
 }
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
+  // small-T path: fp4 signs x 3-part fp8 activations on the scaled MFMA
+  const int tcb = gemv_tokens_per_block(a.ell);
+  if (tcb > 0 && a.T <= kGemvMaxT) {
+    const int64_t segs = a.multi ? (a.num_adapters < a.T ? a.num_adapters : a.T) : 1;
+    const int64_t per_seg = cdiv(a.T, segs);
+    const bool want = a.path == Path::Gemv || (a.path != Path::Mfma && per_seg <= tcb);
+    if (want) return launch_gemv(a, s);
+  }
+  const WsLayout L = ws_layout(a.N, a.R, a.M, a.ell, a.T);
   char* ws = (char*)a.ws;
   WsHeader* hdr = (WsHeader*)ws;
-  ColBlock* cbl = (ColBlock*)(ws + sizeof(WsHeader));
-  float* z = (float*)(ws + sizeof(WsHeader) + align256((size_t)max_colblocks(a.T) * sizeof(ColBlock)));
+  ColBlock* cbl = (ColBlock*)(ws + L.cbl);
+  float* z = (float*)(ws + L.z);
 
   int RW, CW;
-  if (a.path == Path::Gemv) {
+  if (a.T <= 16 && !a.multi) {
     RW = 1;
     CW = 1;
   } else if (a.T <= 64 && !a.multi) {
@@ -534,9 +514,7 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
 
   int64_t n_cb_max;
   if (a.multi) {
-    hipLaunchKernelGGL(k_segment, dim3(1), dim3(1024), 0, s, a.ids, a.T, a.num_adapters, chunk,
-                       cbl, hdr);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_segment(a, chunk, s);
     if (e != hipSuccess) return e;
     n_cb_max = a.T + cdiv(a.T, chunk);
     if (n_cb_max > max_colblocks(a.T)) n_cb_max = max_colblocks(a.T);

@@ -35,6 +35,45 @@ struct ForwardArgs {
   Path path;
 };
 
+// Largest batch the small-T (fp4 matrix-core) path accepts; its operand
+// buffers in the workspace are sized for this many tokens.
+constexpr int64_t kGemvMaxT = 4096;
+// fp8 parts each activation is split into on the small-T path.
+constexpr int kParts = 3;
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+inline int64_t ldz_of(int64_t R) { return cdiv(R, 8) * 8; }
+inline int64_t max_colblocks(int64_t T) { return T + cdiv(T, 16) + 1; }
+
+// Byte offsets of the workspace regions.
+struct WsLayout {
+  size_t cbl, z, p1o, p1s, p2o, p2s, total;
+};
+
+inline WsLayout ws_layout(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T) {
+  (void)N;
+  WsLayout w{};
+  const int64_t tg = T < kGemvMaxT ? T : kGemvMaxT;
+  // small-T operands: [ell][tg][nkb][kParts][4] x 32 bytes, plus one scale byte each
+  const size_t n1 = (size_t)ell * tg * cdiv(M, kColBlock) * kParts * 4;
+  const size_t n2 = (size_t)ell * tg * cdiv(R, kColBlock) * kParts * 4;
+  size_t off = sizeof(WsHeader);
+  w.cbl = off;
+  off += align256((size_t)max_colblocks(T) * sizeof(ColBlock));
+  w.z = off;
+  off += align256((size_t)ell * T * ldz_of(R) * sizeof(float));
+  w.p1o = off;
+  off += align256(n1 * 32);
+  w.p1s = off;
+  off += align256(n1);
+  w.p2o = off;
+  off += align256(n2 * 32);
+  w.p2s = off;
+  off += align256(n2);
+  w.total = off;
+  return w;
+}
+
 size_t workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T);
 hipError_t launch_pack(const void* src, int dtype, int64_t rows, int64_t cols, int64_t ld,
                        uint32_t* dst, hipStream_t s);
@@ -42,5 +81,10 @@ hipError_t launch_unpack(const uint32_t* src, int64_t rows, int64_t cols, int8_t
                          hipStream_t s);
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s);
 Path choose_path(int64_t T, int64_t tokens_per_segment_estimate);
+// tokens per column block on the small-T path (3 fp8 parts x ell terms
+// x tokens must fit the 16 columns of one MFMA); 0 if ell is too large.
+inline int gemv_tokens_per_block(int32_t ell) { return ell <= 5 ? 16 / (kParts * ell) : 0; }
+hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_segment(const ForwardArgs& a, int chunk, hipStream_t s);
 
 }  // namespace dbf

@@ -10,14 +10,14 @@ import double_binary_rank_amd as dbf
 
 def pack_ref(S: np.ndarray) -> np.ndarray:
     """The packed words of sign(S) under the layout the library documents:
-    16-row tiles x 128-col blocks of 256 bytes, row-tile major; row rho of a
-    block owns words 4*rho..4*rho+3; slot s of a word at bit 4*(s%8)+s//8;
-    bit 1 means -1."""
+    16-row tiles x 128-col blocks of 256 bytes, row-tile major; word
+    16*q + rho of a block holds row rho, cols 32*q..32*q+31 of the block;
+    slot s of a word at bit 4*(s%8)+s//8; bit 1 means -1."""
     rows, cols = S.shape
     nrt, nkb = -(-rows // 16), -(-cols // 128)
     words = np.zeros(nrt * nkb * 64, dtype=np.uint64)
     r, k = np.nonzero(np.asarray(S) < 0)
-    idx = ((r // 16) * nkb + k // 128) * 64 + 4 * (r % 16) + (k % 128) // 32
+    idx = ((r // 16) * nkb + k // 128) * 64 + 16 * ((k % 128) // 32) + (r % 16)
     s = k % 32
     bit = 4 * (s % 8) + s // 8
     np.bitwise_or.at(words, idx, (np.uint64(1) << bit.astype(np.uint64)))
@@ -31,14 +31,31 @@ def to_dev(a, dtype=None):
     return t.cuda()
 
 
+def to_dev_rows(a, dtype=None, mult=8):
+    """2-D device tensor whose row stride is padded to a multiple of ``mult``
+    elements (the ABI wants 16-byte aligned rows); returns the [rows][cols]
+    view."""
+    a = np.asarray(a)
+    rows, cols = a.shape
+    ld = -(-max(cols, 1) // mult) * mult
+    t = torch.zeros((rows, ld), dtype=dtype or torch.from_numpy(a[:0]).dtype, device="cuda")
+    t[:, :cols] = to_dev(a, dtype)
+    return t[:, :cols]
+
+
+def empty_rows(rows, cols, dtype, mult=8):
+    ld = -(-max(cols, 1) // mult) * mult
+    return torch.empty((rows, ld), dtype=dtype, device="cuda")[:, :cols]
+
+
 def upload(L) -> dbf.PackedLayer:
     return dbf.PackedLayer.from_signs(L.S1, L.S2, L.alpha, L.beta, L.gamma, device="cuda")
 
 
 def run_layer(L, path=None, y_dtype=torch.float16, accumulate=False, y_init=None, pl=None):
     pl = pl or upload(L)
-    x = to_dev(L.x)
-    y = None if y_init is None else to_dev(y_init)
+    x = to_dev_rows(L.x)
+    y = empty_rows(L.T, L.N, y_dtype) if y_init is None else to_dev_rows(y_init)
     out = pl.forward(x, path=path, y_dtype=y_dtype, accumulate=accumulate, y=y)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
