@@ -117,13 +117,15 @@ def main():
                         y=y256, ws=ws)
 
     # ---------------------------------------------------- prefill T=256 --
-    sec = time_calls(call256, args.steps, args.warmup)
-    t_call = sec / args.steps
     flops = alg_flops(N_, R_, M_, 1, T)
     byts = alg_bytes(N_, R_, M_, 1, T)
-    value = T / t_call
-    achieved_tflops = flops / t_call / 1e12
-    log(f"prefill T=256: {t_call * 1e6:.2f} us/call, {achieved_tflops:.1f} TFLOP/s")
+    t_call = value = achieved_tflops = float("nan")
+    if want("prefill"):
+        sec = time_calls(call256, args.steps, args.warmup)
+        t_call = sec / args.steps
+        value = T / t_call
+        achieved_tflops = flops / t_call / 1e12
+        log(f"prefill T=256: {t_call * 1e6:.2f} us/call, {achieved_tflops:.1f} TFLOP/s")
 
     # ------------------------------------------------------ decode T=1 --
     if want("decode"):

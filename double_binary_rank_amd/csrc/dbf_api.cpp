@@ -68,8 +68,7 @@ const char* dbf_status_string(dbf_status s) {
 
 dbf_status dbf_packed_bytes(int64_t rows, int64_t cols, size_t* bytes) {
   if (rows <= 0 || cols <= 0 || bytes == nullptr) return DBF_ERR_INVALID_ARG;
-  *bytes = (size_t)cdiv(rows, dbf::kRowTile) * (size_t)cdiv(cols, dbf::kColBlock) *
-           (size_t)dbf::kBlockWords * 4u;
+  *bytes = (size_t)dbf::packed_words_total(rows, cols) * 4u;
   return DBF_OK;
 }
 

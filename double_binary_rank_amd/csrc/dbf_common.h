@@ -19,29 +19,40 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #define DBF_GLOBAL __attribute__((address_space(1)))
 typedef const DBF_GLOBAL uint32_t* gu32p;
 typedef const DBF_GLOBAL v8i* gv8ip;
+typedef const DBF_GLOBAL v4u* gv4up;
 
 // ---------------------------------------------------------------------------
 // Packed sign layout (one bit per sign; bit value 1 means -1).
 //
 // A rows x cols sign matrix is packed along cols (the reduction dimension of
-// its product).  Rows are grouped in tiles of 16, cols in blocks of 128.  Each
-// (row tile, col block) pair is one 256-byte block; blocks are stored row-tile
-// major: block (rt, kb) starts at word (rt * nkb + kb) * 64.  Inside a block
-// the 64 words are in matrix-core lane order: word lam = 16*q + rho holds
-// row rho (0..15) of the tile and cols kb*128 + 32*q + s, s = 0..31, which
-// is what lane lam of a 16x16x128 MFMA holds as its A operand.  Inside a
-// word, slot s sits at bit
+// its product).  Rows form tiles of 16 and quads of 4 tiles (64 rows); cols
+// form blocks of 128.  Each (row quad, col block) unit is 1 KB, units stored
+// quad-major: unit (rq, kb) starts at word (rq * nkb + kb) * 256.  Inside a
+// unit, lane lam (0..63) owns 4 consecutive words, one per row tile h of the
+// quad: word lam*4 + h holds row rho = lam % 16 of tile 4*rq + h and cols
+// kb*128 + 32*(lam/16) + s, s = 0..31 -- what lane lam of a 16x16x128 MFMA
+// holds as its A operand.  So one 16-byte load per lane brings the A operands
+// of four row tiles for one col block, and a wave's load is 1 KB contiguous.
+// Inside a word, slot s sits at bit
 //     b(s) = 4 * (s % 8) + s / 8
 // so that slots 8d..8d+7 occupy bits d, d+4, ..., d+28.  This order lets a
 // lane turn a word into fp4 operands with a shift and a mask per register:
 // ((w << (3-d)) & 0x88888888) | 0x22222222 is +-1.0 in e2m1 for 8 slots.
-// A 64-lane wave reading one block reads 256 contiguous bytes.
+// Padding rows and cols are +1 (bit 0).
 constexpr int kRowTile = 16;
+constexpr int kQuad = 4;
 constexpr int kColBlock = 128;
-constexpr int kBlockWords = 64;
+constexpr int kUnitWords = 256;
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int slot_bit(int s) { return 4 * (s & 7) + (s >> 3); }
+// word of (row tile rt, col block kb, lane lam) in a matrix with nkb col blocks
+__host__ __device__ inline int64_t packed_word(int64_t rt, int64_t kb, int lam, int64_t nkb) {
+  return ((rt >> 2) * nkb + kb) * kUnitWords + lam * 4 + (rt & 3);
+}
+__host__ __device__ inline int64_t packed_words_total(int64_t rows, int64_t cols) {
+  return cdiv(rows, kRowTile * kQuad) * cdiv(cols, kColBlock) * kUnitWords;
+}
 
 // One adapter's factors (device pointers).
 struct Factors {

@@ -69,26 +69,32 @@ struct PrepParams {
 // 128-block: lane group g holds bytes e = 0..15 for k = 16g + e and bytes
 // e = 16..31 for k = 64 + 16g + (e - 16).  (The fp4 operand holds 32
 // consecutive k = 32g + e; measured on gfx950 with one-hot operands.)
-__device__ inline int fp8_operand_k(int g, int e) { return e < 16 ? 16 * g + e : 48 + 16 * g + e; }
+// Byte offset of block entry k inside one part's 128 bytes:
+__device__ inline int fp8_operand_byte(int k) {
+  const int h = k >> 6, r = k & 63;           // half, position in the half
+  return (r >> 4) * 32 + h * 16 + (r & 15);   // lane group (r/16), byte e
+}
 
-// One thread per (term, token, 128-block, lane group g); the four threads of
-// a block are adjacent lanes.  Each loads the 32 values its lane group holds
-// in the fp8 operand order, then the block is split into kParts fp8 parts.
-// All four lane groups of a block share one E8M0 scale per part (the block
-// maximum is exchanged with two lane shuffles), so the scale covers the
-// whole 128-block whichever 32 of them the hardware attaches it to.
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// One wave per (term, token, 128-block); lane l owns entries 2l and 2l+1.
+// The block is split into kParts fp8 parts; each part has one E8M0 scale
+// for the whole block (the block maximum is a wave reduction), so the scale
+// is the same whichever 32 entries the hardware attaches a lane's scale to.
 __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)p.ell * p.T * p.nkb * 4;
-  const bool in = gid < total;  // out-of-range lanes still take part in the shuffles
-  const int64_t gq = in ? gid : total - 1;
-  const int g = (int)(gq & 3);
-  int64_t rest = gq >> 2;
-  const int64_t kb = rest % p.nkb;
-  rest /= p.nkb;
-  const int64_t t = rest % p.T;
-  const int64_t i = rest / p.T;
-  const int64_t kbase = kb * kColBlock;
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nblk = (int64_t)p.ell * p.T * p.nkb;
+  if (blk >= nblk) return;  // uniform per wave
+  const int64_t kb = blk % p.nkb;
+  const int64_t t = (blk / p.nkb) % p.T;
+  const int64_t i = blk / (p.nkb * p.T);
+  const int kl = 2 * lane;
+  const int64_t k = kb * kColBlock + kl;
 
   bool live = true;
   const half_t* gam = p.gamma;
@@ -97,53 +103,33 @@ __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
     live = ad >= 0 && ad < p.num_adapters;
     if (live && !p.from_z) gam = p.gammas[ad];
   }
-  float v[32];
-  if (!live) {
-#pragma unroll
-    for (int e = 0; e < 32; ++e) v[e] = 0.0f;
-  } else if (p.from_z) {
-    const float* zr = p.z + i * p.zstride + t * p.ldz;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int64_t k = kbase + fp8_operand_k(g, e);
-      v[e] = k < p.K ? zr[k] : 0.0f;
-    }
-  } else {
-    const half_t* gi = gam + i * p.K;
-    const half_t* xr = p.x + t * p.ldx;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int64_t k = kbase + fp8_operand_k(g, e);
-      v[e] = k < p.K ? (float)gi[k] * (float)xr[k] : 0.0f;
+  float v0 = 0.0f, v1 = 0.0f;
+  if (live) {
+    if (p.from_z) {
+      const float* zr = p.z + i * p.zstride + t * p.ldz;
+      if (k < p.K) v0 = zr[k];
+      if (k + 1 < p.K) v1 = zr[k + 1];
+    } else {
+      const half_t* gi = gam + i * p.K;
+      const half_t* xr = p.x + t * p.ldx;
+      if (k < p.K) v0 = (float)gi[k] * (float)xr[k];
+      if (k + 1 < p.K) v1 = (float)gi[k + 1] * (float)xr[k + 1];
     }
   }
-
-  const int64_t idx0 = ((i * p.T + t) * p.nkb + kb) * (kParts * 4);
+  uint8_t* out = (uint8_t*)p.opnd + blk * (kParts * 4 * 32);
+  const int boff = fp8_operand_byte(kl);  // kl even: entries kl, kl+1 are adjacent bytes
 #pragma unroll
   for (int part = 0; part < kParts; ++part) {
-    float mx = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(v[e]));
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
     int s = mx > 0.0f ? floor_log2_pos(mx) - 7 : 0;  // scaled block max in [128, 256)
     s = s < -127 ? -127 : (s > 127 ? 127 : s);
     const float down = __builtin_ldexpf(1.0f, -s), up = __builtin_ldexpf(1.0f, s);
-    uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      float q;
-      const uint32_t code = e4m3_rne(v[e] * down, q);
-      v[e] -= q * up;  // exact: q*up is v rounded on a grid no finer than v's own
-      words[e >> 2] |= code << (8 * (e & 3));
-    }
-    if (in) {
-      const int64_t idx = idx0 + part * 4 + g;
-      v4u* dst = (v4u*)(p.opnd + idx * 8);
-      dst[0] = v4u{words[0], words[1], words[2], words[3]};
-      dst[1] = v4u{words[4], words[5], words[6], words[7]};
-      p.oscl[idx] = (uint8_t)(s + 127);
-    }
+    float q0, q1;
+    const uint32_t c0 = e4m3_rne(v0 * down, q0), c1 = e4m3_rne(v1 * down, q1);
+    v0 -= q0 * up;  // exact: q*up is v rounded on a grid no finer than v's own
+    v1 -= q1 * up;
+    *(uint16_t*)(out + part * 128 + boff) = (uint16_t)(c0 | (c1 << 8));
+    if (lane < 4) p.oscl[blk * (kParts * 4) + part * 4 + lane] = (uint8_t)(s + 127);
   }
 }
 
@@ -152,19 +138,30 @@ __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
 // 32 sign slots of a packed word as fp4 (e2m1) +-1.0: register d holds slots
 // 8d..8d+7, slot 8d+j in nibble j.  Slot 8d+j is stored at bit 4j+d, so a
 // left shift by 3-d moves all eight sign bits to the nibble sign positions.
-__device__ inline v8i expand_signs_fp4(uint32_t w) {
+// The constants arrive as kernel arguments (0x88888888, 0x22222222) so that
+// they live in registers and each register costs one shift and one and-or.
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;  // (a & m) | c in one VALU op (ALU only; no memory access)
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+  return r;
+}
+
+__device__ inline v8i expand_signs_fp4(uint32_t w, uint32_t msk, uint32_t one) {
   v8i a;
-  a[0] = (int)(((w << 3) & 0x88888888u) | 0x22222222u);
-  a[1] = (int)(((w << 2) & 0x88888888u) | 0x22222222u);
-  a[2] = (int)(((w << 1) & 0x88888888u) | 0x22222222u);
-  a[3] = (int)((w & 0x88888888u) | 0x22222222u);
+  a[0] = (int)and_or(w << 3, msk, one);
+  a[1] = (int)and_or(w << 2, msk, one);
+  a[2] = (int)and_or(w << 1, msk, one);
+  a[3] = (int)and_or(w, msk, one);
   a[4] = a[5] = a[6] = a[7] = 0;
   return a;
 }
 
 struct GemvParams {
   int64_t rows, K, T, nrt, nkb, n_rg;
+  int64_t nq, n_qg;      // streaming kernel: row quads, quad groups per column block
+  int64_t lds_b, lds_s;  // streaming kernel: LDS bytes for staged B operands / their scales
   int32_t ell, tcb;
+  uint32_t sign_mask, fp4_one;  // 0x88888888, 0x22222222
   const uint32_t* opnd;
   const uint8_t* oscl;
   float* z;
@@ -183,16 +180,78 @@ struct GemvParams {
   const half_t* const* betas;
 };
 
+// Epilogue of one row tile: `sum` is the fp32 MFMA tile of this lane (rows
+// 4g..4g+3 of column j).  The kParts parts of a column sit in lanes j, j+1,
+// j+2 and are added in that order; stage 1 writes z_i = beta_i * u (fp32),
+// stage 2 sums alpha_i * w_i over the ell terms and writes y.  Every lane of
+// the wave must call this (it shuffles).
+// `srow` gives the per-row output scale of this lane's term (beta_ci for
+// stage 1, alpha_ci for stage 2): srow[r] for the rows of `tile`; with
+// SCALE_LDS it points into shared memory.
+template <int STAGE, bool SCALE_LDS = false>
+__device__ inline void gemv_epilogue(const GemvParams& p, const half_t* srow, v4f sum,
+                                     int64_t tile, int lane, int g, int part, bool colv, int ci,
+                                     int ct, int ntok, int64_t t0) {
+  const int64_t r0 = tile * kRowTile + 4 * g;
+  float tot[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float d1 = __shfl(sum[v], lane + 1 < 64 ? lane + 1 : lane);
+    const float d2 = __shfl(sum[v], lane + 2 < 64 ? lane + 2 : lane);
+    tot[v] = (sum[v] + d1) + d2;
+  }
+  float sc[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    if (SCALE_LDS)
+      sc[v] = (r0 + v < p.rows) ? (float)((const __attribute__((address_space(3))) half_t*)srow)[r0 + v]
+                                : 0.0f;
+    else
+      sc[v] = (r0 + v < p.rows) ? (float)srow[r0 + v] : 0.0f;
+  }
+  if (STAGE == 1) {
+    if (part == 0 && colv && r0 < p.rows) {
+      float o[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[v] = tot[v] * sc[v];
+      store4(p.z + ci * p.zstride, p.ldz, true, t0 + ct, r0, p.rows, o);
+    }
+  } else {
+    float val[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) val[v] = (part == 0 && colv) ? tot[v] * sc[v] : 0.0f;
+    // sum the ell terms of token ct: their part-0 lanes are 3*(i*ntok + ct)
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int ii = 0; ii < p.ell; ++ii) {
+      int src = 16 * g + kParts * (ii * ntok + ct);
+      src = src < 64 ? src : lane;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[v] += __shfl(val[v], src);
+    }
+    if (part == 0 && colv && ci == 0 && r0 < p.rows) {
+      if (p.accumulate) {
+        float old[4];
+        load4(p.y, p.ldy, p.y_f32, t0 + ct, r0, p.rows, old);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] += old[v];
+      }
+      store4(p.y, p.ldy, p.y_f32, t0 + ct, r0, p.rows, o);
+    }
+  }
+}
+
 // Work item: (column block of <= tcb tokens, group of RTG row tiles).  The
 // four waves split the reduction into interleaved chunks of KC blocks; each
 // wave keeps the B operands of its chunk in registers and streams the sign
 // blocks of all RTG row tiles against them.  Partial tiles are summed across
 // waves in a fixed order through LDS.
-template <int STAGE, int RTG>
+template <int STAGE, int RTG, int KC>
 __global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
-  constexpr int KC = 8;
   __shared__ v4f red[4][RTG][64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  static_assert(RTG % kQuad == 0, "row tiles come in quads");
+  constexpr int RQ = RTG / kQuad;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15, g = lane >> 4;
   const int c = j / kParts, part = j - kParts * (j / kParts);
   const int64_t n_cb = p.multi ? (int64_t)p.hdr->n_colblocks : p.n_cb_host;
@@ -241,15 +300,12 @@ __global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
     const int ci = colv ? c / ntok : 0, ct = colv ? c - ntok * (c / ntok) : 0;
     const uint32_t* __restrict__ S = STAGE == 1 ? f.B2 : f.B1;
 
-    v4f acc[RTG];
-#pragma unroll
-    for (int rt = 0; rt < RTG; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
-
     const int64_t nrt_here = (p.nrt - tile0) < RTG ? (p.nrt - tile0) : RTG;
+    const int nq_here = (int)((nrt_here + kQuad - 1) / kQuad);
+    bool first_chunk = true;
     for (int64_t kbase = 0; kbase < p.nkb; kbase += 4 * KC) {
       const int64_t kw0 = kbase + wv * KC;
       const int nk = (int)((p.nkb - kw0) < KC ? ((p.nkb - kw0) > 0 ? (p.nkb - kw0) : 0) : KC);
-      if (nk == 0) continue;
       v8i bop[KC];
       int bsc[KC];
 #pragma unroll
@@ -264,135 +320,332 @@ __global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
           bsc[kk] = 127;
         }
       }
-      gu32p base = (gu32p)S + (tile0 * p.nkb + kw0) * kBlockWords + lane;
-      const int64_t tstride = p.nkb * kBlockWords;  // words between row tiles
-      if (nk == KC && nrt_here == RTG) {
-        // full chunk: two row tiles at a time, the next pair prefetched
-        uint32_t wc[2][KC], wn[2][KC];
+      // lane's 16 bytes of unit (quad, block): the A words of its 4 row tiles
+      gv4up base = (gv4up)S + ((tile0 / kQuad) * p.nkb + kw0) * (kUnitWords / 4) + lane;
+      if (nk > 0) {
+        // every sign word of this round is requested before the first MFMA:
+        // RQ*KC 16-byte loads (16 KB per wave at RTG*KC = 64) in flight at once
+        v4u wd[RQ][KC];
 #pragma unroll
-        for (int h = 0; h < 2 && h < RTG; ++h)
+        for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
-          for (int kk = 0; kk < KC; ++kk) wc[h][kk] = base[h * tstride + kk * kBlockWords];
+          for (int kk = 0; kk < KC; ++kk)
+            wd[rq][kk] = (rq < nq_here && kk < nk) ? base[(rq * p.nkb + kk) * (kUnitWords / 4)]
+                                                   : v4u{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int rt = 0; rt < RTG; rt += 2) {
-          if (rt + 2 < RTG) {
+        for (int rq = 0; rq < RQ; ++rq) {
+          v4f a4[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int kk = 0; kk < KC; ++kk)
-                wn[h][kk] = base[(rt + 2 + h) * tstride + kk * kBlockWords];
-          }
+          for (int h = 0; h < 4; ++h) a4[h] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < KC; ++kk)
 #pragma unroll
-            for (int h = 0; h < 2 && rt + h < RTG; ++h)
-              acc[rt + h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  expand_signs_fp4(wc[h][kk]), bop[kk], acc[rt + h], 4 /* A: fp4 e2m1 */,
-                  0 /* B: fp8 e4m3 */, 0, 127 /* A scale 2^0 */, 0, bsc[kk]);
-          if (rt + 2 < RTG) {
+            for (int h = 0; h < 4; ++h)
+              a4[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  expand_signs_fp4(wd[rq][kk][h], p.sign_mask, p.fp4_one), bop[kk], a4[h],
+                  4 /* A: fp4 e2m1 */, 0 /* B: fp8 e4m3 */, 0, 127 /* A scale 2^0 */, 0,
+                  bsc[kk]);
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int kk = 0; kk < KC; ++kk) wc[h][kk] = wn[h][kk];
+          for (int h = 0; h < 4; ++h) {
+            const int rt = 4 * rq + h;
+            red[wv][rt][lane] = first_chunk ? a4[h] : red[wv][rt][lane] + a4[h];
           }
         }
-      } else {
-        // ragged chunk or last row-tile group
-#pragma unroll
-        for (int rt = 0; rt < RTG; ++rt) {
-          if (rt >= nrt_here) break;
-          uint32_t w[KC];
-#pragma unroll
-          for (int kk = 0; kk < KC; ++kk)
-            w[kk] = kk < nk ? base[rt * tstride + kk * kBlockWords] : 0u;
-#pragma unroll
-          for (int kk = 0; kk < KC; ++kk)
-            acc[rt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                expand_signs_fp4(w[kk]), bop[kk], acc[rt], 4, 0, 0, 127, 0, bsc[kk]);
-        }
+      } else if (first_chunk) {
+        for (int rt = 0; rt < RTG; ++rt) red[wv][rt][lane] = v4f{0.f, 0.f, 0.f, 0.f};
       }
+      first_chunk = false;
     }
 
-#pragma unroll
-    for (int rt = 0; rt < RTG; ++rt) red[wv][rt][lane] = acc[rt];
     __syncthreads();
     for (int rt = wv; rt < RTG; rt += 4) {
       const int64_t tile = tile0 + rt;
       if (tile >= p.nrt) break;
       const v4f sum = ((red[0][rt][lane] + red[1][rt][lane]) + red[2][rt][lane]) + red[3][rt][lane];
-      const int64_t r0 = tile * kRowTile + 4 * g;
-      float tot[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        // parts of one column sit in lanes j, j+1, j+2 (same row group)
-        const float d1 = __shfl(sum[v], lane + 1 < 64 ? lane + 1 : lane);
-        const float d2 = __shfl(sum[v], lane + 2 < 64 ? lane + 2 : lane);
-        tot[v] = (sum[v] + d1) + d2;
-      }
-      if (STAGE == 1) {
-        if (part == 0 && colv && r0 < p.rows) {
-          const half_t* bi = f.beta + (int64_t)ci * p.rows;
-          float o[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] = (r0 + v < p.rows) ? tot[v] * (float)bi[r0 + v] : 0.0f;
-          store4(p.z + ci * p.zstride, p.ldz, true, t0 + ct, r0, p.rows, o);
-        }
-      } else {
-        const half_t* ai = f.alpha + (int64_t)ci * p.rows;
-        float val[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          val[v] = (part == 0 && colv && r0 + v < p.rows) ? tot[v] * (float)ai[r0 + v] : 0.0f;
-        // sum the ell terms of token ct: their part-0 lanes are 3*(i*ntok + ct)
-        float o[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int ii = 0; ii < p.ell; ++ii) {
-          int src = 16 * g + kParts * (ii * ntok + ct);
-          src = src < 64 ? src : lane;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] += __shfl(val[v], src);
-        }
-        if (part == 0 && colv && ci == 0 && r0 < p.rows) {
-          if (p.accumulate) {
-            float old[4];
-            load4(p.y, p.ldy, p.y_f32, t0 + ct, r0, p.rows, old);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) o[v] += old[v];
-          }
-          store4(p.y, p.ldy, p.y_f32, t0 + ct, r0, p.rows, o);
-        }
-      }
+      const half_t* srow = (STAGE == 1 ? f.beta : f.alpha) + (int64_t)ci * p.rows;
+      gemv_epilogue<STAGE>(p, srow, sum, tile, lane, g, part, colv, ci, ct, ntok, t0);
     }
     __syncthreads();
   }
 }
 
+// Throughput kernel for many row quads (batched decode over many layers).
+// Work item: (column block, group of 4*QPW row quads); wave w of the
+// workgroup owns quads w, w+4, ... of the group over the WHOLE reduction, so
+// the main loop has no barrier and no cross-wave sum.  Per item, the B
+// operands of the live columns are staged once in LDS (in chunks of blocks
+// when they do not fit), together with the rows' output scales.  Each lane
+// streams its 16-byte A words through a ring of D registers: the load D
+// steps ahead is issued as a step is consumed, across quad boundaries (steps
+// are padded to a multiple of D per quad; padding and past-the-end loads read
+// a clamped in-range address, padding steps meet a zero B operand).  The
+// streaming loops hold loads and matrix ops only; tiles are parked in LDS and
+// finished by one epilogue loop.
+template <int STAGE, int QPW>
+__global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
+  constexpr int D = 8;
+  constexpr int ROWS_ITEM = 4 * QPW * kQuad * kRowTile;  // rows of one item
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // LDS: staged B operands [blocks][live column][g][32 B] (p.lds_b bytes),
+  // a 32-byte zero slot for lanes of unused columns, scales [blocks][16]
+  // (p.lds_s bytes), per-wave partial tiles [4][QPW][4][64] x 16 B, output
+  // scales [ell][ROWS_ITEM].
+  uint8_t* bl = smem;
+  uint8_t* zslot = smem + p.lds_b;  // 32 zero bytes, then 16 bytes of scale 127
+  uint8_t* bs = zslot + 48;
+  v4f* partial = (v4f*)(bs + p.lds_s);
+  half_t* srows = (half_t*)(partial + 4 * QPW * 4 * 64);
+  if (threadIdx.x < 2) *(v4u*)(zslot + 16 * threadIdx.x) = v4u{0u, 0u, 0u, 0u};
+  if (threadIdx.x == 2) *(v4u*)(zslot + 32) = v4u{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int c = j / kParts, part = j - kParts * (j / kParts);
+  const int64_t n_cb = p.multi ? (int64_t)p.hdr->n_colblocks : p.n_cb_host;
+  const int64_t n_items = n_cb * p.n_qg;
+
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int64_t cb = it / p.n_qg, qg = it % p.n_qg;
+    int64_t t0, t1;
+    int32_t ad;
+    Factors f;
+    if (p.multi) {
+      const ColBlock cbk = p.cbl[cb];
+      t0 = cbk.t0;
+      t1 = cbk.t1;
+      ad = cbk.adapter;
+      if (ad >= 0) {
+        f.B1 = p.B1s[ad];
+        f.B2 = p.B2s[ad];
+        f.alpha = p.alphas[ad];
+        f.beta = p.betas[ad];
+      }
+    } else {
+      t0 = cb * p.tcb;
+      t1 = t0 + p.tcb < p.T ? t0 + p.tcb : p.T;
+      ad = 0;
+      f = p.single;
+    }
+    const int64_t qbase = qg * 4 * QPW;
+    const int64_t row0 = qbase * kQuad * kRowTile;
+    if (ad < 0) {
+      if (STAGE == 2 && !p.accumulate) {
+        const int64_t nr = (p.rows - row0) < ROWS_ITEM ? (p.rows - row0) : ROWS_ITEM;
+        for (int64_t e = threadIdx.x; e < (t1 - t0) * nr; e += blockDim.x) {
+          const int64_t t = t0 + e / nr, r = row0 + e % nr;
+          if (p.y_f32)
+            ((float*)p.y)[t * p.ldy + r] = 0.0f;
+          else
+            ((half_t*)p.y)[t * p.ldy + r] = (half_t)0.0f;
+        }
+      }
+      continue;
+    }
+    const int ntok = (int)(t1 - t0);
+    const int ncols = kParts * p.ell * ntok;
+    const bool colv = j < ncols;
+    const int ci = colv ? c / ntok : 0, ct = colv ? c - ntok * (c / ntok) : 0;
+    const char* S = (const char*)(STAGE == 1 ? f.B2 : f.B1);
+    const int64_t qw0 = qbase + wv;  // this wave's quads: qw0 + 4*qi
+    int nqw = 0;
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi)
+      if (qw0 + 4 * qi < p.nq) nqw = qi + 1;
+    // blocks per chunk: this item's live columns must fit p.lds_b
+    // (padded to a multiple of D, which must fit too)
+    int64_t kchunk = p.lds_b / ((int64_t)ncols * 128);
+    kchunk = kchunk < p.lds_s / 16 ? kchunk : p.lds_s / 16;
+    kchunk = kchunk / D * D;
+    kchunk = kchunk > D ? kchunk : D;  // D blocks of 16 columns always fit p.lds_b
+    kchunk = kchunk < p.nkb ? kchunk : p.nkb;
+
+    for (int64_t k0 = 0; k0 < p.nkb; k0 += kchunk) {
+      const int64_t nkc = (p.nkb - k0) < kchunk ? (p.nkb - k0) : kchunk;
+      const int64_t nkc_pad = (nkc + D - 1) / D * D;
+      __syncthreads();  // every wave is done with the previous chunk's LDS
+      // stage the live B pieces (block, column, g, half) of 16 bytes at byte
+      // e*16; each thread issues all loads of a pass before its LDS writes
+      {
+        const int nlive = (int)nkc * ncols * 8;      // < 2^31 (LDS-bounded)
+        const int npiece = (int)nkc_pad * ncols * 8;  // padding blocks: zeros, scale 1.0
+        const int64_t tb = (int64_t)p.T * p.nkb * (kParts * 4);  // idx stride of one term
+        const int64_t ib = ((t0 * p.nkb + k0) * kParts) * 4;     // idx of (term 0, token t0, block k0)
+        constexpr int PT = 4;
+        for (int e0 = threadIdx.x; e0 < npiece; e0 += PT * (int)blockDim.x) {
+          v4u v[PT];
+          uint32_t sc[PT];
+#pragma unroll
+          for (int q = 0; q < PT; ++q) {
+            const int e = e0 + q * (int)blockDim.x;
+            const int ee = e < nlive ? e : 0;
+            const int half = ee & 1, gg = (ee >> 1) & 3;
+            const int rest = ee >> 3;
+            const int kbl = rest / ncols, col = rest - kbl * ncols;
+            const int cc = col / kParts, cpart = col - kParts * cc;
+            const int cci = cc / ntok, cct = cc - ntok * cci;
+            const int64_t idx = cci * tb + ib + ((int64_t)cct * p.nkb + kbl) * (kParts * 4) +
+                                cpart * 4 + gg;
+            v[q] = *(gv4up)(p.opnd + idx * 8 + half * 4);
+            sc[q] = p.oscl[idx];
+          }
+#pragma unroll
+          for (int q = 0; q < PT; ++q) {
+            const int e = e0 + q * (int)blockDim.x;
+            if (e < npiece) {
+              const bool lv = e < nlive;
+              *(v4u*)(bl + e * 16) = lv ? v[q] : v4u{0u, 0u, 0u, 0u};
+              if ((e & 7) == 0) {
+                const int rest = e >> 3, kbl = rest / ncols;
+                bs[kbl * 16 + (rest - kbl * ncols)] = lv ? (uint8_t)sc[q] : (uint8_t)127;
+              }
+            }
+          }
+        }
+      }
+      if (k0 == 0) {  // output scales of this item's rows, for every term
+        const half_t* sv = STAGE == 1 ? f.beta : f.alpha;
+        for (int e = threadIdx.x; e < p.ell * ROWS_ITEM; e += blockDim.x) {
+          const int i = e / ROWS_ITEM, rr = e - i * ROWS_ITEM;
+          srows[e] = (row0 + rr < p.rows) ? sv[(int64_t)i * p.rows + row0 + rr] : (half_t)0.0f;
+        }
+      }
+      __syncthreads();
+      if (nqw == 0) continue;
+
+      // A words: this wave's quads are contiguous runs of 1 KB units; the
+      // address is a uniform base plus lane*16 (scalar-base global loads)
+      const char* S0 = S + ((qw0 * p.nkb + k0) << 10);
+      const int64_t qbytes = (int64_t)4 * p.nkb << 10;  // between this wave's quads
+      const int lane16 = lane * 16;
+      const int nk = (int)nkc, nkp = (int)nkc_pad;
+      v4u ring[D];
+#pragma unroll
+      for (int u = 0; u < D; ++u) ring[u] = *(gv4up)(S0 + ((u < nk ? u : 0) << 10) + lane16);
+
+      v4f acc[QPW][4];
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) acc[qi][h] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) {
+        if (qi >= nqw) break;
+        const char* cur = S0 + qi * qbytes;
+        const char* nxt = (qi + 1 < nqw) ? cur + qbytes : cur;
+        for (int kb0 = 0; kb0 < nkp; kb0 += D) {
+          const bool same = kb0 + D < nkp;
+          const char* src = same ? cur : nxt;
+          const int kn0 = same ? kb0 + D : 0;
+          // lanes of live columns read [kb][j][g] (padding blocks are staged
+          // zeros); the others read the zero slot with stride 0
+          const uint8_t* bstep = colv ? bl + ((kb0 * ncols + j) * 4 + g) * 32 : zslot;
+          const int bstride = colv ? ncols * 128 : 0;
+          const uint8_t* sstep = colv ? bs + kb0 * 16 + j : zslot + 32;
+          const int sstride = colv ? 16 : 0;
+#pragma unroll
+          for (int u = 0; u < D; ++u) {
+            // expand the slot's four words, then refill the slot; the refill
+            // stays after the last read of the old value so the slot keeps
+            // its register (copying an in-flight slot would drain the queue)
+            const v4u w = ring[u];
+            const v8i a0 = expand_signs_fp4(w[0], p.sign_mask, p.fp4_one);
+            const v8i a1 = expand_signs_fp4(w[1], p.sign_mask, p.fp4_one);
+            const v8i a2 = expand_signs_fp4(w[2], p.sign_mask, p.fp4_one);
+            const v8i a3 = expand_signs_fp4(w[3], p.sign_mask, p.fp4_one);
+            __builtin_amdgcn_sched_barrier(0);
+            const int kn = kn0 + u < nk ? kn0 + u : 0;
+            ring[u] = *(gv4up)(src + (kn << 10) + lane16);
+            const uint8_t* bp = bstep + u * bstride;
+            const v4u lo = *(const v4u*)bp, hi = *(const v4u*)(bp + 16);
+            const v8i bop = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            const int bsc = sstep[u * sstride];
+            acc[qi][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, bop, acc[qi][0], 4, 0,
+                                                                           0, 127, 0, bsc);
+            acc[qi][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, bop, acc[qi][1], 4, 0,
+                                                                           0, 127, 0, bsc);
+            acc[qi][2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, bop, acc[qi][2], 4, 0,
+                                                                           0, 127, 0, bsc);
+            acc[qi][3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a3, bop, acc[qi][3], 4, 0,
+                                                                           0, 127, 0, bsc);
+          }
+        }
+      }
+      // park this chunk's tiles in the wave's own LDS partials
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) {
+        if (qi >= nqw) break;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          v4f* slot = partial + ((wv * QPW + qi) * 4 + h) * 64 + lane;
+          *slot = (k0 == 0) ? acc[qi][h] : *slot + acc[qi][h];
+        }
+      }
+    }
+    // epilogue of this wave's tiles (its own partials; the scales were
+    // staged before the last barrier)
+    const half_t* srow = srows + ci * ROWS_ITEM - row0;
+    for (int e = 0; e < nqw * 4; ++e) {
+      const int64_t tile = (qw0 + 4 * (e >> 2)) * kQuad + (e & 3);
+      if (tile < p.nrt)
+        gemv_epilogue<STAGE, true>(p, srow, partial[(wv * QPW * 4 + e) * 64 + lane], tile, lane, g,
+                                   part, colv, ci, ct, ntok, t0);
+    }
+  }
+}
+
 // -------------------------------------------------------------- launch ----
 
-template <int STAGE, int RTG>
+template <int STAGE, int RTG, int KC>
 static hipError_t launch_gemv_stage(const GemvParams& p, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv_fp4<STAGE, RTG>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_gemv_fp4<STAGE, RTG, KC>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
+
+// Tile choice: KC reduction blocks per wave chunk (8, or 4 when the four
+// waves would otherwise idle), RTG row tiles per item with RTG*KC <= 64 sign
+// words per lane in flight; fewer row tiles per item when there are too few
+// items to fill the GPU.
+constexpr int kStreamQPW = 2;
+constexpr int64_t kStreamLdsB = 32 * 1024;  // LDS budget for staged B operands
 
 template <int STAGE>
 static hipError_t launch_gemv_stage_any(GemvParams p, int64_t n_cb_est, int64_t n_cb_max,
                                         bool multi, hipStream_t s) {
-  int rtg = 1;
-  if (n_cb_est * cdiv(p.nrt, 16) >= 1024)
-    rtg = 16;
-  else if (n_cb_est * cdiv(p.nrt, 4) >= 1024)
-    rtg = 4;
+  p.nq = cdiv(p.nrt, kQuad);
+  if (n_cb_est * p.nq >= 1024) {
+    // many quads: streaming kernel
+    p.lds_b = kStreamLdsB;
+    p.lds_s = 16 * (cdiv(p.nkb, 8) * 8 < 256 ? cdiv(p.nkb, 8) * 8 : 256);
+    p.n_qg = cdiv(p.nq, 4 * kStreamQPW);
+    const size_t lds = (size_t)p.lds_b + 48 + (size_t)p.lds_s +
+                       (size_t)4 * kStreamQPW * 4 * 64 * 16 +
+                       (size_t)p.ell * 4 * kStreamQPW * kQuad * kRowTile * sizeof(half_t);
+    int64_t grid = n_cb_max * p.n_qg;
+    if (grid > 2048) grid = 2048;
+    hipLaunchKernelGGL((k_gemv_stream<STAGE, kStreamQPW>), dim3((unsigned)grid), dim3(256), lds, s,
+                       p);
+    return hipGetLastError();
+  }
+  const int kc = p.nkb > 16 ? 8 : 4;
+  const int rtg_max = 64 / kc;
+  int rtg = 4;
+  if (n_cb_est * cdiv(p.nrt, rtg_max) >= 1024) rtg = rtg_max;
   p.n_rg = cdiv(p.nrt, rtg);
   int64_t grid = n_cb_max * p.n_rg;
   if (multi && grid > 4096) grid = 4096;
-  if (rtg == 16) return launch_gemv_stage<STAGE, 16>(p, grid, s);
-  if (rtg == 4) return launch_gemv_stage<STAGE, 4>(p, grid, s);
-  return launch_gemv_stage<STAGE, 1>(p, grid, s);
+  if (kc == 8) {
+    if (rtg == 8) return launch_gemv_stage<STAGE, 8, 8>(p, grid, s);
+    return launch_gemv_stage<STAGE, 4, 8>(p, grid, s);
+  }
+  if (rtg == 16) return launch_gemv_stage<STAGE, 16, 4>(p, grid, s);
+  return launch_gemv_stage<STAGE, 4, 4>(p, grid, s);
 }
 
 static hipError_t launch_prep(PrepParams p, hipStream_t s) {
-  const int64_t total = (int64_t)p.ell * p.T * p.nkb * 4;
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, p);
+  const int64_t nblk = (int64_t)p.ell * p.T * p.nkb;
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)cdiv(nblk, 4)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -430,6 +683,8 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
   pp.gammas = a.gammas;
 
   GemvParams gp{};
+  gp.sign_mask = 0x88888888u;
+  gp.fp4_one = 0x22222222u;
   gp.T = a.T;
   gp.ell = a.ell;
   gp.tcb = tcb;

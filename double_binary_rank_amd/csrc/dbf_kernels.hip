@@ -19,11 +19,11 @@ __global__ void k_pack(const void* __restrict__ src, int dtype, int64_t rows, in
                        int64_t ld, int64_t nkb, int64_t total_words, uint32_t* __restrict__ dst) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total_words) return;
-  const int64_t blk = gid / kBlockWords;
-  const int w = (int)(gid % kBlockWords);
-  const int rho = w & 15, q = w >> 4;
-  const int64_t row = (blk / nkb) * kRowTile + rho;
-  const int64_t k0 = (blk % nkb) * kColBlock + 32 * q;
+  const int64_t unit = gid / kUnitWords;
+  const int w = (int)(gid % kUnitWords);
+  const int lam = w >> 2, h = w & 3;
+  const int64_t row = ((unit / nkb) * kQuad + h) * kRowTile + (lam & 15);
+  const int64_t k0 = (unit % nkb) * kColBlock + 32 * (lam >> 4);
   uint32_t word = 0;
   if (row < rows) {
     const int64_t base = row * ld;
@@ -47,10 +47,11 @@ __global__ void k_unpack(const uint32_t* __restrict__ src, int64_t rows, int64_t
                          int64_t total_words, int8_t* __restrict__ dst, int64_t ld) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total_words) return;
-  const int64_t blk = gid / kBlockWords;
-  const int w = (int)(gid % kBlockWords);
-  const int64_t row = (blk / nkb) * kRowTile + (w & 15);
-  const int64_t k0 = (blk % nkb) * kColBlock + 32 * (w >> 4);
+  const int64_t unit = gid / kUnitWords;
+  const int w = (int)(gid % kUnitWords);
+  const int lam = w >> 2, h = w & 3;
+  const int64_t row = ((unit / nkb) * kQuad + h) * kRowTile + (lam & 15);
+  const int64_t k0 = (unit % nkb) * kColBlock + 32 * (lam >> 4);
   if (row >= rows) return;
   const uint32_t word = src[gid];
   for (int s = 0; s < 32; ++s) {
@@ -63,7 +64,7 @@ __global__ void k_unpack(const uint32_t* __restrict__ src, int64_t rows, int64_t
 hipError_t launch_pack(const void* src, int dtype, int64_t rows, int64_t cols, int64_t ld,
                        uint32_t* dst, hipStream_t s) {
   const int64_t nkb = cdiv(cols, kColBlock);
-  const int64_t total = cdiv(rows, kRowTile) * nkb * kBlockWords;
+  const int64_t total = packed_words_total(rows, cols);
   const int64_t grid = cdiv(total, 256);
   hipLaunchKernelGGL(k_pack, dim3((unsigned)grid), dim3(256), 0, s, src, dtype, rows, cols, ld,
                      nkb, total, dst);
@@ -73,7 +74,7 @@ hipError_t launch_pack(const void* src, int dtype, int64_t rows, int64_t cols, i
 hipError_t launch_unpack(const uint32_t* src, int64_t rows, int64_t cols, int8_t* dst, int64_t ld,
                          hipStream_t s) {
   const int64_t nkb = cdiv(cols, kColBlock);
-  const int64_t total = cdiv(rows, kRowTile) * nkb * kBlockWords;
+  const int64_t total = packed_words_total(rows, cols);
   const int64_t grid = cdiv(total, 256);
   hipLaunchKernelGGL(k_unpack, dim3((unsigned)grid), dim3(256), 0, s, src, rows, cols, nkb, total,
                      dst, ld);
@@ -177,7 +178,8 @@ struct StageParams {
 template <int STAGE, int RW, int CW>
 __global__ __launch_bounds__(256) void k_stage_f16(StageParams p) {
   __shared__ float red[3][RW * CW * 4][64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int64_t n_cb = p.multi ? (int64_t)p.hdr->n_colblocks : p.n_cb_host;
   const int64_t n_items = n_cb * p.nrb;
@@ -245,9 +247,9 @@ __global__ __launch_bounds__(256) void k_stage_f16(StageParams p) {
 #pragma unroll
         for (int rt = 0; rt < RW; ++rt) {
           const int64_t tile = row0 / 16 + rt;
-          const uint32_t* blk = S + (tile * p.nkb + kb) * kBlockWords + c16;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) wd[rt][q] = tile < p.nrt ? blk[16 * q] : 0u;
+          for (int q = 0; q < 4; ++q)
+            wd[rt][q] = tile < p.nrt ? S[packed_word(tile, kb, 16 * q + c16, p.nkb)] : 0u;
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {

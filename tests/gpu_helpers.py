@@ -10,14 +10,16 @@ import double_binary_rank_amd as dbf
 
 def pack_ref(S: np.ndarray) -> np.ndarray:
     """The packed words of sign(S) under the layout the library documents:
-    16-row tiles x 128-col blocks of 256 bytes, row-tile major; word
-    16*q + rho of a block holds row rho, cols 32*q..32*q+31 of the block;
-    slot s of a word at bit 4*(s%8)+s//8; bit 1 means -1."""
+    units of 64 rows (4 tiles of 16) x 128 cols, 1 KB each, quad-major;
+    in a unit, word 4*lam + h holds row lam%16 of tile h and cols
+    32*(lam//16) .. +31 of the block; slot s of a word at bit 4*(s%8)+s//8;
+    bit 1 means -1."""
     rows, cols = S.shape
-    nrt, nkb = -(-rows // 16), -(-cols // 128)
-    words = np.zeros(nrt * nkb * 64, dtype=np.uint64)
+    nq, nkb = -(-rows // 64), -(-cols // 128)
+    words = np.zeros(nq * nkb * 256, dtype=np.uint64)
     r, k = np.nonzero(np.asarray(S) < 0)
-    idx = ((r // 16) * nkb + k // 128) * 64 + 16 * ((k % 128) // 32) + (r % 16)
+    lam = 16 * ((k % 128) // 32) + (r % 16)
+    idx = ((r // 64) * nkb + k // 128) * 256 + 4 * lam + (r % 64) // 16
     s = k % 32
     bit = 4 * (s % 8) + s // 8
     np.bitwise_or.at(words, idx, (np.uint64(1) << bit.astype(np.uint64)))

@@ -33,12 +33,13 @@ def test_version_and_strings():
     assert _lib.status_string(-99) == "unknown dbf_status"
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 1), (16, 128), (17, 129), (4096, 2048), (14336, 6368)])
+@pytest.mark.parametrize("rows,cols", [(1, 1), (64, 128), (65, 129), (4096, 2048), (14336, 6368)])
 def test_packed_bytes_closed_form(rows, cols):
-    want = -(-rows // 16) * -(-cols // 128) * 256
+    want = -(-rows // 64) * -(-cols // 128) * 1024
     assert _lib.packed_bytes(rows, cols) == want
     assert want * 8 >= rows * cols  # at least one bit per sign
-    assert want * 8 - rows * cols < (16 * cols + 128 * rows + 16 * 128) * 2  # padding < one tile each way
+    # padding is less than one 64-row x 128-col unit in each direction
+    assert want * 8 < (rows + 64) * (cols + 128)
 
 
 def test_packed_bytes_errors():

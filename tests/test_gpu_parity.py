@@ -266,3 +266,24 @@ def test_multi_equals_single():
     ys = D.layers[2].forward(x, path="gemv")
     torch.cuda.synchronize()
     assert torch.equal(ym, ys)
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_multi_adapter_stream_path(integer):
+    """Many adapters with <= 5 tokens each: the decode path's streaming kernel
+    (row quads spread over all waves, reduction chunked through LDS when the
+    staged operands of a 36-block reduction do not fit at once)."""
+    kind = dict(alpha="ones", beta="ones", gamma="ones", x_kind="int3") if integer else {}
+    B = synth.make_multi_adapter(num_adapters=64, N=1024, R=1100, M=4608, ell=1, T=300, seed=55,
+                                 **kind)
+    ids = np.repeat(np.arange(64, dtype=np.int32), 5)[:300]
+    D = H().DeviceAdapters(B.adapters)
+    y = D.forward(H().to_dev(B.x), H().to_dev(ids), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = _multi_ref(B, ids)
+    if integer:
+        assert np.array_equal(y.cpu().numpy().astype(np.float64),
+                              want.astype(np.float32).astype(np.float64))
+    else:
+        err = oracle.max_norm_error(y.cpu().numpy(), want)
+        assert err <= TOL, err
