@@ -23,6 +23,8 @@ dbf_status check_common(const void* x, int64_t ldx, int64_t N, int64_t R, int64_
                         int64_t T, void* y, int64_t ldy, dbf_dtype y_type, uint32_t flags,
                         void* ws, size_t ws_bytes) {
   if (N <= 0 || R <= 0 || M <= 0 || ell < 1 || T < 0) return DBF_ERR_INVALID_ARG;
+  if (N > DBF_MAX_DIM || R > DBF_MAX_DIM || M > DBF_MAX_DIM || T > DBF_MAX_DIM)
+    return DBF_ERR_INVALID_ARG;
   if (!valid_dtype_out(y_type)) return DBF_ERR_INVALID_ARG;
   if (flags & ~kKnownFlags) return DBF_ERR_INVALID_ARG;
   if ((flags & DBF_PATH_GEMV) && (flags & DBF_PATH_MFMA)) return DBF_ERR_INVALID_ARG;

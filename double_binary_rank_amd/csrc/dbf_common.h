@@ -29,10 +29,14 @@ typedef const DBF_GLOBAL v4u* gv4up;
 // form blocks of 128.  Each (row quad, col block) unit is 1 KB, units stored
 // quad-major: unit (rq, kb) starts at word (rq * nkb + kb) * 256.  Inside a
 // unit, lane lam (0..63) owns 4 consecutive words, one per row tile h of the
-// quad: word lam*4 + h holds row rho = lam % 16 of tile 4*rq + h and cols
-// kb*128 + 32*(lam/16) + s, s = 0..31 -- what lane lam of a 16x16x128 MFMA
-// holds as its A operand.  So one 16-byte load per lane brings the A operands
-// of four row tiles for one col block, and a wave's load is 1 KB contiguous.
+// quad: word lam*4 + h holds row rho = lam % 16 of tile 4*rq + h.  With lane
+// group g = lam / 16, slot s = 0..31 of the word is col
+//     kb*128 + slot_col(g, s),   slot_col(g, s) = 32*(s/8) + 8*g + s%8,
+// i.e. the two 2-bit fields of the block-local col index are (s/8, g).  One
+// 16-byte load per lane brings four row tiles' words for one col block, and
+// a wave's load is 1 KB contiguous.  The col order makes the eight slots
+// 8j..8j+7 of the four lane groups one contiguous run of 32 cols, so the
+// activations that meet them are read 64 bytes at a time per token.
 // Inside a word, slot s sits at bit
 //     b(s) = 4 * (s % 8) + s / 8
 // so that slots 8d..8d+7 occupy bits d, d+4, ..., d+28.  This order lets a
@@ -46,6 +50,8 @@ constexpr int kUnitWords = 256;
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int slot_bit(int s) { return 4 * (s & 7) + (s >> 3); }
+// block-local col of slot s in a word of lane group g (see above)
+__host__ __device__ inline int slot_col(int g, int s) { return 32 * (s >> 3) + 8 * g + (s & 7); }
 // word of (row tile rt, col block kb, lane lam) in a matrix with nkb col blocks
 __host__ __device__ inline int64_t packed_word(int64_t rt, int64_t kb, int lam, int64_t nkb) {
   return ((rt >> 2) * nkb + kb) * kUnitWords + lam * 4 + (rt & 3);

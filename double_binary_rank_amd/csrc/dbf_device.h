@@ -7,6 +7,16 @@ namespace dbf {
 
 typedef half_t v4h __attribute__((ext_vector_type(4)));
 
+// (a & m) | c in one VALU op (ALU only; no memory access).  gfx950 VOP3
+// encodings take no literal constants, so m and c come from registers (m a
+// wave-uniform SGPR, c a VGPR): the compiler would otherwise emit a separate
+// and plus or with literals.
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+  return r;
+}
+
 __device__ inline void store4(void* y, int64_t ldy, bool f32, int64_t t, int64_t r, int64_t rows,
                               const float v[4]) {
   if (f32) {

@@ -69,10 +69,17 @@ struct PrepParams {
 // 128-block: lane group g holds bytes e = 0..15 for k = 16g + e and bytes
 // e = 16..31 for k = 64 + 16g + (e - 16).  (The fp4 operand holds 32
 // consecutive k = 32g + e; measured on gfx950 with one-hot operands.)
-// Byte offset of block entry k inside one part's 128 bytes:
+// Byte offset of the operand's k-th entry inside one part's 128 bytes:
 __device__ inline int fp8_operand_byte(int k) {
   const int h = k >> 6, r = k & 63;           // half, position in the half
   return (r >> 4) * 32 + h * 16 + (r & 15);   // lane group (r/16), byte e
+}
+
+// The fp4 operand's k-th entry (lane group k/32, slot k%32) carries the sign
+// of block col slot_col(k/32, k%32); the inverse swaps the same two 2-bit
+// fields of the col index, so col c meets operand entry
+__device__ inline int operand_k_of_col(int c) {
+  return ((c & 0x18) << 2) | ((c & 0x60) >> 2) | (c & 7);
 }
 
 __device__ inline float wave_max(float v) {
@@ -117,7 +124,8 @@ __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
     }
   }
   uint8_t* out = (uint8_t*)p.opnd + blk * (kParts * 4 * 32);
-  const int boff = fp8_operand_byte(kl);  // kl even: entries kl, kl+1 are adjacent bytes
+  // kl even: cols kl, kl+1 meet adjacent operand entries, i.e. adjacent bytes
+  const int boff = fp8_operand_byte(operand_k_of_col(kl));
 #pragma unroll
   for (int part = 0; part < kParts; ++part) {
     const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
@@ -140,11 +148,6 @@ __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
 // left shift by 3-d moves all eight sign bits to the nibble sign positions.
 // The constants arrive as kernel arguments (0x88888888, 0x22222222) so that
 // they live in registers and each register costs one shift and one and-or.
-__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t r;  // (a & m) | c in one VALU op (ALU only; no memory access)
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
-  return r;
-}
 
 __device__ inline v8i expand_signs_fp4(uint32_t w, uint32_t msk, uint32_t one) {
   v8i a;

@@ -60,6 +60,10 @@ typedef int32_t dbf_dtype;
 
 #define DBF_ABI_VERSION 1
 
+/* Largest N, R, M or T accepted by dbf_forward / dbf_forward_multi_adapter
+   (the kernels index rows, columns and tokens with 32-bit integers). */
+#define DBF_MAX_DIM (((int64_t)1) << 30)
+
 /* ABI version of the loaded library (DBF_ABI_VERSION it was built with). */
 int32_t dbf_abi_version(void);
 
@@ -70,8 +74,8 @@ const char* dbf_status_string(dbf_status s);
  * Bytes of the packed form of a rows x cols sign matrix, packed along cols
  * (the reduction dimension of its product).  One bit per sign (LoRDBA
  * summary, section 2 "Eficiencia de Almacenamiento"); rows are padded to a
- * multiple of 16 and cols to a multiple of 128, so the size is
- * ceil(rows/16) * ceil(cols/128) * 256.  The layout itself is internal.
+ * multiple of 64 and cols to a multiple of 128, so the size is
+ * ceil(rows/64) * ceil(cols/128) * 1024.  The layout itself is internal.
  * Errors: INVALID_ARG if rows <= 0, cols <= 0 or bytes == NULL.
  */
 dbf_status dbf_packed_bytes(int64_t rows, int64_t cols, size_t* bytes);
@@ -119,8 +123,8 @@ dbf_status dbf_workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int
  * Alignment: x, y, B1, B2 and ws 16-byte aligned; ldx a multiple of 8;
  * ldy a multiple of 8 (fp16 y) or 4 (fp32 y).
  * T == 0 is a successful no-op (x, y and ws may then be NULL).
- * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE (ws_bytes below
- * dbf_workspace_bytes), HIP.
+ * Errors: INVALID_ARG (also for N, R, M or T above DBF_MAX_DIM), ALIGNMENT,
+ * WORKSPACE (ws_bytes below dbf_workspace_bytes), HIP.
  */
 dbf_status dbf_forward(const void* x, int64_t ldx, const uint32_t* B1, const uint32_t* B2,
                        const void* alpha, const void* beta, const void* gamma, int64_t N,

@@ -11,16 +11,18 @@ import double_binary_rank_amd as dbf
 def pack_ref(S: np.ndarray) -> np.ndarray:
     """The packed words of sign(S) under the layout the library documents:
     units of 64 rows (4 tiles of 16) x 128 cols, 1 KB each, quad-major;
-    in a unit, word 4*lam + h holds row lam%16 of tile h and cols
-    32*(lam//16) .. +31 of the block; slot s of a word at bit 4*(s%8)+s//8;
-    bit 1 means -1."""
+    in a unit, word 4*lam + h holds row lam%16 of tile h; with g = lam//16,
+    slot s of that word is block col 32*(s//8) + 8*g + s%8 and sits at bit
+    4*(s%8) + s//8; bit 1 means -1."""
     rows, cols = S.shape
     nq, nkb = -(-rows // 64), -(-cols // 128)
     words = np.zeros(nq * nkb * 256, dtype=np.uint64)
     r, k = np.nonzero(np.asarray(S) < 0)
-    lam = 16 * ((k % 128) // 32) + (r % 16)
+    c = k % 128
+    g = (c // 8) % 4
+    s = 8 * (c // 32) + c % 8
+    lam = 16 * g + (r % 16)
     idx = ((r // 64) * nkb + k // 128) * 256 + 4 * lam + (r % 64) // 16
-    s = k % 32
     bit = 4 * (s % 8) + s // 8
     np.bitwise_or.at(words, idx, (np.uint64(1) << bit.astype(np.uint64)))
     return words.astype(np.uint32)

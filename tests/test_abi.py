@@ -77,6 +77,8 @@ def _fwd(**kw):
     (dict(M=0), _lib.DBF_ERR_INVALID_ARG),
     (dict(ell=0), _lib.DBF_ERR_INVALID_ARG),
     (dict(T=-1), _lib.DBF_ERR_INVALID_ARG),
+    (dict(N=(1 << 30) + 1), _lib.DBF_ERR_INVALID_ARG),
+    (dict(T=(1 << 30) + 1), _lib.DBF_ERR_INVALID_ARG),
     (dict(x=None), _lib.DBF_ERR_INVALID_ARG),
     (dict(y=None), _lib.DBF_ERR_INVALID_ARG),
     (dict(B1=None), _lib.DBF_ERR_INVALID_ARG),
