@@ -21,8 +21,9 @@
 // per wave, each over the whole reduction (for short reductions).  Output
 // column j of an MFMA depends only on operand column j, so columns of tokens
 // past the block's end read a valid token's row and are simply not stored.
-// Stage 1 writes z_i = beta_i * u_i as fp16 into the workspace; stage 2 reads
-// it and writes y = sum_i alpha_i * (B1 z_i).
+// Stage 1 writes z_i = beta_i * u_i as fp16 into the workspace, in the order
+// stage 2's MFMA operands take it (so each of its operand loads is 1 KB
+// contiguous); stage 2 writes y = sum_i alpha_i * (B1 z_i).
 #include "dbf_device.h"
 #include "dbf_launch.h"
 
@@ -39,8 +40,9 @@ struct GemmParams {
   uint32_t msk16, one16;  // 0x80008000, 0x3C003C00 (kept in registers)
   const half_t* x;
   int64_t ldx;
-  half_t* zh;
-  int64_t ldzh, zhstride;  // z_i[t][r] at zh + i*zhstride + t*ldzh + r (fp16)
+  half_t* zt;         // z_i, fp16 in MFMA operand order (see zt_term_halfs)
+  int64_t zt_term;    // halfs per term
+  int32_t zt_nkb;     // 128-row blocks of z
   void* y;
   int64_t ldy;
   Factors single;
@@ -80,15 +82,22 @@ struct Block {
   v8h gm[4];
 };
 
+// arow[c]: stage 1, the row of x of token column c (plus 8g); stage 2, the
+// lane's 16 bytes of that token's z tile row, so step s of block kb sits at
+// arow[c] + kb*2048 + s*512.
+template <int STAGE, int NC>
+__device__ inline const half_t* act_ptr(const half_t* arow, int kb, int s) {
+  return STAGE == 1 ? arow + kb * kColBlock + 32 * s : arow + (int64_t)kb * 2048 + s * 512;
+}
+
 template <int STAGE, int NC>
 __device__ inline void load_full(Block<STAGE, NC>& B, const char* sq, const half_t* const (&arow)[NC],
                                  int kb, int g) {
   B.a = *(gv4up)(sq + ((int64_t)kb << 10));
-  const int kbase = kb * kColBlock + 8 * g;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) B.b[s][c] = *(gv8hp)(arow[c] + kbase + 32 * s);
+    for (int c = 0; c < NC; ++c) B.b[s][c] = *(gv8hp)act_ptr<STAGE, NC>(arow[c], kb, s);
 }
 
 // gamma of block kb from the LDS window that starts at block wb0
@@ -102,16 +111,14 @@ __device__ inline void load_gamma(Block<STAGE, NC>& B, const half_t* gl, int kb,
 }
 
 // The last, partial 128-block: activations past K are zero (the padding
-// signs are +1, so they must not contribute).
+// signs are +1, so they must not contribute).  Cold code: not unrolled.
 template <int STAGE, int NC>
 __device__ inline void load_tail(Block<STAGE, NC>& B, const char* sq, const half_t* const (&arow)[NC],
                                  const half_t* gam, int kb, int g, int K) {
   B.a = *(gv4up)(sq + ((int64_t)kb << 10));
   const int kbase = kb * kColBlock + 8 * g;
-#pragma unroll
   for (int s = 0; s < 4; ++s) {
     v8h gv = {};
-#pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int k = kbase + 32 * s + e;
       if (STAGE == 1 && k < K) gv[e] = gam[k];
@@ -120,10 +127,16 @@ __device__ inline void load_tail(Block<STAGE, NC>& B, const char* sq, const half
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       v8h v = {};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = kbase + 32 * s + e;
-        if (k < K) v[e] = arow[c][k];
+      if (STAGE == 1) {
+        for (int e = 0; e < 8; ++e) {
+          const int k = kbase + 32 * s + e;
+          if (k < K) v[e] = arow[c][k - 8 * g];  // arow already points 8g in
+        }
+      } else if (kbase + 32 * s < K) {
+        // the z tile spans the whole block; rows past K are not written
+        v = *(gv8hp)act_ptr<STAGE, NC>(arow[c], kb, s);
+        for (int e = 0; e < 8; ++e)
+          if (kbase + 32 * s + e >= K) v[e] = (half_t)0.0f;
       }
       B.b[s][c] = v;
     }
@@ -225,14 +238,17 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
       // row scales of this wave's quad (lane L: row 64q + L), issued first so
       // that their latency hides behind the reduction; lanes fetch the ones
       // they need with a cross-lane read at the end
+      // (kept as loaded; converting here would wait for the load)
       const half_t* sv = (STAGE == 1 ? f.beta : f.alpha) + (int64_t)i * p.rows;
       const int srow = q * kQuad * kRowTile + lane;
-      const float scl = (active && srow < p.rows) ? (float)sv[srow] : 0.0f;
+      const half_t sclh = sv[min(srow, p.rows - 1)];
       const half_t* arow[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int t = min(t0 + 16 * c + c16, t1 - 1);
-        arow[c] = STAGE == 1 ? p.x + (int64_t)t * p.ldx : p.zh + i * p.zhstride + (int64_t)t * p.ldzh;
+        arow[c] = STAGE == 1 ? p.x + (int64_t)t * p.ldx + 8 * g
+                             : p.zt + i * p.zt_term + (int64_t)(t >> 4) * p.zt_nkb * 2048 +
+                                   (16 * g + (t & 15)) * 8;
       }
       const half_t* gam = STAGE == 1 ? f.gamma + (int64_t)i * p.K : nullptr;
 
@@ -328,20 +344,20 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
           const int rl = h * kRowTile + 4 * g;  // quad-local row of v = 0
           const int r0 = q * kQuad * kRowTile + rl;
           const int t = t0 + 16 * c + c16;
+          const float scl = srow < p.rows ? (float)sclh : 0.0f;
           float sc[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) sc[v] = __shfl(scl, rl + v, 64);
           if (STAGE == 1) {
-            if (t < t1 && r0 < p.rows) {
-              half_t* zp = p.zh + i * p.zhstride + (int64_t)t * p.ldzh + r0;
-              const v4h zv = {(half_t)(sum[0] * sc[0]), (half_t)(sum[1] * sc[1]),
+            // rows r0..r0+3 share one 8-element chunk of the z tile; rows
+            // past R get scale 0, so the chunk is written whole
+            if (t < t1) {
+              const int k = r0 & 127;
+              half_t* zp = p.zt + i * p.zt_term +
+                           ((int64_t)(t >> 4) * p.zt_nkb + (r0 >> 7)) * 2048 + (k >> 5) * 512 +
+                           (16 * ((k >> 3) & 3) + (t & 15)) * 8 + (k & 7);
+              *(v4h*)zp = v4h{(half_t)(sum[0] * sc[0]), (half_t)(sum[1] * sc[1]),
                               (half_t)(sum[2] * sc[2]), (half_t)(sum[3] * sc[3])};
-              if (r0 + 4 <= p.rows) {
-                *(v4h*)zp = zv;
-              } else {
-                for (int v = 0; v < 4; ++v)
-                  if (r0 + v < p.rows) zp[v] = zv[v];
-              }
             }
           } else {
 #pragma unroll
@@ -420,9 +436,9 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   p.multi = a.multi;
   p.x = a.x;
   p.ldx = a.ldx;
-  p.zh = (half_t*)(ws + L.z);
-  p.ldzh = ldz_of(a.R);
-  p.zhstride = a.T * p.ldzh;
+  p.zt = (half_t*)(ws + L.z);
+  p.zt_term = zt_term_halfs(a.R, a.T);
+  p.zt_nkb = (int32_t)cdiv(a.R, kColBlock);
   p.y = a.y;
   p.ldy = a.ldy;
   p.single = a.single;
