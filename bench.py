@@ -13,10 +13,25 @@ Every timed call reads factors that are not in any cache: calls rotate over
 distinct device copies of the layer whose total size exceeds twice the 256 MB
 Infinity Cache.  Times come from HIP events on the stream the library
 launches on.  Prints ONE JSON line on stdout.
+
+The roofline object is for the dominant kernel of the timed call: each of the
+two launch groups is also timed alone (DBF_STAGE1_ONLY / DBF_STAGE2_ONLY,
+one kernel each on this path), and the slower one is reported against the
+fp16 matrix-core peak.  Its HBM traffic comes from the rocprofv3 FETCH_SIZE /
+WRITE_SIZE summary committed under profiles/ (scaled by what the counters
+read for a device copy of known size), and is reported only while the kernel
+source still matches the one the counters were taken on.
+
+Other modes: --copy-calibration runs a 256 MiB device copy (for the counter
+calibration run); --summarize-pmc FETCH_DIR WRITE_DIR prints the traffic
+summary from two rocprofv3 --pmc output directories.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +47,9 @@ METRIC = "DBF sign-matmul tokens/s + effective GB/s (4096², R=2048, T=1/256), %
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 N_, R_, M_ = 4096, 2048, 4096
+GEMM_SRC = os.path.join(ROOT, "double_binary_rank_amd", "csrc", "dbf_gemm.hip")
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "k_gemm_traffic_attn4096_R2048_T256.md")
+COPY_MIB = 256
 
 
 def log(msg):
@@ -68,6 +86,65 @@ def replicate(t: torch.Tensor, k: int):
     return [t.clone() for _ in range(k)]
 
 
+def file_sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def committed_traffic(stage):
+    """HBM bytes per launch of the stage kernel from the committed counter
+    summary, or None when absent or taken on different kernel source."""
+    try:
+        with open(TRAFFIC_MD) as f:
+            for line in f:
+                if line.startswith("traffic_json:"):
+                    d = json.loads(line.split(":", 1)[1])
+                    if d.get("source_sha256") != file_sha256(GEMM_SRC):
+                        return None
+                    return d["stages"][str(stage)]["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+    return None
+
+
+def _pmc_rows(d):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the stage kernels and of
+    the calibration copy, scaled by the copy's known size."""
+    def per_kernel(d, counter):
+        acc = {}
+        for r in _pmc_rows(d):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = ("stage1" if "k_gemm<1" in name else "stage2" if "k_gemm<2" in name
+                   else "copy" if "copy" in name.lower() or "elementwise" in name else None)
+            if key:
+                acc.setdefault(key, []).append(float(r["Counter_Value"]))
+        # the calibration copy is the largest copy dispatch (the set-up also
+        # copies the layer instances, 2 MiB each)
+        return {k: (max(v) if k == "copy" else sum(v) / len(v)) for k, v in acc.items()}
+
+    fe, wr = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_kib = COPY_MIB * 1024.0
+    f_fac, w_fac = copy_kib / fe["copy"], copy_kib / wr["copy"]
+    stages = {}
+    for st in ("1", "2"):
+        k = "stage" + st
+        fb, wb = fe[k] * 1024 * f_fac, wr[k] * 1024 * w_fac
+        stages[st] = {"fetch_kib_raw": fe[k], "write_kib_raw": wr[k], "fetch_bytes": fb,
+                      "write_bytes": wb, "bytes_per_launch": fb + wb}
+    return {"source_sha256": file_sha256(GEMM_SRC), "copy_mib": COPY_MIB,
+            "copy_fetch_kib_raw": fe["copy"], "copy_write_kib_raw": wr["copy"],
+            "fetch_factor": f_fac, "write_factor": w_fac, "stages": stages}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,7 +152,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of cases to run (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"also run a {COPY_MIB} MiB device copy (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print("traffic_json: " + json.dumps(summarize_pmc(*args.summarize_pmc)))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -120,12 +203,37 @@ def main():
     flops = alg_flops(N_, R_, M_, 1, T)
     byts = alg_bytes(N_, R_, M_, 1, T)
     t_call = value = achieved_tflops = float("nan")
+    roof = None
     if want("prefill"):
         sec = time_calls(call256, args.steps, args.warmup)
         t_call = sec / args.steps
         value = T / t_call
         achieved_tflops = flops / t_call / 1e12
         log(f"prefill T=256: {t_call * 1e6:.2f} us/call, {achieved_tflops:.1f} TFLOP/s")
+
+        # each launch group alone: stage 1 (z = beta * B2 (gamma * x)) and
+        # stage 2 (y = alpha * B1 z, reading the z stage 1 left in ws)
+        def stage_call(st):
+            def f(i):
+                k = i % n_inst
+                dbf.dbf_forward(xs[i % len(xs)], B1s[k], B2s[k], pl.alpha, pl.beta, pl.gamma, N_,
+                                R_, M_, y=y256, ws=ws, stage=st)
+            return f
+
+        t_st = {}
+        for st in (1, 2):
+            stage_call(1)(0)
+            t_st[st] = time_calls(stage_call(st), args.steps, args.warmup) / args.steps
+        f_st = {1: 2 * T * R_ * M_, 2: 2 * T * N_ * R_}
+        dom = max(t_st, key=t_st.get)
+        ach = f_st[dom] / t_st[dom] / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": committed_traffic(dom),
+                "kernel": f"k_gemm<{dom}, 2, true> (stage {dom} of the T=256 call)",
+                "launch_us": t_st[dom] * 1e6, "alg_flops_per_launch": f_st[dom],
+                "stage_launch_us": {str(k): v * 1e6 for k, v in t_st.items()}}
+        log(f"stage launches: " + ", ".join(f"stage {k} {v * 1e6:.2f} us" for k, v in t_st.items())
+            + f"; dominant stage {dom}: {ach:.1f} TFLOP/s")
 
     # ------------------------------------------------------ decode T=1 --
     if want("decode"):
@@ -212,6 +320,16 @@ def main():
         }
         log(f"multi-adapter: {tm * 1e6:.1f} us/call, {bm / tm / 1e9:.1f} GB/s")
 
+    # ------------------------------------------------ copy calibration --
+    if args.copy_calibration:
+        n = COPY_MIB << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {COPY_MIB} MiB device copy x5")
+
     # ------------------------------------------------------ CPU oracle --
     cpu = None
     if not args.no_cpu_baseline:
@@ -247,10 +365,8 @@ def main():
                    "ell": 1, "T": T, "cold_cache_instances": n_inst},
         "effective_GBs": byts / t_call / 1e9,
         "parity_err": err256,
-        "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / MFMA_F16_PEAK_TFLOPS,
-                     "traffic": None,
-                     "kernel": "k_stage_f16 stage 1 + stage 2 (one dbf_forward call)"},
+        "achieved_TFLOPs_per_call": achieved_tflops,
+        "roofline": roof,
         "cpu_baseline": cpu,
         "cases": out,
     }

@@ -84,7 +84,7 @@ def dbf_unpack_signs(packed: torch.Tensor, rows: int, cols: int, out: torch.Tens
     return out
 
 
-def _flags(accumulate: bool, path: str | None) -> int:
+def _flags(accumulate: bool, path: str | None, stage: int | None = None) -> int:
     f = _lib.DBF_ACCUMULATE if accumulate else 0
     if path == "gemv":
         f |= _lib.DBF_PATH_GEMV
@@ -92,6 +92,12 @@ def _flags(accumulate: bool, path: str | None) -> int:
         f |= _lib.DBF_PATH_MFMA
     elif path not in (None, "auto"):
         raise ValueError(f"unknown path {path!r}")
+    if stage == 1:
+        f |= _lib.DBF_STAGE1_ONLY
+    elif stage == 2:
+        f |= _lib.DBF_STAGE2_ONLY
+    elif stage is not None:
+        raise ValueError(f"stage must be 1, 2 or None, not {stage!r}")
     return f
 
 
@@ -112,11 +118,12 @@ def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torc
                 beta: torch.Tensor, gamma: torch.Tensor, N: int, R: int, M: int, *,
                 y: torch.Tensor | None = None, y_dtype=torch.float16, accumulate: bool = False,
                 path: str | None = None, ws: torch.Tensor | None = None,
-                stream=None) -> torch.Tensor:
+                stream=None, stage: int | None = None) -> torch.Tensor:
     """y = sum_i diag(alpha_i) B1 diag(beta_i) B2 diag(gamma_i) x per token row.
 
     x [T][M] fp16; B1, B2 packed (dbf_pack_signs); alpha [ell][N],
-    beta [ell][R], gamma [ell][M] fp16 contiguous."""
+    beta [ell][R], gamma [ell][M] fp16 contiguous.  ``stage`` 1 or 2 runs
+    only that launch group (DBF_STAGE1_ONLY / DBF_STAGE2_ONLY)."""
     T = x.shape[0]
     ell = alpha.shape[0] if alpha.dim() == 2 else 1
     ldx = _row_major(x, "x")
@@ -124,7 +131,7 @@ def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torc
     ws = _ws(ws, N, R, M, ell, T, x.device)
     yt = _DTYPE[y.dtype]
     check(lib.dbf_forward(_ptr(x), ldx, _ptr(B1), _ptr(B2), _ptr(alpha), _ptr(beta), _ptr(gamma),
-                          N, R, M, ell, T, _ptr(y), ldy, yt, _flags(accumulate, path), _ptr(ws),
+                          N, R, M, ell, T, _ptr(y), ldy, yt, _flags(accumulate, path, stage), _ptr(ws),
                           ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward")
     return y
 
@@ -139,7 +146,8 @@ def dbf_forward_multi_adapter(x: torch.Tensor, ids: torch.Tensor, B1s: torch.Ten
                               gammas: torch.Tensor, num_adapters: int, N: int, R: int, M: int,
                               ell: int, *, y: torch.Tensor | None = None, y_dtype=torch.float16,
                               accumulate: bool = False, path: str | None = None,
-                              ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                              ws: torch.Tensor | None = None, stream=None,
+                              stage: int | None = None) -> torch.Tensor:
     """Token t uses adapter ids[t]; the five tables are device int64 arrays
     of per-adapter device pointers (see ``pointer_table``)."""
     T = x.shape[0]
@@ -149,7 +157,7 @@ def dbf_forward_multi_adapter(x: torch.Tensor, ids: torch.Tensor, B1s: torch.Ten
     yt = _DTYPE[y.dtype]
     check(lib.dbf_forward_multi_adapter(
         _ptr(x), ldx, T, _ptr(ids), num_adapters, _ptr(B1s), _ptr(B2s), _ptr(alphas), _ptr(betas),
-        _ptr(gammas), N, R, M, ell, _ptr(y), ldy, yt, _flags(accumulate, path), _ptr(ws),
+        _ptr(gammas), N, R, M, ell, _ptr(y), ldy, yt, _flags(accumulate, path, stage), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward_multi_adapter")
     return y
 

@@ -421,8 +421,10 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   GemmParams p{};
   if (a.multi) {
     // column blocks of at most kGemmChunk tokens of one adapter
-    const hipError_t e = launch_segment(a, kGemmChunk, s);
-    if (e != hipSuccess) return e;
+    if (a.stages & 1) {
+      const hipError_t e = launch_segment(a, kGemmChunk, s);
+      if (e != hipSuccess) return e;
+    }
     int64_t n_cb = a.T + cdiv(a.T, kGemmChunk);
     if (n_cb > max_colblocks(a.T)) n_cb = max_colblocks(a.T);
     p.n_cb_host = (int32_t)n_cb;
@@ -459,9 +461,11 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   p2.K = (int32_t)a.R;
   p2.nq = (int32_t)cdiv(a.N, kRowTile * kQuad);
   p2.nkb = (int32_t)cdiv(a.R, kColBlock);
-  const hipError_t e = launch_stage<1>(p1, s);
-  if (e != hipSuccess) return e;
-  return launch_stage<2>(p2, s);
+  if (a.stages & 1) {
+    const hipError_t e = launch_stage<1>(p1, s);
+    if (e != hipSuccess) return e;
+  }
+  return (a.stages & 2) ? launch_stage<2>(p2, s) : hipSuccess;
 }
 
 }  // namespace dbf

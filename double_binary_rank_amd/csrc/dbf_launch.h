@@ -33,6 +33,7 @@ struct ForwardArgs {
   void* ws;
   size_t ws_bytes;
   Path path;
+  int stages;  // bit 0: stage 1 (z), bit 1: stage 2 (y)
 };
 
 // Largest batch the small-T (fp4 matrix-core) path accepts; its operand

@@ -287,3 +287,44 @@ def test_multi_adapter_stream_path(integer):
     else:
         err = oracle.max_norm_error(y.cpu().numpy(), want)
         assert err <= TOL, err
+
+
+# ------------------------------------------------- split launch groups --
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("shape", [(300, 130, 260, 1, 37), (64, 16, 8, 3, 70)])
+def test_stage_split_equals_whole(shape, path):
+    """STAGE1_ONLY then STAGE2_ONLY on one workspace gives the whole call's
+    result bit for bit, and STAGE1_ONLY leaves y untouched."""
+    N, R, M, ell, T = shape
+    L = synth.make_layer(N, R, M, ell, T, seed=81)
+    pl = H().upload(L)
+    x = H().to_dev_rows(L.x)
+    y_whole = pl.forward(x, path=path, y=H().empty_rows(T, N, torch.float16))
+    ws = torch.empty(dbf_ws(N, R, M, ell, T), dtype=torch.uint8, device="cuda")
+    y = H().empty_rows(T, N, torch.float16)
+    y.fill_(7.0)
+    pl.forward(x, path=path, y=y, ws=ws, stage=1)
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all())
+    pl.forward(x, path=path, y=y, ws=ws, stage=2)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_whole)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_stage_split_multi_adapter(path):
+    B = synth.make_multi_adapter(num_adapters=6, N=96, R=48, M=160, ell=2, T=90, seed=83)
+    D = H().DeviceAdapters(B.adapters)
+    x, ids = H().to_dev(B.x), H().to_dev(B.ids)
+    y_whole = D.forward(x, ids, path=path, y=H().empty_rows(90, 96, torch.float16))
+    ws = torch.empty(dbf_ws(96, 48, 160, 2, 90), dtype=torch.uint8, device="cuda")
+    y = H().empty_rows(90, 96, torch.float16)
+    D.forward(x, ids, path=path, y=y, ws=ws, stage=1)
+    D.forward(x, ids, path=path, y=y, ws=ws, stage=2)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_whole)
+
+
+def dbf_ws(N, R, M, ell, T):
+    import double_binary_rank_amd as dbf
+    return dbf.dbf_workspace_bytes(N, R, M, ell, T)
