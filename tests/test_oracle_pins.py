@@ -317,6 +317,14 @@ def test_fp16_rne():
     assert np.isinf(oracle.fp16_rne(np.array([70000.0]))[0])
 
 
+def test_max_norm_error_definition():
+    # the error measure of the parity bar: max|y - ref| / max|ref|
+    assert oracle.max_norm_error([1.0, 2.0], [1.0, 4.0]) == 0.5
+    assert oracle.max_norm_error([[3.0, -1.0]], [[1.0, -2.0]]) == 1.0
+    assert oracle.max_norm_error([0.0], [0.0]) == 0.0
+    assert oracle.max_norm_error([1.0], [0.0]) == float("inf")
+
+
 # ---------------------------------------------- storage: the pages' figures --
 
 def test_storage_closed_form_and_claims():
