@@ -24,8 +24,9 @@ DBF_F32 = 3
 DBF_ACCUMULATE = 1
 DBF_PATH_GEMV = 2
 DBF_PATH_MFMA = 4
-DBF_STAGE1_ONLY = 8
-DBF_STAGE2_ONLY = 16
+DBF_RUN_PREP = 8
+DBF_RUN_STAGE1 = 16
+DBF_RUN_STAGE2 = 32
 MAX_DIM = 1 << 30
 
 ABI_VERSION = 1

@@ -84,7 +84,10 @@ def dbf_unpack_signs(packed: torch.Tensor, rows: int, cols: int, out: torch.Tens
     return out
 
 
-def _flags(accumulate: bool, path: str | None, stage: int | None = None) -> int:
+_PHASE = {"prep": 8, "stage1": 16, "stage2": 32}
+
+
+def _flags(accumulate: bool, path: str | None, phases=None) -> int:
     f = _lib.DBF_ACCUMULATE if accumulate else 0
     if path == "gemv":
         f |= _lib.DBF_PATH_GEMV
@@ -92,12 +95,10 @@ def _flags(accumulate: bool, path: str | None, stage: int | None = None) -> int:
         f |= _lib.DBF_PATH_MFMA
     elif path not in (None, "auto"):
         raise ValueError(f"unknown path {path!r}")
-    if stage == 1:
-        f |= _lib.DBF_STAGE1_ONLY
-    elif stage == 2:
-        f |= _lib.DBF_STAGE2_ONLY
-    elif stage is not None:
-        raise ValueError(f"stage must be 1, 2 or None, not {stage!r}")
+    for ph in ([phases] if isinstance(phases, str) else (phases or ())):
+        if ph not in _PHASE:
+            raise ValueError(f"unknown phase {ph!r} (prep, stage1, stage2)")
+        f |= _PHASE[ph]
     return f
 
 
@@ -118,12 +119,13 @@ def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torc
                 beta: torch.Tensor, gamma: torch.Tensor, N: int, R: int, M: int, *,
                 y: torch.Tensor | None = None, y_dtype=torch.float16, accumulate: bool = False,
                 path: str | None = None, ws: torch.Tensor | None = None,
-                stream=None, stage: int | None = None) -> torch.Tensor:
+                stream=None, phases=None) -> torch.Tensor:
     """y = sum_i diag(alpha_i) B1 diag(beta_i) B2 diag(gamma_i) x per token row.
 
     x [T][M] fp16; B1, B2 packed (dbf_pack_signs); alpha [ell][N],
-    beta [ell][R], gamma [ell][M] fp16 contiguous.  ``stage`` 1 or 2 runs
-    only that launch group (DBF_STAGE1_ONLY / DBF_STAGE2_ONLY)."""
+    beta [ell][R], gamma [ell][M] fp16 contiguous.  ``phases`` (a name or a
+    list of "prep", "stage1", "stage2") runs only those phases
+    (DBF_RUN_PREP / DBF_RUN_STAGE1 / DBF_RUN_STAGE2); None runs all."""
     T = x.shape[0]
     ell = alpha.shape[0] if alpha.dim() == 2 else 1
     ldx = _row_major(x, "x")
@@ -131,7 +133,7 @@ def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torc
     ws = _ws(ws, N, R, M, ell, T, x.device)
     yt = _DTYPE[y.dtype]
     check(lib.dbf_forward(_ptr(x), ldx, _ptr(B1), _ptr(B2), _ptr(alpha), _ptr(beta), _ptr(gamma),
-                          N, R, M, ell, T, _ptr(y), ldy, yt, _flags(accumulate, path, stage), _ptr(ws),
+                          N, R, M, ell, T, _ptr(y), ldy, yt, _flags(accumulate, path, phases), _ptr(ws),
                           ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward")
     return y
 
@@ -147,7 +149,7 @@ def dbf_forward_multi_adapter(x: torch.Tensor, ids: torch.Tensor, B1s: torch.Ten
                               ell: int, *, y: torch.Tensor | None = None, y_dtype=torch.float16,
                               accumulate: bool = False, path: str | None = None,
                               ws: torch.Tensor | None = None, stream=None,
-                              stage: int | None = None) -> torch.Tensor:
+                              phases=None) -> torch.Tensor:
     """Token t uses adapter ids[t]; the five tables are device int64 arrays
     of per-adapter device pointers (see ``pointer_table``)."""
     T = x.shape[0]
@@ -157,7 +159,7 @@ def dbf_forward_multi_adapter(x: torch.Tensor, ids: torch.Tensor, B1s: torch.Ten
     yt = _DTYPE[y.dtype]
     check(lib.dbf_forward_multi_adapter(
         _ptr(x), ldx, T, _ptr(ids), num_adapters, _ptr(B1s), _ptr(B2s), _ptr(alphas), _ptr(betas),
-        _ptr(gammas), N, R, M, ell, _ptr(y), ldy, yt, _flags(accumulate, path, stage), _ptr(ws),
+        _ptr(gammas), N, R, M, ell, _ptr(y), ldy, yt, _flags(accumulate, path, phases), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward_multi_adapter")
     return y
 

@@ -16,13 +16,15 @@ dbf_status hip_status(hipError_t e) { return e == hipSuccess ? DBF_OK : DBF_ERR_
 
 bool valid_dtype_out(dbf_dtype t) { return t == DBF_F16 || t == DBF_F32; }
 
-constexpr uint32_t kKnownFlags =
-    DBF_ACCUMULATE | DBF_PATH_GEMV | DBF_PATH_MFMA | DBF_STAGE1_ONLY | DBF_STAGE2_ONLY;
+constexpr uint32_t kPhases = DBF_RUN_PREP | DBF_RUN_STAGE1 | DBF_RUN_STAGE2;
+constexpr uint32_t kKnownFlags = DBF_ACCUMULATE | DBF_PATH_GEMV | DBF_PATH_MFMA | kPhases;
 
-int stages_of(uint32_t flags) {
-  if (flags & DBF_STAGE1_ONLY) return 1;
-  if (flags & DBF_STAGE2_ONLY) return 2;
-  return 3;
+// phase bits 0 (prep), 1 (stage 1), 2 (stage 2); none selected means all
+int phases_of(uint32_t flags) {
+  const uint32_t f = flags & kPhases;
+  if (f == 0) return 7;
+  return ((f & DBF_RUN_PREP) ? 1 : 0) | ((f & DBF_RUN_STAGE1) ? 2 : 0) |
+         ((f & DBF_RUN_STAGE2) ? 4 : 0);
 }
 
 // Checks shared by dbf_forward and dbf_forward_multi_adapter.
@@ -35,7 +37,6 @@ dbf_status check_common(const void* x, int64_t ldx, int64_t N, int64_t R, int64_
   if (!valid_dtype_out(y_type)) return DBF_ERR_INVALID_ARG;
   if (flags & ~kKnownFlags) return DBF_ERR_INVALID_ARG;
   if ((flags & DBF_PATH_GEMV) && (flags & DBF_PATH_MFMA)) return DBF_ERR_INVALID_ARG;
-  if ((flags & DBF_STAGE1_ONLY) && (flags & DBF_STAGE2_ONLY)) return DBF_ERR_INVALID_ARG;
   if (T == 0) return DBF_OK;
   if (x == nullptr || y == nullptr) return DBF_ERR_INVALID_ARG;
   if (ldx < M || ldy < N) return DBF_ERR_INVALID_ARG;
@@ -138,7 +139,7 @@ dbf_status dbf_forward(const void* x, int64_t ldx, const uint32_t* B1, const uin
   a.ws = ws;
   a.ws_bytes = ws_bytes;
   a.path = pick_path(flags, T, T);
-  a.stages = stages_of(flags);
+  a.phases = phases_of(flags);
   return hip_status(dbf::launch_forward(a, (hipStream_t)stream));
 }
 
@@ -184,7 +185,7 @@ dbf_status dbf_forward_multi_adapter(const void* x, int64_t ldx, int64_t T, cons
   a.ws_bytes = ws_bytes;
   const int64_t per = T / (num_adapters < T ? num_adapters : T);
   a.path = pick_path(flags, per, T);
-  a.stages = stages_of(flags);
+  a.phases = phases_of(flags);
   return hip_status(dbf::launch_forward(a, (hipStream_t)stream));
 }
 

@@ -4,26 +4,29 @@
 // Once the signs are expanded to +-1 each stage is a dense contraction over
 // the batch (DBF summary, section 2, inference: the product with the weight
 // becomes two products with sign matrices), so it runs on
-// v_mfma_f32_16x16x32_f16 with fp32 accumulation; the operands gamma_i*x and
-// z_i = beta_i*u_i are rounded to fp16.
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation; the operands v_i =
+// gamma_i*x and z_i = beta_i*u_i are rounded to fp16 once each.
+//
+// Launches: prep (v_i = gamma_i * x) -> stage 1 (z_i = beta_i * B2 v_i) ->
+// stage 2 (y = sum_i alpha_i * B1 z_i).  v and z live in the workspace in
+// MFMA operand order: tiles of 16 tokens x 128 reduction entries, 4 KB each
+// (4 steps x 64 lanes x 8), so every operand load of a wave is 1 KB
+// contiguous, and entries past the reduction length are zero, so the last
+// block needs no masking (the padding signs are +1).
 //
 // K order: the packed word a lane of group g holds for (row rho, 128-block)
 // supplies the A operand of four 32-K steps s = 0..3, slots 8s..8s+7 each
 // (bits s, s+4, ..., s+28), which are the block cols 32s + 8g + e, e = 0..7.
-// The activation operand of lane group g, element e, step s is that same col,
-// so both operands see the same k and no lane exchange is needed; one load
-// instruction of step s reads 64 contiguous bytes (cols 32s..32s+31) of each
-// of its 16 token rows.
+// The operand tiles put entry 32s + 8g + e of token c16 in lane 16g + c16 of
+// step s, so both operands see the same k and no lane exchange is needed.
 //
 // Work item: a column block of 16*NC tokens and either one row quad (64
 // rows) whose reduction the four waves split (SPLITK: interleaved 128-blocks,
 // partial tiles summed in a fixed order through LDS), or four row quads, one
 // per wave, each over the whole reduction (for short reductions).  Output
 // column j of an MFMA depends only on operand column j, so columns of tokens
-// past the block's end read a valid token's row and are simply not stored.
-// Stage 1 writes z_i = beta_i * u_i as fp16 into the workspace, in the order
-// stage 2's MFMA operands take it (so each of its operand loads is 1 KB
-// contiguous); stage 2 writes y = sum_i alpha_i * (B1 z_i).
+// past the block's end read a valid token's tile row and are simply not
+// stored.
 #include "dbf_device.h"
 #include "dbf_launch.h"
 
@@ -38,11 +41,12 @@ struct GemmParams {
   int32_t n_cb_host, n_rg;  // column blocks (single adapter), row groups
   int32_t y_f32, accumulate, multi, xcd_remap;
   uint32_t msk16, one16;  // 0x80008000, 0x3C003C00 (kept in registers)
-  const half_t* x;
-  int64_t ldx;
-  half_t* zt;         // z_i, fp16 in MFMA operand order (see zt_term_halfs)
-  int64_t zt_term;    // halfs per term
-  int32_t zt_nkb;     // 128-row blocks of z
+  const half_t* opnd;     // this stage's operand tiles (v or z)
+  int64_t opnd_term;      // halfs per term
+  int32_t opnd_nkb;       // 128-blocks per token tile row of the operand
+  int32_t z_nkb;          // stage 1: 128-row blocks of z
+  half_t* z;              // stage 1 output tiles
+  int64_t z_term;
   void* y;
   int64_t ldy;
   Factors single;
@@ -52,7 +56,6 @@ struct GemmParams {
   const uint32_t* const* B2s;
   const half_t* const* alphas;
   const half_t* const* betas;
-  const half_t* const* gammas;
 };
 
 // A operand of step s for one lane: slots 8s..8s+7 of its word as fp16 +-1.
@@ -72,79 +75,28 @@ __device__ inline v8h expand_step_f16(uint32_t w, uint32_t msk, uint32_t one) {
   return __builtin_bit_cast(v8h, o);
 }
 
-// Operands of one 128-block as loaded: sign words of the four row tiles,
-// raw activations b[s][c] (k = kb*128 + 32s + 8g .. +7 of token column c)
-// and, in stage 1, gamma over the same k.
-template <int STAGE, int NC>
+// Operands of one 128-block: sign words of the four row tiles and the
+// operand b[s][c] of step s for token column c.
+template <int NC>
 struct Block {
   v4u a;
   v8h b[4][NC];
-  v8h gm[4];
 };
 
-// arow[c]: stage 1, the row of x of token column c (plus 8g); stage 2, the
-// lane's 16 bytes of that token's z tile row, so step s of block kb sits at
-// arow[c] + kb*2048 + s*512.
-template <int STAGE, int NC>
-__device__ inline const half_t* act_ptr(const half_t* arow, int kb, int s) {
-  return STAGE == 1 ? arow + kb * kColBlock + 32 * s : arow + (int64_t)kb * 2048 + s * 512;
-}
-
-template <int STAGE, int NC>
-__device__ inline void load_full(Block<STAGE, NC>& B, const char* sq, const half_t* const (&arow)[NC],
-                                 int kb, int g) {
+// orow[c]: the lane's 16 bytes of token column c's tile row; step s of
+// block kb sits at orow[c] + kb*2048 + s*512.
+template <int NC>
+__device__ inline void load_block(Block<NC>& B, const char* sq, const half_t* const (&orow)[NC],
+                                  int kb) {
   B.a = *(gv4up)(sq + ((int64_t)kb << 10));
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) B.b[s][c] = *(gv8hp)act_ptr<STAGE, NC>(arow[c], kb, s);
+    for (int c = 0; c < NC; ++c) B.b[s][c] = *(gv8hp)(orow[c] + (int64_t)kb * 2048 + s * 512);
 }
 
-// gamma of block kb from the LDS window that starts at block wb0
-template <int STAGE, int NC>
-__device__ inline void load_gamma(Block<STAGE, NC>& B, const half_t* gl, int kb, int wb0, int g) {
-  if (STAGE == 1) {
-    const v8h* gp = (const v8h*)(gl + (kb - wb0) * kColBlock + 8 * g);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) B.gm[s] = gp[4 * s];
-  }
-}
-
-// The last, partial 128-block: activations past K are zero (the padding
-// signs are +1, so they must not contribute).  Cold code: not unrolled.
-template <int STAGE, int NC>
-__device__ inline void load_tail(Block<STAGE, NC>& B, const char* sq, const half_t* const (&arow)[NC],
-                                 const half_t* gam, int kb, int g, int K) {
-  B.a = *(gv4up)(sq + ((int64_t)kb << 10));
-  const int kbase = kb * kColBlock + 8 * g;
-  for (int s = 0; s < 4; ++s) {
-    v8h gv = {};
-    for (int e = 0; e < 8; ++e) {
-      const int k = kbase + 32 * s + e;
-      if (STAGE == 1 && k < K) gv[e] = gam[k];
-    }
-    B.gm[s] = gv;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      v8h v = {};
-      if (STAGE == 1) {
-        for (int e = 0; e < 8; ++e) {
-          const int k = kbase + 32 * s + e;
-          if (k < K) v[e] = arow[c][k - 8 * g];  // arow already points 8g in
-        }
-      } else if (kbase + 32 * s < K) {
-        // the z tile spans the whole block; rows past K are not written
-        v = *(gv8hp)act_ptr<STAGE, NC>(arow[c], kb, s);
-        for (int e = 0; e < 8; ++e)
-          if (kbase + 32 * s + e >= K) v[e] = (half_t)0.0f;
-      }
-      B.b[s][c] = v;
-    }
-  }
-}
-
-template <int STAGE, int NC>
-__device__ inline void mma_block(v4f (&acc)[4][NC], const Block<STAGE, NC>& B, uint32_t msk,
+template <int NC>
+__device__ inline void mma_block(v4f (&acc)[4][NC], const Block<NC>& B, uint32_t msk,
                                  uint32_t one) {
   auto step = [&](auto sc) {
     constexpr int s = decltype(sc)::value;
@@ -152,12 +104,10 @@ __device__ inline void mma_block(v4f (&acc)[4][NC], const Block<STAGE, NC>& B, u
 #pragma unroll
     for (int h = 0; h < 4; ++h) a[h] = expand_step_f16<s>(B.a[h], msk, one);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const v8h bv = STAGE == 1 ? B.b[s][c] * B.gm[s] : B.b[s][c];
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int h = 0; h < 4; ++h)
-        acc[h][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[h], bv, acc[h][c], 0, 0, 0);
-    }
+        acc[h][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[h], B.b[s][c], acc[h][c], 0, 0, 0);
   };
   step(std::integral_constant<int, 0>{});
   step(std::integral_constant<int, 1>{});
@@ -165,15 +115,79 @@ __device__ inline void mma_block(v4f (&acc)[4][NC], const Block<STAGE, NC>& B, u
   step(std::integral_constant<int, 3>{});
 }
 
-// Blocks of gamma held in LDS at a time (a window of the reduction).
-constexpr int kGamWindow = 128;
+// Half offset of entry (t, k) in one term's operand tiles.
+__device__ inline int64_t tile_off(int t, int k, int nkb) {
+  const int kk = k & 127;
+  return ((int64_t)(t >> 4) * nkb + (k >> 7)) * 2048 + (kk >> 5) * 512 +
+         (16 * ((kk >> 3) & 3) + (t & 15)) * 8 + (kk & 7);
+}
+
+__device__ inline int32_t norm_adapter(int32_t id, int32_t n) { return (id >= 0 && id < n) ? id : -1; }
+
+struct PrepVParams {
+  const half_t* x;
+  int64_t ldx;
+  int32_t T, M, ell, nkb, multi, num_adapters;
+  int64_t n_units;  // ell * ceil(T/16) * nkb
+  const half_t* gamma;
+  const int32_t* ids;
+  const half_t* const* gammas;
+  half_t* v;
+  int64_t v_term;
+};
+
+// v_i = fp16(gamma_i * x) in operand tiles, one wave per (term, 16-token
+// tile, 128-block): lane 16g + c16 writes the 8 entries 32s + 8g .. of token
+// c16 for each step s (1 KB contiguous per step).  Entries past M, tokens
+// past T and tokens whose adapter id is out of range are zero.  One fp16
+// rounding of the exact product.
+__global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (u >= p.n_units) return;  // uniform per wave
+  const int kb = (int)(u % p.nkb);
+  const int64_t r = u / p.nkb;
+  const int ntt = (p.T + 15) >> 4;
+  const int tt = (int)(r % ntt);
+  const int i = (int)(r / ntt);
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t = tt * 16 + c16;
+  const half_t* gam = nullptr;
+  if (t < p.T) {
+    if (p.multi) {
+      const int32_t ad = norm_adapter(p.ids[t], p.num_adapters);
+      if (ad >= 0) gam = p.gammas[ad];
+    } else {
+      gam = p.gamma;
+    }
+  }
+  half_t* out = p.v + i * p.v_term + ((int64_t)tt * p.nkb + kb) * 2048 + lane * 8;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int k = kb * kColBlock + 32 * s + 8 * g;
+    v8h o = {};
+    if (gam != nullptr) {
+      const half_t* xr = p.x + (int64_t)t * p.ldx + k;
+      const half_t* gr = gam + (int64_t)i * p.M + k;
+      if (k + 8 <= p.M) {
+        const v8h xv = *(gv8hp)xr;
+        v8h gv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] = gr[e];
+        o = xv * gv;
+      } else {
+        for (int e = 0; e < 8; ++e)
+          if (k + e < p.M) o[e] = xr[e] * gr[e];
+      }
+    }
+    *(v8h*)(out + s * 512) = o;
+  }
+}
 
 template <int STAGE, int NC, bool SPLITK>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   constexpr int D = 2;  // operand buffers per wave (deeper rings measured slower)
   __shared__ v4f red[SPLITK ? 4 : 1][SPLITK ? 4 * NC : 1][64];
-  extern __shared__ v8h gam_lds[];  // stage 1: gamma_i over one window
-  half_t* gl = (half_t*)gam_lds;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
@@ -181,14 +195,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   const int n_cb = p.multi ? p.hdr->n_colblocks : p.n_cb_host;
   const int64_t n_items = (int64_t)n_cb * p.n_rg;
   // consecutive items share a column block; with the remap the items of one
-  // XCD (workgroups b, b+8, ...) are consecutive, so they share activations
-  // in that XCD's L2
+  // XCD (workgroups b, b+8, ...) are consecutive, so they share operand
+  // tiles in that XCD's L2
   int64_t first = blockIdx.x;
   if (p.xcd_remap) first = (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
-  const int nfull = p.K / kColBlock;
-  const bool has_tail = nfull < p.nkb;
-  // stage 2 reads no gamma: one window spans the whole reduction
-  const int win = STAGE == 1 ? kGamWindow : (nfull > 0 ? nfull : 1);
 
   for (int64_t it = first; it < n_items; it += gridDim.x) {
     const int cb = (int)(it / p.n_rg), rg = (int)(it % p.n_rg);
@@ -204,7 +214,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         f.B2 = p.B2s[ad];
         f.alpha = p.alphas[ad];
         f.beta = p.betas[ad];
-        f.gamma = p.gammas[ad];
       }
     } else {
       t0 = cb * 16 * NC;
@@ -216,7 +225,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     const int row_lo = (SPLITK ? rg : 4 * rg) * kQuad * kRowTile;
     const int row_hi = min(p.rows, row_lo + (SPLITK ? 1 : 4) * kQuad * kRowTile);
     if (ad < 0) {
-      // tokens whose adapter id is out of range: y = 0 (or unchanged)
+      // tokens whose adapter id is out of range: y = 0 (or unchanged); their
+      // z is never read (stage 2 skips the same column blocks)
       if (STAGE == 2 && !p.accumulate) {
         const int nr = row_hi - row_lo;
         for (int e = threadIdx.x; e < (t1 - t0) * nr; e += blockDim.x) {
@@ -232,25 +242,26 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     const bool active = SPLITK || q < p.nq;  // idle waves still reach every barrier
     const char* sq =
         (const char*)(STAGE == 1 ? f.B2 : f.B1) + ((int64_t)(active ? q : 0) * p.nkb << 10) + lane * 16;
+    // this wave's 128-blocks: wv, wv+4, ... (SPLITK) or all of them
+    const int kb0 = SPLITK ? wv : 0, kst = SPLITK ? 4 : 1;
+    const int nkw = SPLITK ? (p.nkb - wv + 3) / 4 : p.nkb;
+    const bool run = active && nkw > 0;
     float ys[SPLITK ? NC : 4 * NC][4];  // stage 2: running sum over the terms
 
     for (int i = 0; i < p.ell; ++i) {
-      // row scales of this wave's quad (lane L: row 64q + L), issued first so
-      // that their latency hides behind the reduction; lanes fetch the ones
-      // they need with a cross-lane read at the end
-      // (kept as loaded; converting here would wait for the load)
+      // row scales of this wave's quad (lane L: row 64q + L), loaded first
+      // and kept as loaded (converting here would wait for the load); lanes
+      // fetch the ones they need with a cross-lane read at the end
       const half_t* sv = (STAGE == 1 ? f.beta : f.alpha) + (int64_t)i * p.rows;
       const int srow = q * kQuad * kRowTile + lane;
       const half_t sclh = sv[min(srow, p.rows - 1)];
-      const half_t* arow[NC];
+      const half_t* orow[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int t = min(t0 + 16 * c + c16, t1 - 1);
-        arow[c] = STAGE == 1 ? p.x + (int64_t)t * p.ldx + 8 * g
-                             : p.zt + i * p.zt_term + (int64_t)(t >> 4) * p.zt_nkb * 2048 +
-                                   (16 * g + (t & 15)) * 8;
+        orow[c] = p.opnd + i * p.opnd_term + (int64_t)(t >> 4) * p.opnd_nkb * 2048 +
+                  (16 * g + (t & 15)) * 8;
       }
-      const half_t* gam = STAGE == 1 ? f.gamma + (int64_t)i * p.K : nullptr;
 
       v4f acc[4][NC];
 #pragma unroll
@@ -258,66 +269,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[h][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-      for (int wb0 = 0; wb0 < nfull; wb0 += win) {
-        const int wb1 = min(nfull, wb0 + win);
-        // this wave's blocks of the window: wb0+wv, wb0+wv+4, ... (SPLITK)
-        // or all of them
-        const int kb0 = wb0 + (SPLITK ? wv : 0), kst = SPLITK ? 4 : 1;
-        const int nkw = SPLITK ? (wb1 - wb0 - wv + 3) / 4 : wb1 - wb0;
-        const bool run = active && nkw > 0;
+      if (run) {
         // Operands of the next D-1 blocks are in flight while one is
         // consumed: D buffers with fixed roles (the loop is unrolled by D),
         // refilled right after their last use.  Every step issues the same
         // loads (clamped at the end), so each in-order wait covers exactly
-        // the buffer about to be used.  The first D blocks are requested
-        // before gamma is staged, so one memory round trip covers both.
-        auto kb_of = [&](int j) {  // block of the wave's j-th step (clamped)
-          return kb0 + min(j, nkw - 1) * kst;
-        };
-        Block<STAGE, NC> buf[D];
-        if (run) {
+        // the buffer about to be used.
+        auto kb_of = [&](int j) { return kb0 + min(j, nkw - 1) * kst; };
+        Block<NC> buf[D];
 #pragma unroll
-          for (int d = 0; d < D; ++d) load_full<STAGE, NC>(buf[d], sq, arow, kb_of(d), g);
-        }
-        if (STAGE == 1) {
-          // gamma of this window into LDS, element by element (any
-          // alignment), eight loads in flight per thread
-          __syncthreads();
-          const int nk = (wb1 - wb0) * kColBlock;
-          const half_t* gw = gam + wb0 * kColBlock;
-          for (int k0 = 0; k0 < nk; k0 += 8 * 256) {
-            half_t v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int k = k0 + e * 256 + threadIdx.x;
-              v[e] = k < nk ? gw[k] : (half_t)0.0f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int k = k0 + e * 256 + threadIdx.x;
-              if (k < nk) gl[k] = v[e];
-            }
-          }
-          __syncthreads();
-        }
-        if (!run) continue;
-#pragma unroll
-        for (int d = 0; d < D; ++d) load_gamma<STAGE, NC>(buf[d], gl, kb_of(d), wb0, g);
+        for (int d = 0; d < D; ++d) load_block<NC>(buf[d], sq, orow, kb_of(d));
         for (int j = 0; j < nkw; j += D) {
 #pragma unroll
           for (int d = 0; d < D; ++d) {
-            if (j + d < nkw) mma_block<STAGE, NC>(acc, buf[d], p.msk16, one);
+            if (j + d < nkw) mma_block<NC>(acc, buf[d], p.msk16, one);
             __builtin_amdgcn_sched_barrier(0);
-            const int kr = kb_of(j + d + D);
-            load_full<STAGE, NC>(buf[d], sq, arow, kr, g);
-            load_gamma<STAGE, NC>(buf[d], gl, kr, wb0, g);
+            load_block<NC>(buf[d], sq, orow, kb_of(j + d + D));
           }
         }
-      }
-      if (has_tail && active && (!SPLITK || (nfull & 3) == wv)) {
-        Block<STAGE, NC> bt;
-        load_tail<STAGE, NC>(bt, sq, arow, gam, nfull, g, p.K);
-        mma_block<STAGE, NC>(acc, bt, p.msk16, one);
       }
 
       if (SPLITK) {
@@ -330,6 +299,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         __syncthreads();
       }
       if (active) {
+        const float scl = srow < p.rows ? (float)sclh : 0.0f;
         constexpr int NE = SPLITK ? NC : 4 * NC;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
@@ -344,21 +314,16 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
           const int rl = h * kRowTile + 4 * g;  // quad-local row of v = 0
           const int r0 = q * kQuad * kRowTile + rl;
           const int t = t0 + 16 * c + c16;
-          const float scl = srow < p.rows ? (float)sclh : 0.0f;
           float sc[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) sc[v] = __shfl(scl, rl + v, 64);
           if (STAGE == 1) {
-            // rows r0..r0+3 share one 8-element chunk of the z tile; rows
-            // past R get scale 0, so the chunk is written whole
-            if (t < t1) {
-              const int k = r0 & 127;
-              half_t* zp = p.zt + i * p.zt_term +
-                           ((int64_t)(t >> 4) * p.zt_nkb + (r0 >> 7)) * 2048 + (k >> 5) * 512 +
-                           (16 * ((k >> 3) & 3) + (t & 15)) * 8 + (k & 7);
-              *(v4h*)zp = v4h{(half_t)(sum[0] * sc[0]), (half_t)(sum[1] * sc[1]),
-                              (half_t)(sum[2] * sc[2]), (half_t)(sum[3] * sc[3])};
-            }
+            // rows r0..r0+3 share one 8-entry chunk of the z tile; rows past
+            // R get scale 0, so the chunk is written whole
+            if (t < t1)
+              *(v4h*)(p.z + i * p.z_term + tile_off(t, r0, p.z_nkb)) =
+                  v4h{(half_t)(sum[0] * sc[0]), (half_t)(sum[1] * sc[1]),
+                      (half_t)(sum[2] * sc[2]), (half_t)(sum[3] * sc[3])};
           } else {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -377,6 +342,19 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
             }
           }
         }
+        // stage 1: when the row quads stop half way through the last 128-row
+        // block of z, the quad before the gap zeroes the rest of that block
+        if (STAGE == 1 && q == p.nq - 1 && (p.nq & 1) && (!SPLITK || wv == 0)) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int t = t0 + 16 * c + c16;
+            if (t < t1)
+#pragma unroll
+              for (int h = 0; h < 4; ++h)
+                *(v4h*)(p.z + i * p.z_term + tile_off(t, p.nq * 64 + h * 16 + 4 * g, p.z_nkb)) =
+                    v4h{};
+          }
+        }
       }
       if (SPLITK) __syncthreads();
     }
@@ -390,15 +368,14 @@ hipError_t launch_one(GemmParams p, hipStream_t s) {
   int64_t grid = items;
   if (p.multi && grid > 8192) grid = 8192;
   p.xcd_remap = (grid == items && items % 8 == 0) ? 1 : 0;
-  const int nfull = p.K / kColBlock;
-  const size_t lds = STAGE == 1 ? (size_t)(nfull < kGamWindow ? nfull : kGamWindow) * kColBlock * 2 : 0;
-  hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK>), dim3((unsigned)grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 // Tokens per column block: 64 feeds each expanded sign operand to more
 // MFMAs, 32 doubles the number of work items when 64 would leave compute
-// units idle; the row-split variant (short reductions) always takes 32.
+// units idle; the row-split variant (short reductions) and the multi-adapter
+// column blocks take 32.
 template <int STAGE>
 hipError_t launch_stage(GemmParams p, hipStream_t s) {
   const bool split = p.nkb >= 4;
@@ -421,7 +398,7 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   GemmParams p{};
   if (a.multi) {
     // column blocks of at most kGemmChunk tokens of one adapter
-    if (a.stages & 1) {
+    if (a.phases & 1) {
       const hipError_t e = launch_segment(a, kGemmChunk, s);
       if (e != hipSuccess) return e;
     }
@@ -436,11 +413,6 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   p.y_f32 = a.y_f32;
   p.accumulate = a.accumulate;
   p.multi = a.multi;
-  p.x = a.x;
-  p.ldx = a.ldx;
-  p.zt = (half_t*)(ws + L.z);
-  p.zt_term = zt_term_halfs(a.R, a.T);
-  p.zt_nkb = (int32_t)cdiv(a.R, kColBlock);
   p.y = a.y;
   p.ldy = a.ldy;
   p.single = a.single;
@@ -450,22 +422,53 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   p.B2s = a.B2s;
   p.alphas = a.alphas;
   p.betas = a.betas;
-  p.gammas = a.gammas;
+  half_t* vt = (half_t*)(ws + L.v);
+  half_t* zt = (half_t*)(ws + L.z);
 
   GemmParams p1 = p, p2 = p;
   p1.rows = (int32_t)a.R;
   p1.K = (int32_t)a.M;
   p1.nq = (int32_t)cdiv(a.R, kRowTile * kQuad);
   p1.nkb = (int32_t)cdiv(a.M, kColBlock);
+  p1.opnd = vt;
+  p1.opnd_term = zt_term_halfs(a.M, a.T);
+  p1.opnd_nkb = p1.nkb;
+  p1.z = zt;
+  p1.z_term = zt_term_halfs(a.R, a.T);
+  p1.z_nkb = (int32_t)cdiv(a.R, kColBlock);
   p2.rows = (int32_t)a.N;
   p2.K = (int32_t)a.R;
   p2.nq = (int32_t)cdiv(a.N, kRowTile * kQuad);
   p2.nkb = (int32_t)cdiv(a.R, kColBlock);
-  if (a.stages & 1) {
+  p2.opnd = zt;
+  p2.opnd_term = zt_term_halfs(a.R, a.T);
+  p2.opnd_nkb = p2.nkb;
+
+  if (a.phases & 1) {
+    PrepVParams pv{};
+    pv.x = a.x;
+    pv.ldx = a.ldx;
+    pv.T = (int32_t)a.T;
+    pv.M = (int32_t)a.M;
+    pv.ell = a.ell;
+    pv.nkb = p1.nkb;
+    pv.multi = a.multi;
+    pv.num_adapters = a.num_adapters;
+    pv.n_units = (int64_t)a.ell * cdiv(a.T, 16) * p1.nkb;
+    pv.gamma = a.single.gamma;
+    pv.ids = a.ids;
+    pv.gammas = a.gammas;
+    pv.v = vt;
+    pv.v_term = p1.opnd_term;
+    hipLaunchKernelGGL(k_prep_v, dim3((unsigned)cdiv(pv.n_units, 4)), dim3(256), 0, s, pv);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.phases & 2) {
     const hipError_t e = launch_stage<1>(p1, s);
     if (e != hipSuccess) return e;
   }
-  return (a.stages & 2) ? launch_stage<2>(p2, s) : hipSuccess;
+  return (a.phases & 4) ? launch_stage<2>(p2, s) : hipSuccess;
 }
 
 }  // namespace dbf

@@ -659,7 +659,7 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
   hipError_t e;
   int64_t n_cb_max, n_cb_est;
   if (a.multi) {
-    if (a.stages & 1) {
+    if (a.phases & 1) {
       e = launch_segment(a, tcb, s);
       if (e != hipSuccess) return e;
     }
@@ -716,7 +716,7 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
   pp.from_z = 0;
   pp.opnd = (uint32_t*)(ws + L.p1o);
   pp.oscl = (uint8_t*)(ws + L.p1s);
-  if ((a.stages & 1) && (e = launch_prep(pp, s)) != hipSuccess) return e;
+  if ((a.phases & 1) && (e = launch_prep(pp, s)) != hipSuccess) return e;
   GemvParams g1 = gp;
   g1.rows = a.R;
   g1.K = a.M;
@@ -724,9 +724,9 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
   g1.nkb = pp.nkb;
   g1.opnd = pp.opnd;
   g1.oscl = pp.oscl;
-  if ((a.stages & 1) && (e = launch_gemv_stage_any<1>(g1, n_cb_est, n_cb_max, a.multi, s)) != hipSuccess)
+  if ((a.phases & 2) && (e = launch_gemv_stage_any<1>(g1, n_cb_est, n_cb_max, a.multi, s)) != hipSuccess)
     return e;
-  if (!(a.stages & 2)) return hipSuccess;
+  if (!(a.phases & 4)) return hipSuccess;
 
   // stage 2: y = sum_i alpha_i * (S1 . z_i)
   pp.K = a.R;

@@ -33,7 +33,7 @@ struct ForwardArgs {
   void* ws;
   size_t ws_bytes;
   Path path;
-  int stages;  // bit 0: stage 1 (z), bit 1: stage 2 (y)
+  int phases;  // bit 0: prep (operands of stage 1), bit 1: stage 1 (z), bit 2: stage 2 (y)
 };
 
 // Largest batch the small-T (fp4 matrix-core) path accepts; its operand
@@ -45,17 +45,17 @@ constexpr int kParts = 3;
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline int64_t ldz_of(int64_t R) { return cdiv(R, 8) * 8; }
 inline int64_t max_colblocks(int64_t T) { return T + cdiv(T, 16) + 1; }
-// Large-T path intermediate z_i (fp16) in MFMA operand order: per term,
-// tiles of 16 tokens x 128 rows of z, each 4 KB = 4 steps x 64 lanes x 8:
-// element (t, r) with k = r % 128 sits at half
+// Large-T path operands v_i = gamma_i * x and z_i (fp16) in MFMA operand
+// order: per term, tiles of 16 tokens x 128 reduction entries, each 4 KB =
+// 4 steps x 64 lanes x 8: entry (t, r) with k = r % 128 sits at half
 //   ((t/16 * nkb + r/128) * 4 + k/32) * 512 + (16 * (k/8 % 4) + t%16) * 8 + k%8
-// so the 16 tokens x 32 rows a wave reads for one MFMA step are 1 KB
-// contiguous.
-inline int64_t zt_term_halfs(int64_t R, int64_t T) { return cdiv(T, 16) * cdiv(R, 128) * 2048; }
+// so the 16 tokens x 32 entries a wave reads for one MFMA step are 1 KB
+// contiguous.  (K = reduction length, nkb = ceil(K/128).)
+inline int64_t zt_term_halfs(int64_t K, int64_t T) { return cdiv(T, 16) * cdiv(K, 128) * 2048; }
 
 // Byte offsets of the workspace regions.
 struct WsLayout {
-  size_t cbl, z, p1o, p1s, p2o, p2s, total;
+  size_t cbl, z, v, p1o, p1s, p2o, p2s, total;
 };
 
 inline WsLayout ws_layout(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T) {
@@ -73,6 +73,9 @@ inline WsLayout ws_layout(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t 
   const size_t z32 = (size_t)ell * T * ldz_of(R) * sizeof(float);
   const size_t z16 = (size_t)ell * zt_term_halfs(R, T) * sizeof(half_t);
   off += align256(z32 > z16 ? z32 : z16);
+  // large-T path: v_i = gamma_i * x, fp16 tiles like z (16 tokens x 128 cols)
+  w.v = off;
+  off += align256((size_t)ell * zt_term_halfs(M, T) * sizeof(half_t));
   w.p1o = off;
   off += align256(n1 * 32);
   w.p1s = off;

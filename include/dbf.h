@@ -57,13 +57,18 @@ typedef int32_t dbf_dtype;
                              default overwrites y                            */
 #define DBF_PATH_GEMV 2u  /* force the small-T (decode) kernels  (tuning/tests) */
 #define DBF_PATH_MFMA 4u  /* force the large-T (prefill) kernels (tuning/tests) */
-/* Split one product into its two launch groups (profiling, or overlapping
-   other work between them).  STAGE1_ONLY computes z_i = beta_i * (B2
-   (gamma_i * x)) into ws and leaves y untouched; STAGE2_ONLY computes y from
-   the z that a STAGE1_ONLY call with the same arguments, workspace and path
-   flag left in ws, on the same stream.  Without either flag both run. */
-#define DBF_STAGE1_ONLY 8u
-#define DBF_STAGE2_ONLY 16u
+/* Run only some phases of one product (profiling, or overlapping other work
+   between them); with none of these bits set, all three run.  A phase reads
+   what the earlier phases of a call with the same arguments, workspace and
+   path flag left in ws, on the same stream.
+     DBF_RUN_PREP    the activation operands gamma_i * x (and, with several
+                     adapters, the token runs) into ws
+     DBF_RUN_STAGE1  z_i = beta_i * (B2 (gamma_i * x)) into ws
+     DBF_RUN_STAGE2  y from z (the only phase that writes y)
+   On the large-T path each phase is one kernel launch. */
+#define DBF_RUN_PREP 8u
+#define DBF_RUN_STAGE1 16u
+#define DBF_RUN_STAGE2 32u
 
 #define DBF_ABI_VERSION 1
 

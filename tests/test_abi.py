@@ -89,7 +89,6 @@ def _fwd(**kw):
     (dict(y_type=7), _lib.DBF_ERR_INVALID_ARG),
     (dict(flags=64), _lib.DBF_ERR_INVALID_ARG),
     (dict(flags=_lib.DBF_PATH_GEMV | _lib.DBF_PATH_MFMA), _lib.DBF_ERR_INVALID_ARG),
-    (dict(flags=_lib.DBF_STAGE1_ONLY | _lib.DBF_STAGE2_ONLY), _lib.DBF_ERR_INVALID_ARG),
     (dict(flags=128), _lib.DBF_ERR_INVALID_ARG),
     (dict(x=MIS), _lib.DBF_ERR_ALIGNMENT),
     (dict(y=MIS), _lib.DBF_ERR_ALIGNMENT),

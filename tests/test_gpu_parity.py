@@ -289,12 +289,13 @@ def test_multi_adapter_stream_path(integer):
         assert err <= TOL, err
 
 
-# ------------------------------------------------- split launch groups --
+# ------------------------------------------------------- split phases --
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("shape", [(300, 130, 260, 1, 37), (64, 16, 8, 3, 70)])
 def test_stage_split_equals_whole(shape, path):
-    """STAGE1_ONLY then STAGE2_ONLY on one workspace gives the whole call's
-    result bit for bit, and STAGE1_ONLY leaves y untouched."""
+    """The three phases run one at a time on one workspace give the whole
+    call's result bit for bit, and the phases before stage 2 leave y
+    untouched."""
     N, R, M, ell, T = shape
     L = synth.make_layer(N, R, M, ell, T, seed=81)
     pl = H().upload(L)
@@ -303,10 +304,11 @@ def test_stage_split_equals_whole(shape, path):
     ws = torch.empty(dbf_ws(N, R, M, ell, T), dtype=torch.uint8, device="cuda")
     y = H().empty_rows(T, N, torch.float16)
     y.fill_(7.0)
-    pl.forward(x, path=path, y=y, ws=ws, stage=1)
+    pl.forward(x, path=path, y=y, ws=ws, phases="prep")
+    pl.forward(x, path=path, y=y, ws=ws, phases="stage1")
     torch.cuda.synchronize()
     assert bool((y == 7.0).all())
-    pl.forward(x, path=path, y=y, ws=ws, stage=2)
+    pl.forward(x, path=path, y=y, ws=ws, phases=["stage2"])
     torch.cuda.synchronize()
     assert torch.equal(y, y_whole)
 
@@ -319,8 +321,8 @@ def test_stage_split_multi_adapter(path):
     y_whole = D.forward(x, ids, path=path, y=H().empty_rows(90, 96, torch.float16))
     ws = torch.empty(dbf_ws(96, 48, 160, 2, 90), dtype=torch.uint8, device="cuda")
     y = H().empty_rows(90, 96, torch.float16)
-    D.forward(x, ids, path=path, y=y, ws=ws, stage=1)
-    D.forward(x, ids, path=path, y=y, ws=ws, stage=2)
+    D.forward(x, ids, path=path, y=y, ws=ws, phases=["prep", "stage1"])
+    D.forward(x, ids, path=path, y=y, ws=ws, phases="stage2")
     torch.cuda.synchronize()
     assert torch.equal(y, y_whole)
 
