@@ -191,26 +191,32 @@ struct GemvParams {
 // `srow` gives the per-row output scale of this lane's term (beta_ci for
 // stage 1, alpha_ci for stage 2): srow[r] for the rows of `tile`; with
 // SCALE_LDS it points into shared memory.
+// Value of lane + n within the lane's row of 16 (0 past the row's end):
+// DPP row_shl:n, a VALU move with no LDS round trip.
+template <int n>
+__device__ inline float row_next(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x100 + n, 0xF, 0xF, true));
+}
+
 template <int STAGE, bool SCALE_LDS = false>
 __device__ inline void gemv_epilogue(const GemvParams& p, const half_t* srow, v4f sum,
                                      int64_t tile, int lane, int g, int part, bool colv, int ci,
                                      int ct, int ntok, int64_t t0) {
   const int64_t r0 = tile * kRowTile + 4 * g;
+  // the parts of a column are lanes j, j+1, j+2 of one row of 16 (j <= 13)
   float tot[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float d1 = __shfl(sum[v], lane + 1 < 64 ? lane + 1 : lane);
-    const float d2 = __shfl(sum[v], lane + 2 < 64 ? lane + 2 : lane);
-    tot[v] = (sum[v] + d1) + d2;
-  }
+  for (int v = 0; v < 4; ++v) tot[v] = (sum[v] + row_next<1>(sum[v])) + row_next<2>(sum[v]);
   float sc[4];
+  if (SCALE_LDS) {
+    // staged rows are zero past p.rows: one 8-byte LDS read, no guards
+    typedef const __attribute__((address_space(3))) v4h* lds_v4hp;
+    const v4h s4 = *(lds_v4hp)(srow + r0);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    if (SCALE_LDS)
-      sc[v] = (r0 + v < p.rows) ? (float)((const __attribute__((address_space(3))) half_t*)srow)[r0 + v]
-                                : 0.0f;
-    else
-      sc[v] = (r0 + v < p.rows) ? (float)srow[r0 + v] : 0.0f;
+    for (int v = 0; v < 4; ++v) sc[v] = (float)s4[v];
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sc[v] = (r0 + v < p.rows) ? (float)srow[r0 + v] : 0.0f;
   }
   if (STAGE == 1) {
     if (part == 0 && colv && r0 < p.rows) {
@@ -223,13 +229,19 @@ __device__ inline void gemv_epilogue(const GemvParams& p, const half_t* srow, v4
     float val[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) val[v] = (part == 0 && colv) ? tot[v] * sc[v] : 0.0f;
-    // sum the ell terms of token ct: their part-0 lanes are 3*(i*ntok + ct)
+    // sum the ell terms of token ct: their part-0 lanes are 3*(i*ntok + ct);
+    // with one term that is this lane itself
     float o[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int ii = 0; ii < p.ell; ++ii) {
-      int src = 16 * g + kParts * (ii * ntok + ct);
-      src = src < 64 ? src : lane;
+    if (p.ell == 1) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) o[v] += __shfl(val[v], src);
+      for (int v = 0; v < 4; ++v) o[v] += val[v];
+    } else {
+      for (int ii = 0; ii < p.ell; ++ii) {
+        int src = 16 * g + kParts * (ii * ntok + ct);
+        src = src < 64 ? src : lane;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] += __shfl(val[v], src);
+      }
     }
     if (part == 0 && colv && ci == 0 && r0 < p.rows) {
       if (p.accumulate) {
@@ -467,6 +479,20 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
       const int64_t nkc = (p.nkb - k0) < kchunk ? (p.nkb - k0) : kchunk;
       const int64_t nkc_pad = (nkc + D - 1) / D * D;
       __syncthreads();  // every wave is done with the previous chunk's LDS
+      // output scales of this item's rows for every term (first chunk only),
+      // requested together with the B pieces below
+      constexpr int kSrPer = (5 * ROWS_ITEM + 255) / 256;  // ell <= 5 on this path
+      half_t srv[kSrPer];
+      if (k0 == 0) {
+        const half_t* sv = STAGE == 1 ? f.beta : f.alpha;
+#pragma unroll
+        for (int u = 0; u < kSrPer; ++u) {
+          const int e = threadIdx.x + u * 256;
+          const int i = e / ROWS_ITEM, rr = e - i * ROWS_ITEM;
+          srv[u] = (e < p.ell * ROWS_ITEM && row0 + rr < p.rows)
+                       ? sv[(int64_t)i * p.rows + row0 + rr] : (half_t)0.0f;
+        }
+      }
       // stage the live B pieces (block, column, g, half) of 16 bytes at byte
       // e*16; each thread issues all loads of a pass before its LDS writes
       {
@@ -506,11 +532,11 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
           }
         }
       }
-      if (k0 == 0) {  // output scales of this item's rows, for every term
-        const half_t* sv = STAGE == 1 ? f.beta : f.alpha;
-        for (int e = threadIdx.x; e < p.ell * ROWS_ITEM; e += blockDim.x) {
-          const int i = e / ROWS_ITEM, rr = e - i * ROWS_ITEM;
-          srows[e] = (row0 + rr < p.rows) ? sv[(int64_t)i * p.rows + row0 + rr] : (half_t)0.0f;
+      if (k0 == 0) {
+#pragma unroll
+        for (int u = 0; u < kSrPer; ++u) {
+          const int e = threadIdx.x + u * 256;
+          if (e < p.ell * ROWS_ITEM) srows[e] = srv[u];
         }
       }
       __syncthreads();
@@ -535,11 +561,15 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
       for (int qi = 0; qi < QPW; ++qi) {
         if (qi >= nqw) break;
         const char* cur = S0 + qi * qbytes;
-        const char* nxt = (qi + 1 < nqw) ? cur + qbytes : cur;
+        const bool last_quad = qi + 1 >= nqw;
+        const char* nxt = last_quad ? cur : cur + qbytes;
         for (int kb0 = 0; kb0 < nkp; kb0 += D) {
           const bool same = kb0 + D < nkp;
           const char* src = same ? cur : nxt;
-          const int kn0 = same ? kb0 + D : 0;
+          // past the wave's last block the refills re-read that block (just
+          // loaded, so a cache hit): their registers are reused after the
+          // loop, which waits for them
+          const int kn0 = same ? kb0 + D : (last_quad ? nk - 1 : 0);
           // lanes of live columns read [kb][j][g] (padding blocks are staged
           // zeros); the others read the zero slot with stride 0
           const uint8_t* bstep = colv ? bl + ((kb0 * ncols + j) * 4 + g) * 32 : zslot;
@@ -557,7 +587,7 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
             const v8i a2 = expand_signs_fp4(w[2], p.sign_mask, p.fp4_one);
             const v8i a3 = expand_signs_fp4(w[3], p.sign_mask, p.fp4_one);
             __builtin_amdgcn_sched_barrier(0);
-            const int kn = kn0 + u < nk ? kn0 + u : 0;
+            const int kn = (!same && last_quad) ? kn0 : (kn0 + u < nk ? kn0 + u : nk - 1);
             ring[u] = *(gv4up)(src + (kn << 10) + lane16);
             const uint8_t* bp = bstep + u * bstride;
             const v4u lo = *(const v4u*)bp, hi = *(const v4u*)(bp + 16);
@@ -589,9 +619,10 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
     // epilogue of this wave's tiles (its own partials; the scales were
     // staged before the last barrier)
     const half_t* srow = srows + ci * ROWS_ITEM - row0;
-    for (int e = 0; e < nqw * 4; ++e) {
+#pragma unroll
+    for (int e = 0; e < QPW * 4; ++e) {
       const int64_t tile = (qw0 + 4 * (e >> 2)) * kQuad + (e & 3);
-      if (tile < p.nrt)
+      if (e < nqw * 4 && tile < p.nrt)
         gemv_epilogue<STAGE, true>(p, srow, partial[(wv * QPW * 4 + e) * 64 + lane], tile, lane, g,
                                    part, colv, ci, ct, ntok, t0);
     }
