@@ -7,8 +7,9 @@
 // v_mfma_f32_16x16x32_f16 with fp32 accumulation; the operands v_i =
 // gamma_i*x and z_i = beta_i*u_i are rounded to fp16 once each.
 //
-// Launches: prep (v_i = gamma_i * x) -> stage 1 (z_i = beta_i * B2 v_i) ->
-// stage 2 (y = sum_i alpha_i * B1 z_i).  v and z live in the workspace in
+// Launches: prep (v_i = gamma_i * x; with several adapters one extra
+// workgroup also builds the column blocks) -> stage 1 (z_i = beta_i * B2 v_i)
+// -> stage 2 (y = sum_i alpha_i * B1 z_i).  v and z live in the workspace in
 // MFMA operand order: tiles of 16 tokens x 128 reduction entries, 4 KB each
 // (4 steps x 64 lanes x 8), so every operand load of a wave is 1 KB
 // contiguous, and entries past the reduction length are zero, so the last
@@ -122,8 +123,6 @@ __device__ inline int64_t tile_off(int t, int k, int nkb) {
          (16 * ((kk >> 3) & 3) + (t & 15)) * 8 + (kk & 7);
 }
 
-__device__ inline int32_t norm_adapter(int32_t id, int32_t n) { return (id >= 0 && id < n) ? id : -1; }
-
 struct PrepVParams {
   const half_t* x;
   int64_t ldx;
@@ -134,6 +133,11 @@ struct PrepVParams {
   const half_t* const* gammas;
   half_t* v;
   int64_t v_term;
+  // multi-adapter column blocks, built by the extra workgroup n_units / 4
+  // (none when seg_cbl is null)
+  ColBlock* seg_cbl;
+  WsHeader* seg_hdr;
+  int32_t seg_chunk;
 };
 
 // v_i = fp16(gamma_i * x) in operand tiles, one wave per (term, 16-token
@@ -142,6 +146,10 @@ struct PrepVParams {
 // past T and tokens whose adapter id is out of range are zero.  One fp16
 // rounding of the exact product.
 __global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
+  if (p.seg_cbl != nullptr && (int64_t)blockIdx.x == cdiv(p.n_units, 4)) {
+    segment_ids(p.ids, p.T, p.num_adapters, p.seg_chunk, p.seg_cbl, p.seg_hdr);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (u >= p.n_units) return;  // uniform per wave
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
   const half_t* gam = nullptr;
   if (t < p.T) {
     if (p.multi) {
-      const int32_t ad = norm_adapter(p.ids[t], p.num_adapters);
+      const int32_t ad = norm_id(p.ids[t], p.num_adapters);
       if (ad >= 0) gam = p.gammas[ad];
     } else {
       gam = p.gamma;
@@ -397,11 +405,8 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   char* ws = (char*)a.ws;
   GemmParams p{};
   if (a.multi) {
-    // column blocks of at most kGemmChunk tokens of one adapter
-    if (a.phases & 1) {
-      const hipError_t e = launch_segment(a, kGemmChunk, s);
-      if (e != hipSuccess) return e;
-    }
+    // column blocks of at most kGemmChunk tokens of one adapter (built by
+    // the prep launch)
     int64_t n_cb = a.T + cdiv(a.T, kGemmChunk);
     if (n_cb > max_colblocks(a.T)) n_cb = max_colblocks(a.T);
     p.n_cb_host = (int32_t)n_cb;
@@ -460,7 +465,13 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
     pv.gammas = a.gammas;
     pv.v = vt;
     pv.v_term = p1.opnd_term;
-    hipLaunchKernelGGL(k_prep_v, dim3((unsigned)cdiv(pv.n_units, 4)), dim3(256), 0, s, pv);
+    if (a.multi) {
+      pv.seg_cbl = (ColBlock*)(ws + L.cbl);
+      pv.seg_hdr = (WsHeader*)ws;
+      pv.seg_chunk = kGemmChunk;
+    }
+    const int64_t grid = cdiv(pv.n_units, 4) + (a.multi ? 1 : 0);
+    hipLaunchKernelGGL(k_prep_v, dim3((unsigned)grid), dim3(256), 0, s, pv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -17,7 +17,9 @@
 // epilogue.  So one 16x16x128 MFMA covers 16 rows x 128 reduction entries
 // for up to floor(16 / (3*ell)) tokens x ell terms.
 //
-// Launches: prep(x) -> stage 1 (writes z = beta*u, fp32) -> prep(z) -> stage 2.
+// Launches: prep(x) (with several adapters one extra workgroup also builds
+// the column blocks) -> stage 1 (writes z = beta*u, fp32) -> prep(z) ->
+// stage 2.
 #include "dbf_device.h"
 #include "dbf_launch.h"
 
@@ -42,9 +44,8 @@ __device__ inline uint32_t e4m3_rne(float a, float& q) {
     q = __builtin_copysignf(qn * (1.0f / 512.0f), a);
     return sgn | (uint32_t)qn;
   }
-  const float step = __builtin_ldexpf(1.0f, e - 3);
-  const float qn = __builtin_rintf(m / step);  // 8..16
-  q = __builtin_copysignf(qn * step, a);
+  const float qn = __builtin_rintf(__builtin_ldexpf(m, 3 - e));  // 8..16, m / 2^(e-3) exactly
+  q = __builtin_copysignf(__builtin_ldexpf(qn, e - 3), a);
   return sgn | (((uint32_t)(e + 7) << 3) + (uint32_t)(qn - 8.0f));
 }
 
@@ -63,6 +64,12 @@ struct PrepParams {
   const half_t* const* gammas;
   uint32_t* opnd;  // [ell][T][nkb][kParts][4] x 8 words
   uint8_t* oscl;   // [ell][T][nkb][kParts][4]
+  // multi-adapter column blocks, built by the extra workgroup seg_block
+  // (none when seg_cbl is null)
+  ColBlock* seg_cbl;
+  WsHeader* seg_hdr;
+  int32_t seg_chunk;
+  int64_t seg_block;
 };
 
 // K order of an fp8 operand of v_mfma_scale_f32_16x16x128_f8f6f4 inside a
@@ -82,17 +89,55 @@ __device__ inline int operand_k_of_col(int c) {
   return ((c & 0x18) << 2) | ((c & 0x60) >> 2) | (c & 7);
 }
 
+// Maximum over the wave, returned in every lane: DPP within rows of 16
+// (quad swaps, then half-row and row mirrors), then the four row maxima
+// read as scalars; no LDS traffic.
+template <int ctrl>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false));
+}
 __device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// The kParts fp8 parts of one 128-block whose entries 2*lane and 2*lane+1
+// this lane holds; every lane of the wave must call it (wave reductions).
+// Each part has one E8M0 scale for the whole block (the block maximum is a
+// wave reduction), so the scale is the same whichever 32 entries the
+// hardware attaches a lane's scale to.  For each part, put(part, code, s)
+// receives the pair's e4m3 codes (entry 2*lane in the low byte) and the
+// part's scale exponent s; the pair's byte offset inside the part's 128
+// operand bytes is fp8_operand_byte(operand_k_of_col(2*lane)).
+template <typename Put>
+__device__ inline void block_parts(float v0, float v1, Put&& put) {
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  for (int part = 0; part < kParts; ++part) {
+    const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    int s = mx > 0.0f ? floor_log2_pos(mx) - 7 : 0;  // scaled block max in [128, 256)
+    s = s < -127 ? -127 : (s > 127 ? 127 : s);
+    const float down = __builtin_ldexpf(1.0f, -s), up = __builtin_ldexpf(1.0f, s);
+    float q0, q1;
+    const uint32_t c0 = e4m3_rne(v0 * down, q0), c1 = e4m3_rne(v1 * down, q1);
+    v0 -= q0 * up;  // exact: q*up is v rounded on a grid no finer than v's own
+    v1 -= q1 * up;
+    put(part, (uint16_t)(c0 | (c1 << 8)), s);
+  }
 }
 
 // One wave per (term, token, 128-block); lane l owns entries 2l and 2l+1.
-// The block is split into kParts fp8 parts; each part has one E8M0 scale
-// for the whole block (the block maximum is a wave reduction), so the scale
-// is the same whichever 32 entries the hardware attaches a lane's scale to.
 __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
+  if (p.seg_cbl != nullptr && (int64_t)blockIdx.x == p.seg_block) {
+    segment_ids(p.ids, (int32_t)p.T, p.num_adapters, p.seg_chunk, p.seg_cbl, p.seg_hdr);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nblk = (int64_t)p.ell * p.T * p.nkb;
@@ -126,19 +171,10 @@ __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
   uint8_t* out = (uint8_t*)p.opnd + blk * (kParts * 4 * 32);
   // kl even: cols kl, kl+1 meet adjacent operand entries, i.e. adjacent bytes
   const int boff = fp8_operand_byte(operand_k_of_col(kl));
-#pragma unroll
-  for (int part = 0; part < kParts; ++part) {
-    const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-    int s = mx > 0.0f ? floor_log2_pos(mx) - 7 : 0;  // scaled block max in [128, 256)
-    s = s < -127 ? -127 : (s > 127 ? 127 : s);
-    const float down = __builtin_ldexpf(1.0f, -s), up = __builtin_ldexpf(1.0f, s);
-    float q0, q1;
-    const uint32_t c0 = e4m3_rne(v0 * down, q0), c1 = e4m3_rne(v1 * down, q1);
-    v0 -= q0 * up;  // exact: q*up is v rounded on a grid no finer than v's own
-    v1 -= q1 * up;
-    *(uint16_t*)(out + part * 128 + boff) = (uint16_t)(c0 | (c1 << 8));
+  block_parts(v0, v1, [&](int part, uint16_t code, int s) {
+    *(uint16_t*)(out + part * 128 + boff) = code;
     if (lane < 4) p.oscl[blk * (kParts * 4) + part * 4 + lane] = (uint8_t)(s + 127);
-  }
+  });
 }
 
 // ---------------------------------------------------------- stage kernel ----
@@ -384,6 +420,51 @@ __global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
   }
 }
 
+// Stage the live B operand pieces of blocks [k0, k0 + nkc) of a column block
+// (tokens t0.., ncols = kParts * ell * ntok columns) from the prep output into
+// LDS: piece e = ((block * ncols + column) * 4 + g) * 2 + half holds 16 bytes
+// at bl + 16 e, and bs[block * 16 + column] the column's scale code.  Blocks
+// nkc .. nkc_pad-1 are padding: zero operands with scale 1.0.  Each thread
+// issues all loads of a pass before its LDS writes.  Workgroup-wide.
+__device__ inline void stage_b(const GemvParams& p, uint8_t* bl, uint8_t* bs, int64_t k0, int nkc,
+                               int nkc_pad, int ncols, int ntok, int64_t t0) {
+  const int nlive = nkc * ncols * 8;      // < 2^31 (LDS-bounded)
+  const int npiece = nkc_pad * ncols * 8;
+  const int64_t tb = (int64_t)p.T * p.nkb * (kParts * 4);  // idx stride of one term
+  const int64_t ib = ((t0 * p.nkb + k0) * kParts) * 4;     // idx of (term 0, token t0, block k0)
+  constexpr int PT = 4;
+  for (int e0 = threadIdx.x; e0 < npiece; e0 += PT * (int)blockDim.x) {
+    v4u v[PT];
+    uint32_t sc[PT];
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int e = e0 + q * (int)blockDim.x;
+      const int ee = e < nlive ? e : 0;
+      const int half = ee & 1, gg = (ee >> 1) & 3;
+      const int rest = ee >> 3;
+      const int kbl = rest / ncols, col = rest - kbl * ncols;
+      const int cc = col / kParts, cpart = col - kParts * cc;
+      const int cci = cc / ntok, cct = cc - ntok * cci;
+      const int64_t idx =
+          cci * tb + ib + ((int64_t)cct * p.nkb + kbl) * (kParts * 4) + cpart * 4 + gg;
+      v[q] = *(gv4up)(p.opnd + idx * 8 + half * 4);
+      sc[q] = p.oscl[idx];
+    }
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int e = e0 + q * (int)blockDim.x;
+      if (e < npiece) {
+        const bool lv = e < nlive;
+        *(v4u*)(bl + e * 16) = lv ? v[q] : v4u{0u, 0u, 0u, 0u};
+        if ((e & 7) == 0) {
+          const int rest = e >> 3, kbl = rest / ncols;
+          bs[kbl * 16 + (rest - kbl * ncols)] = lv ? (uint8_t)sc[q] : (uint8_t)127;
+        }
+      }
+    }
+  }
+}
+
 // Throughput kernel for many row quads (batched decode over many layers).
 // Work item: (column block, group of 4*QPW row quads); wave w of the
 // workgroup owns quads w, w+4, ... of the group over the WHOLE reduction, so
@@ -396,9 +477,8 @@ __global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
 // a clamped in-range address, padding steps meet a zero B operand).  The
 // streaming loops hold loads and matrix ops only; tiles are parked in LDS and
 // finished by one epilogue loop.
-template <int STAGE, int QPW>
+template <int STAGE, int QPW, int D>
 __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
-  constexpr int D = 8;
   constexpr int ROWS_ITEM = 4 * QPW * kQuad * kRowTile;  // rows of one item
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // LDS: staged B operands [blocks][live column][g][32 B] (p.lds_b bytes),
@@ -479,6 +559,20 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
       const int64_t nkc = (p.nkb - k0) < kchunk ? (p.nkb - k0) : kchunk;
       const int64_t nkc_pad = (nkc + D - 1) / D * D;
       __syncthreads();  // every wave is done with the previous chunk's LDS
+      // A words: this wave's quads are contiguous runs of 1 KB units; the
+      // address is a uniform base plus lane*16 (scalar-base global loads).
+      // The first D are requested before the staging below, so their memory
+      // latency overlaps the staging's.
+      const char* S0 = S + ((qw0 * p.nkb + k0) << 10);
+      const int64_t qbytes = (int64_t)4 * p.nkb << 10;  // between this wave's quads
+      const int lane16 = lane * 16;
+      const int nk = (int)nkc, nkp = (int)nkc_pad;
+      v4u ring[D];
+      if (nqw > 0) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) ring[u] = *(gv4up)(S0 + ((u < nk ? u : 0) << 10) + lane16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // output scales of this item's rows for every term (first chunk only),
       // requested together with the B pieces below
       constexpr int kSrPer = (5 * ROWS_ITEM + 255) / 256;  // ell <= 5 on this path
@@ -493,45 +587,7 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
                        ? sv[(int64_t)i * p.rows + row0 + rr] : (half_t)0.0f;
         }
       }
-      // stage the live B pieces (block, column, g, half) of 16 bytes at byte
-      // e*16; each thread issues all loads of a pass before its LDS writes
-      {
-        const int nlive = (int)nkc * ncols * 8;      // < 2^31 (LDS-bounded)
-        const int npiece = (int)nkc_pad * ncols * 8;  // padding blocks: zeros, scale 1.0
-        const int64_t tb = (int64_t)p.T * p.nkb * (kParts * 4);  // idx stride of one term
-        const int64_t ib = ((t0 * p.nkb + k0) * kParts) * 4;     // idx of (term 0, token t0, block k0)
-        constexpr int PT = 4;
-        for (int e0 = threadIdx.x; e0 < npiece; e0 += PT * (int)blockDim.x) {
-          v4u v[PT];
-          uint32_t sc[PT];
-#pragma unroll
-          for (int q = 0; q < PT; ++q) {
-            const int e = e0 + q * (int)blockDim.x;
-            const int ee = e < nlive ? e : 0;
-            const int half = ee & 1, gg = (ee >> 1) & 3;
-            const int rest = ee >> 3;
-            const int kbl = rest / ncols, col = rest - kbl * ncols;
-            const int cc = col / kParts, cpart = col - kParts * cc;
-            const int cci = cc / ntok, cct = cc - ntok * cci;
-            const int64_t idx = cci * tb + ib + ((int64_t)cct * p.nkb + kbl) * (kParts * 4) +
-                                cpart * 4 + gg;
-            v[q] = *(gv4up)(p.opnd + idx * 8 + half * 4);
-            sc[q] = p.oscl[idx];
-          }
-#pragma unroll
-          for (int q = 0; q < PT; ++q) {
-            const int e = e0 + q * (int)blockDim.x;
-            if (e < npiece) {
-              const bool lv = e < nlive;
-              *(v4u*)(bl + e * 16) = lv ? v[q] : v4u{0u, 0u, 0u, 0u};
-              if ((e & 7) == 0) {
-                const int rest = e >> 3, kbl = rest / ncols;
-                bs[kbl * 16 + (rest - kbl * ncols)] = lv ? (uint8_t)sc[q] : (uint8_t)127;
-              }
-            }
-          }
-        }
-      }
+      stage_b(p, bl, bs, k0, (int)nkc, (int)nkc_pad, ncols, ntok, t0);
       if (k0 == 0) {
 #pragma unroll
         for (int u = 0; u < kSrPer; ++u) {
@@ -541,16 +597,6 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
       }
       __syncthreads();
       if (nqw == 0) continue;
-
-      // A words: this wave's quads are contiguous runs of 1 KB units; the
-      // address is a uniform base plus lane*16 (scalar-base global loads)
-      const char* S0 = S + ((qw0 * p.nkb + k0) << 10);
-      const int64_t qbytes = (int64_t)4 * p.nkb << 10;  // between this wave's quads
-      const int lane16 = lane * 16;
-      const int nk = (int)nkc, nkp = (int)nkc_pad;
-      v4u ring[D];
-#pragma unroll
-      for (int u = 0; u < D; ++u) ring[u] = *(gv4up)(S0 + ((u < nk ? u : 0) << 10) + lane16);
 
       v4f acc[QPW][4];
 #pragma unroll
@@ -629,6 +675,291 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
   }
 }
 
+// ------------------------------------------------------- fused decode ----
+
+// Streams one stage of a fused column block: wave wv of NW owns row quads
+// wv, wv+NW, ... (nqw of them) of the stage's sign matrix (S: the wave's first
+// quad); each quad's four tiles are finished by the epilogue right after its
+// last block, while the ring's loads for the next quad are in flight.  The
+// ring of D sign loads per lane runs on across quads; after the last quad it
+// fetches the first blocks of `tail` (the wave's first quad of the next
+// stage, tail_nk blocks long), or re-reads the last block when tail is null.
+// B operands and their scales come from LDS (bl, bs: blocks padded to a
+// multiple of D with zero operands); srow points at the LDS output scales of
+// this lane's term.
+template <int STAGE, int D, int NW>
+__device__ inline void fused_stream(const GemvParams& p, const char* S, int nqw, int wv, int lane,
+                                    v4u (&ring)[D], const char* tail, int tail_nk,
+                                    const uint8_t* bl, const uint8_t* bs, const uint8_t* zslot,
+                                    const half_t* srow, int ncols, bool colv, int j, int g,
+                                    int part, int ci, int ct, int ntok, int64_t t0) {
+  const int lane16 = lane * 16;
+  const int nk = (int)p.nkb, nkp = (nk + D - 1) / D * D;
+  const int64_t qstride = (int64_t)NW * nk << 10;
+  // lanes of live columns read [kb][j][g]; the others read the zero slot
+  const uint8_t* bbase = colv ? bl + (j * 4 + g) * 32 : zslot;
+  const int bstride = colv ? ncols * 128 : 0;
+  const uint8_t* sbase = colv ? bs + j : zslot + 32;
+  const int sstride = colv ? 16 : 0;
+  for (int qi = 0; qi < nqw; ++qi) {
+    const char* cur = S + qi * qstride;
+    const bool lastq = qi + 1 == nqw;
+    const char* nxt = lastq ? tail : cur + qstride;
+    const int nxt_nk = lastq ? tail_nk : nk;
+    v4f acc[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) acc[h] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int kb0 = 0; kb0 < nkp; kb0 += D) {
+      const bool same = kb0 + D < nkp;
+      const char* src = same ? cur : (nxt != nullptr ? nxt : cur);
+      const int kn0 = same ? kb0 + D : (nxt != nullptr ? 0 : nk - 1);
+      const int lim = same ? nk : (nxt != nullptr ? nxt_nk : nk);
+      const uint8_t* bstep = bbase + kb0 * bstride;
+      const uint8_t* sstep = sbase + kb0 * sstride;
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        // expand the slot's four words, then refill the slot (the refill
+        // stays after the last read of the old value)
+        const v4u w = ring[u];
+        const v8i a0 = expand_signs_fp4(w[0], p.sign_mask, p.fp4_one);
+        const v8i a1 = expand_signs_fp4(w[1], p.sign_mask, p.fp4_one);
+        const v8i a2 = expand_signs_fp4(w[2], p.sign_mask, p.fp4_one);
+        const v8i a3 = expand_signs_fp4(w[3], p.sign_mask, p.fp4_one);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kn = kn0 + u < lim ? kn0 + u : lim - 1;
+        ring[u] = __builtin_nontemporal_load((gv4up)(src + ((int64_t)kn << 10) + lane16));
+        const uint8_t* bp = bstep + u * bstride;
+        const v4u lo = *(const v4u*)bp, hi = *(const v4u*)(bp + 16);
+        const v8i bop = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const int bsc = sstep[u * sstride];
+        acc[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, bop, acc[0], 4, 0, 0, 127, 0, bsc);
+        acc[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, bop, acc[1], 4, 0, 0, 127, 0, bsc);
+        acc[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, bop, acc[2], 4, 0, 0, 127, 0, bsc);
+        acc[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a3, bop, acc[3], 4, 0, 0, 127, 0, bsc);
+      }
+    }
+    const int64_t q = wv + NW * (int64_t)qi;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int64_t tile = q * kQuad + h;
+      if (tile < p.nrt)
+        gemv_epilogue<STAGE, true>(p, srow, acc[h], tile, lane, g, part, colv, ci, ct, ntok, t0);
+    }
+  }
+}
+
+// Inputs of the fused kernel besides the two stages' parameters.
+struct FusedArgs {
+  int32_t rows_pad;  // output-scale rows staged per term: max(R, N) rounded up to 64
+  int32_t n_slots;   // column blocks one workgroup can own: ceil(max blocks / grid)
+  int32_t chunk;     // tokens per column block at most
+  int32_t num_adapters;
+  const int32_t* ids;
+  const half_t* x;
+  int64_t ldx;
+  const half_t* const* gammas;
+};
+
+// Writes the fp8 parts of the operand columns (term i, token tt) of block kb
+// into the LDS operand area, from the two entries v0, v1 (block cols 2*lane,
+// 2*lane+1) of this lane; the arithmetic of the prep kernel.  Wave-wide.
+__device__ inline void parts_to_lds(float v0, float v1, uint8_t* bl, uint8_t* bs, int kb, int col0,
+                                    int ncols, int lane) {
+  uint8_t* dst = bl + ((int64_t)kb * ncols + col0) * 128 + fp8_operand_byte(operand_k_of_col(2 * lane));
+  block_parts(v0, v1, [&](int pp, uint16_t code, int sc) {
+    *(uint16_t*)(dst + pp * 128) = code;
+    if (lane == 0) bs[kb * 16 + col0 + pp] = (uint8_t)(sc + 127);
+  });
+}
+
+// Zero operands with scale 1.0 for the padding blocks [nk, nkp).  Workgroup-wide.
+__device__ inline void pad_blocks(uint8_t* bl, uint8_t* bs, int nk, int nkp, int ncols) {
+  for (int e = threadIdx.x; e < (nkp - nk) * ncols * 8; e += blockDim.x)
+    *(v4u*)(bl + ((int64_t)nk * ncols * 8 + e) * 16) = v4u{0u, 0u, 0u, 0u};
+  for (int e = threadIdx.x; e < (nkp - nk) * 16; e += blockDim.x) bs[nk * 16 + e] = 127;
+}
+
+// The whole multi-adapter product for many column blocks (batched decode)
+// in one launch.  Each workgroup segments the ids itself (every workgroup
+// finds the same list) and keeps the column blocks b, b + G, ... (G =
+// workgroups); for each it builds the stage-1 operands gamma_i * x in fp8
+// parts directly in LDS, streams stage 1 over every row quad of its adapter
+// (z = beta * u goes to the workspace, fp32), turns its own z into the
+// stage-2 parts in LDS, and streams stage 2.  No other launch, no other
+// workgroup and no per-item set-up lies between the steps, and the stage-1
+// ring ends by fetching the first stage-2 sign blocks.  The parts are those
+// of the prep kernel, so the result equals the split-phase path's.  p1/p2
+// describe stage 1 (rows R, reduction M) and stage 2 (rows N, reduction R).
+// NW waves per workgroup: with one column block per compute unit, several
+// waves per SIMD hide each other's LDS and matrix-core latencies.  The sign
+// words are read once, so their loads are non-temporal.
+// LDS: B operands [blocks][column][g][32 B] (p1.lds_b bytes), a 48-byte slot
+// (32 zero bytes, 16 bytes of scale code 127), operand scales [blocks][16]
+// (p1.lds_s bytes), output scales [ell][rows_pad] halfs, column blocks
+// [n_slots].
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParams p2,
+                                                        FusedArgs fx) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* bl = smem;
+  uint8_t* zslot = smem + p1.lds_b;
+  uint8_t* bs = zslot + 48;
+  half_t* srows = (half_t*)(bs + p1.lds_s);
+  ColBlock* cbs = (ColBlock*)(srows + (int64_t)p1.ell * fx.rows_pad);
+  if (threadIdx.x < 2) *(v4u*)(zslot + 16 * threadIdx.x) = v4u{0u, 0u, 0u, 0u};
+  if (threadIdx.x == 2) *(v4u*)(zslot + 32) = v4u{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int c = j / kParts, part = j - kParts * (j / kParts);
+  const int lane16 = lane * 16;
+  const int ell = p1.ell;
+  const int nkb1 = (int)p1.nkb, nkb2 = (int)p2.nkb;
+  const int nkp1 = (nkb1 + D - 1) / D * D, nkp2 = (nkb2 + D - 1) / D * D;
+  const int nqw1 = wv < p1.nq ? (int)((p1.nq - 1 - wv) / NW + 1) : 0;
+  const int nqw2 = wv < p2.nq ? (int)((p2.nq - 1 - wv) / NW + 1) : 0;
+  const int G = gridDim.x, b = blockIdx.x;
+
+  const int32_t n_cb = segment_runs<NW>(
+      fx.ids, (int32_t)p1.T, fx.num_adapters, fx.chunk,
+      [&](int32_t idx, int32_t t, int32_t id) {
+        if (idx % G == b) {
+          cbs[idx / G].t0 = t;
+          cbs[idx / G].adapter = id;
+        }
+      },
+      [&](int32_t idx, int32_t t1) {
+        if (idx % G == b) cbs[idx / G].t1 = t1;
+      });
+  __syncthreads();  // the slots were written by the block-start threads
+
+  int slot = 0;
+  for (int32_t cb = b; cb < n_cb; cb += G, ++slot) {
+    const ColBlock cbk = cbs[slot];
+    const int64_t t0 = cbk.t0, t1 = cbk.t1;
+    const int32_t ad = cbk.adapter;
+    if (ad < 0) {  // out-of-range ids: y = 0 (or unchanged)
+      if (!p2.accumulate) {
+        const int64_t nr = p2.rows;
+        for (int64_t e = threadIdx.x; e < (t1 - t0) * nr; e += blockDim.x) {
+          const int64_t t = t0 + e / nr, r = e % nr;
+          if (p2.y_f32)
+            ((float*)p2.y)[t * p2.ldy + r] = 0.0f;
+          else
+            ((half_t*)p2.y)[t * p2.ldy + r] = (half_t)0.0f;
+        }
+      }
+      continue;
+    }
+    const uint32_t* B1 = p1.B1s[ad];
+    const uint32_t* B2 = p1.B2s[ad];
+    const half_t* alpha = p1.alphas[ad];
+    const half_t* beta = p1.betas[ad];
+    const half_t* gamma = fx.gammas[ad];
+    const int ntok = (int)(t1 - t0);
+    const int ncols = kParts * ell * ntok;
+    const bool colv = j < ncols;
+    const int ci = colv ? c / ntok : 0, ct = colv ? c - ntok * (c / ntok) : 0;
+    const char* S1 = (const char*)B2 + ((int64_t)wv * nkb1 << 10);
+    const char* S2 = (const char*)B1 + ((int64_t)wv * nkb2 << 10);
+
+    // ---- stage 1: the first D sign loads go out before the operands
+    v4u ring[D];
+    if (nqw1 > 0) {
+#pragma unroll
+      for (int u = 0; u < D; ++u)
+        ring[u] = *(gv4up)(S1 + ((int64_t)(u < nkb1 ? u : nkb1 - 1) << 10) + lane16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // the previous column block's LDS readers are done
+    {
+      // v_i = gamma_i * x (exact in fp32) in fp8 parts; wave tasks (term,
+      // token, block), the loads of four tasks requested together
+      const int ntask = ell * ntok * nkb1;
+      const int M = (int)p1.K;
+      for (int task0 = wv; task0 < ntask; task0 += 4 * NW) {
+        float v0[4], v1[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int task = task0 + q * NW;
+          v0[q] = v1[q] = 0.0f;
+          if (task < ntask) {
+            const int kb = task % nkb1, cc = task / nkb1;  // cc = term * ntok + token
+            const int i = cc / ntok, tt = cc - i * ntok;
+            const int k = kb * kColBlock + 2 * lane;
+            const half_t* xr = fx.x + (t0 + tt) * fx.ldx;
+            const half_t* gi = gamma + (int64_t)i * M;
+            if (k < M) v0[q] = (float)gi[k] * (float)xr[k];
+            if (k + 1 < M) v1[q] = (float)gi[k + 1] * (float)xr[k + 1];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int task = task0 + q * NW;
+          if (task < ntask)
+            parts_to_lds(v0[q], v1[q], bl, bs, task % nkb1, (task / nkb1) * kParts, ncols, lane);
+        }
+      }
+      pad_blocks(bl, bs, nkb1, nkp1, ncols);
+      for (int e = threadIdx.x; e < ell * fx.rows_pad; e += blockDim.x) {
+        const int i = e / fx.rows_pad, r = e - i * fx.rows_pad;
+        srows[e] = r < p1.rows ? beta[(int64_t)i * p1.rows + r] : (half_t)0.0f;
+      }
+    }
+    __syncthreads();
+    fused_stream<1, D, NW>(p1, S1, nqw1, wv, lane, ring, nqw2 > 0 ? S2 : nullptr, nkb2, bl, bs,
+                           zslot, srows + ci * fx.rows_pad, ncols, colv, j, g, part, ci, ct, ntok,
+                           t0);
+
+    // ---- z of this column block is complete (and visible to the
+    // workgroup) once every wave is past this barrier
+    __syncthreads();
+    if (nqw1 == 0 && nqw2 > 0) {
+#pragma unroll
+      for (int u = 0; u < D; ++u)
+        ring[u] = *(gv4up)(S2 + ((int64_t)(u < nkb2 ? u : nkb2 - 1) << 10) + lane16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      // stage-2 operands from z, wave tasks (term, token, block)
+      const int ntask = ell * ntok * nkb2;
+      const int R = (int)p1.rows;
+      for (int task0 = wv; task0 < ntask; task0 += 4 * NW) {
+        float v0[4], v1[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int task = task0 + q * NW;
+          v0[q] = v1[q] = 0.0f;
+          if (task < ntask) {
+            const int kb = task % nkb2, cc = task / nkb2;
+            const int i = cc / ntok, tt = cc - i * ntok;
+            const float* zr = p1.z + i * p1.zstride + (t0 + tt) * p1.ldz;
+            const int k = kb * kColBlock + 2 * lane;
+            if (k < R) v0[q] = zr[k];
+            if (k + 1 < R) v1[q] = zr[k + 1];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int task = task0 + q * NW;
+          if (task < ntask)
+            parts_to_lds(v0[q], v1[q], bl, bs, task % nkb2, (task / nkb2) * kParts, ncols, lane);
+        }
+      }
+      pad_blocks(bl, bs, nkb2, nkp2, ncols);
+      for (int e = threadIdx.x; e < ell * fx.rows_pad; e += blockDim.x) {
+        const int i = e / fx.rows_pad, r = e - i * fx.rows_pad;
+        srows[e] = r < p2.rows ? alpha[(int64_t)i * p2.rows + r] : (half_t)0.0f;
+      }
+    }
+    __syncthreads();
+    fused_stream<2, D, NW>(p2, S2, nqw2, wv, lane, ring, nullptr, 0, bl, bs, zslot,
+                           srows + ci * fx.rows_pad, ncols, colv, j, g, part, ci, ct, ntok, t0);
+  }
+}
+
 // -------------------------------------------------------------- launch ----
 
 template <int STAGE, int RTG, int KC>
@@ -641,7 +972,12 @@ static hipError_t launch_gemv_stage(const GemvParams& p, int64_t grid, hipStream
 // waves would otherwise idle), RTG row tiles per item with RTG*KC <= 64 sign
 // words per lane in flight; fewer row tiles per item when there are too few
 // items to fill the GPU.
-constexpr int kStreamQPW = 2;
+constexpr int kFusedD = 8;                    // fused kernel: sign loads in flight per lane
+constexpr int kFusedNW = 12;                  // fused kernel: waves per workgroup
+constexpr int64_t kFusedMinColBlocks = 256;   // one per compute unit
+constexpr int64_t kFusedLdsMax = 80 * 1024;   // LDS budget per workgroup
+constexpr int kStreamQPW = 2;  // row quads per wave and item
+constexpr int kStreamD = 8;    // sign loads in flight per lane
 constexpr int64_t kStreamLdsB = 32 * 1024;  // LDS budget for staged B operands
 
 template <int STAGE>
@@ -658,7 +994,7 @@ static hipError_t launch_gemv_stage_any(GemvParams p, int64_t n_cb_est, int64_t 
                        (size_t)p.ell * 4 * kStreamQPW * kQuad * kRowTile * sizeof(half_t);
     int64_t grid = n_cb_max * p.n_qg;
     if (grid > 2048) grid = 2048;
-    hipLaunchKernelGGL((k_gemv_stream<STAGE, kStreamQPW>), dim3((unsigned)grid), dim3(256), lds, s,
+    hipLaunchKernelGGL((k_gemv_stream<STAGE, kStreamQPW, kStreamD>), dim3((unsigned)grid), dim3(256), lds, s,
                        p);
     return hipGetLastError();
   }
@@ -679,7 +1015,9 @@ static hipError_t launch_gemv_stage_any(GemvParams p, int64_t n_cb_est, int64_t 
 
 static hipError_t launch_prep(PrepParams p, hipStream_t s) {
   const int64_t nblk = (int64_t)p.ell * p.T * p.nkb;
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)cdiv(nblk, 4)), dim3(256), 0, s, p);
+  p.seg_block = cdiv(nblk, 4);
+  const int64_t grid = p.seg_block + (p.seg_cbl != nullptr ? 1 : 0);
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -690,10 +1028,6 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
   hipError_t e;
   int64_t n_cb_max, n_cb_est;
   if (a.multi) {
-    if (a.phases & 1) {
-      e = launch_segment(a, tcb, s);
-      if (e != hipSuccess) return e;
-    }
     n_cb_max = a.T + cdiv(a.T, tcb);
     if (n_cb_max > max_colblocks(a.T)) n_cb_max = max_colblocks(a.T);
     n_cb_est = (int64_t)a.num_adapters + cdiv(a.T, tcb);
@@ -741,20 +1075,66 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
   gp.alphas = a.alphas;
   gp.betas = a.betas;
 
+  GemvParams g1 = gp;
+  g1.rows = a.R;
+  g1.K = a.M;
+  g1.nrt = cdiv(a.R, kRowTile);
+  g1.nkb = cdiv(a.M, kColBlock);
+  GemvParams g2 = gp;
+  g2.rows = a.N;
+  g2.K = a.R;
+  g2.nrt = cdiv(a.N, kRowTile);
+  g2.nkb = cdiv(a.R, kColBlock);
+
+  // many column blocks and every phase in this call: one fused launch when
+  // a column block's operands and output scales fit in LDS
+  if (a.multi && a.phases == 7 && n_cb_est >= kFusedMinColBlocks) {
+    const int64_t nkp = cdiv(g1.nkb > g2.nkb ? g1.nkb : g2.nkb, kFusedD) * kFusedD;
+    const int64_t rows_pad = cdiv(a.R > a.N ? a.R : a.N, 64) * 64;
+    // one workgroup per compute unit: extra workgroups (the host only
+    // bounds the count) would wait for a free unit and end the launch late
+    const int64_t grid = n_cb_max < kFusedMinColBlocks ? n_cb_max : kFusedMinColBlocks;
+    const int64_t n_slots = cdiv(max_colblocks(a.T), grid);
+    const int64_t lds_b = (int64_t)kParts * a.ell * tcb * nkp * 128;
+    const int64_t lds_s = 16 * nkp;
+    const int64_t lds = lds_b + 48 + lds_s + (int64_t)a.ell * rows_pad * (int64_t)sizeof(half_t) +
+                        n_slots * (int64_t)sizeof(ColBlock);
+    if (lds <= kFusedLdsMax) {
+      g1.nq = cdiv(g1.nrt, kQuad);
+      g2.nq = cdiv(g2.nrt, kQuad);
+      g1.lds_b = g2.lds_b = lds_b;
+      g1.lds_s = g2.lds_s = lds_s;
+      FusedArgs fx{};
+      fx.rows_pad = (int32_t)rows_pad;
+      fx.n_slots = (int32_t)n_slots;
+      fx.chunk = tcb;
+      fx.num_adapters = a.num_adapters;
+      fx.ids = a.ids;
+      fx.x = a.x;
+      fx.ldx = a.ldx;
+      fx.gammas = a.gammas;
+      hipLaunchKernelGGL((k_gemv_fused<kFusedD, kFusedNW>), dim3((unsigned)grid),
+                         dim3(64 * kFusedNW), (size_t)lds, s, g1, g2, fx);
+      return hipGetLastError();
+    }
+  }
+
   // stage 1: z = beta * (S2 . (gamma * x))
   pp.K = a.M;
   pp.nkb = cdiv(a.M, kColBlock);
   pp.from_z = 0;
   pp.opnd = (uint32_t*)(ws + L.p1o);
   pp.oscl = (uint8_t*)(ws + L.p1s);
+  if (a.multi) {  // the first prep launch also builds the column blocks
+    pp.seg_cbl = (ColBlock*)(ws + L.cbl);
+    pp.seg_hdr = (WsHeader*)ws;
+    pp.seg_chunk = tcb;
+  }
   if ((a.phases & 1) && (e = launch_prep(pp, s)) != hipSuccess) return e;
-  GemvParams g1 = gp;
-  g1.rows = a.R;
-  g1.K = a.M;
-  g1.nrt = cdiv(a.R, kRowTile);
-  g1.nkb = pp.nkb;
+  pp.seg_cbl = nullptr;
   g1.opnd = pp.opnd;
   g1.oscl = pp.oscl;
+
   if ((a.phases & 2) && (e = launch_gemv_stage_any<1>(g1, n_cb_est, n_cb_max, a.multi, s)) != hipSuccess)
     return e;
   if (!(a.phases & 4)) return hipSuccess;
@@ -766,11 +1146,6 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
   pp.opnd = (uint32_t*)(ws + L.p2o);
   pp.oscl = (uint8_t*)(ws + L.p2s);
   if ((e = launch_prep(pp, s)) != hipSuccess) return e;
-  GemvParams g2 = gp;
-  g2.rows = a.N;
-  g2.K = a.R;
-  g2.nrt = cdiv(a.N, kRowTile);
-  g2.nkb = pp.nkb;
   g2.opnd = pp.opnd;
   g2.oscl = pp.oscl;
   return launch_gemv_stage_any<2>(g2, n_cb_est, n_cb_max, a.multi, s);

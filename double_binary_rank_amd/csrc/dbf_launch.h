@@ -99,7 +99,6 @@ Path choose_path(int64_t T, int64_t tokens_per_segment_estimate);
 // x tokens must fit the 16 columns of one MFMA); 0 if ell is too large.
 inline int gemv_tokens_per_block(int32_t ell) { return ell <= 5 ? 16 / (kParts * ell) : 0; }
 hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s);
-hipError_t launch_segment(const ForwardArgs& a, int chunk, hipStream_t s);
 // large-T path: fp16 matrix-core contractions; with several adapters the
 // column blocks hold at most kGemmChunk tokens of one adapter
 constexpr int kGemmChunk = 32;

@@ -289,6 +289,104 @@ def test_multi_adapter_stream_path(integer):
         assert err <= TOL, err
 
 
+def _fused_case(ell, integer, T=400, A=300, seed=61, max_run=7):
+    kind = dict(alpha="ones", beta="ones", gamma="ones", x_kind="int3") if integer else {}
+    B = synth.make_multi_adapter(num_adapters=A, N=200, R=136, M=264, ell=ell, T=T, seed=seed,
+                                 **kind)
+    rng = np.random.default_rng(seed + 1)
+    runs = np.repeat(rng.integers(-2, A + 2, T), rng.integers(1, max_run + 1, T))[:T]
+    return B, runs.astype(np.int32)
+
+
+@pytest.mark.parametrize("ell,integer,T,max_run", [(1, False, 400, 7), (2, False, 400, 7),
+                                                   (1, True, 400, 7), (2, True, 400, 7),
+                                                   (1, True, 700, 2)])
+def test_multi_adapter_fused_decode(ell, integer, T, max_run):
+    """Many adapters (an estimate of at least 256 column blocks of <= 16/(3*ell)
+    tokens): one fused launch segments the ids and runs both stages per
+    column block.  Unsorted runs of 1..max_run tokens, out-of-range ids, 3
+    stage-1 row quads for 12 waves (most waves stream only stage 2), ragged
+    last quads, a 3-block reduction padded to the ring depth, and (T=700,
+    runs of 1..2) more column blocks than workgroups.  Checked against the
+    oracle, and against the same call split into phases (which takes the
+    multi-launch path)."""
+    B, ids = _fused_case(ell, integer, T=T, max_run=max_run)
+    D = H().DeviceAdapters(B.adapters)
+    x, idd = H().to_dev(B.x), H().to_dev(ids)
+    T = len(ids)
+    y = D.forward(x, idd, path="gemv", y_dtype=torch.float32)
+    ws = torch.empty(dbf_ws(200, 136, 264, ell, T), dtype=torch.uint8, device="cuda")
+    ys = torch.empty((T, 200), dtype=torch.float32, device="cuda")
+    D.forward(x, idd, path="gemv", y=ys, ws=ws, phases=["prep", "stage1"])
+    D.forward(x, idd, path="gemv", y=ys, ws=ws, phases="stage2")
+    torch.cuda.synchronize()
+    want = _multi_ref(B, ids)
+    got, split = y.cpu().numpy().astype(np.float64), ys.cpu().numpy().astype(np.float64)
+    if integer:
+        assert np.array_equal(got, want.astype(np.float32).astype(np.float64))
+        assert np.array_equal(split, got)
+    else:
+        err = oracle.max_norm_error(got, want)
+        assert err <= TOL, err
+        assert oracle.max_norm_error(split, want) <= TOL
+
+
+def test_multi_adapter_fused_accumulate_fp16():
+    """Fused decode with ACCUMULATE into an fp16 output: rows of out-of-range
+    ids keep their old values, the others add the product."""
+    B, ids = _fused_case(1, True, seed=71)
+    D = H().DeviceAdapters(B.adapters)
+    T = len(ids)
+    base = np.random.default_rng(72).integers(-4, 5, (T, 200)).astype(np.float16)
+    y = H().to_dev(base)
+    D.forward(H().to_dev(B.x), H().to_dev(ids), path="gemv", y=y, accumulate=True)
+    torch.cuda.synchronize()
+    want = _multi_ref(B, ids, y_old=base.astype(np.float64))
+    assert np.array_equal(y.cpu().numpy().astype(np.float64),
+                          want.astype(np.float16).astype(np.float64))
+
+
+def _ref_blocks(ids, n_adapters, chunk):
+    """Column blocks by definition: maximal runs of equal normalised id (ids
+    outside [0, n_adapters) count as -1), each cut every `chunk` tokens."""
+    norm = [int(i) if 0 <= i < n_adapters else -1 for i in ids]
+    out, t, T = [], 0, len(norm)
+    while t < T:
+        u = t
+        while u < T and norm[u] == norm[t]:
+            u += 1
+        out += [(s, min(s + chunk, u), norm[t]) for s in range(t, u, chunk)]
+        t = u
+    return out
+
+
+@pytest.mark.parametrize("path,ell,chunk", [("gemv", 1, 5), ("gemv", 2, 2), ("mfma", 2, 32)])
+def test_segmentation_blocks(path, ell, chunk):
+    """The column-block list the prep launch writes into the workspace (its
+    header and list sit at the library's internal offsets 0 and 256) equals
+    the list by definition: runs of 1..70 tokens over several 256-id passes,
+    equal neighbouring runs that merge, and out-of-range ids."""
+    rng = np.random.default_rng(91)
+    A, parts = 7, []
+    while sum(len(p) for p in parts) < 1000:
+        parts.append(np.full(int(rng.integers(1, 71)), int(rng.integers(-3, A + 3)), np.int32))
+    ids = np.concatenate(parts)[:1000]
+    ids[300:340] = 4  # a run across the first pass boundary
+    ids[511:513] = -1
+    B = synth.make_multi_adapter(num_adapters=A, N=64, R=32, M=128, ell=ell, T=len(ids), seed=92)
+    D = H().DeviceAdapters(B.adapters)
+    T = len(ids)
+    ws = torch.full((dbf_ws(64, 32, 128, ell, T),), 0xAB, dtype=torch.uint8, device="cuda")
+    D.forward(H().to_dev(B.x), H().to_dev(ids), path=path, ws=ws, phases="prep")
+    torch.cuda.synchronize()
+    want = _ref_blocks(ids, A, chunk)
+    n = int(ws[:4].view(torch.int32).item())
+    assert n == len(want)
+    got = ws[256:256 + 16 * n].view(torch.int32).reshape(n, 4).cpu().numpy()
+    assert [tuple(int(v) for v in r[:3]) for r in got] == want
+    assert not got[:, 3].any()
+
+
 # ------------------------------------------------------- split phases --
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("shape", [(300, 130, 260, 1, 37), (64, 16, 8, 3, 70)])
