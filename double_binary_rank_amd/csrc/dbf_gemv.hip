@@ -677,6 +677,73 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
 
 // ------------------------------------------------------- fused decode ----
 
+// Epilogue of one tile in the fused kernel; the arithmetic of gemv_epilogue
+// with per-lane row pointers prepared once per column block.  `sum` is this
+// lane's MFMA tile (rows r0..r0+3 of column j, r0 = tile*16 + 4g); the parts
+// of a column sit in lanes j, j+1, j+2 of one row of 16.  p0: this lane holds
+// part 0 of a live column; st: it stores (stage 1: p0; stage 2: p0 and term
+// 0).  Stage 1 writes z = beta * u through zrow (fp32, in LDS, rows past the
+// last are written too: their scale is zero); stage 2 sums
+// alpha_i * w_i over the terms and writes (or accumulates) y through yrow.
+// srow: LDS output scales of this lane's term, zero past the rows.  Every
+// lane of the wave must call it (it shuffles).
+template <int STAGE>
+__device__ inline void fused_epilogue(const GemvParams& p, v4f sum, const half_t* srow, int r0,
+                                      float* zrow, char* yrow, bool p0, bool st, int g, int lane,
+                                      int ntok, int ct) {
+  typedef const __attribute__((address_space(3))) v4h* lds_v4hp;
+  float tot[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) tot[v] = (sum[v] + row_next<1>(sum[v])) + row_next<2>(sum[v]);
+  const v4h s4 = *(lds_v4hp)(srow + r0);
+  const int rows = (int)p.rows;
+  if (STAGE == 1) {
+    typedef __attribute__((address_space(3))) v4f* lds_v4fp;
+    if (st)
+      *(lds_v4fp)(zrow + r0) = v4f{tot[0] * (float)s4[0], tot[1] * (float)s4[1],
+                                   tot[2] * (float)s4[2], tot[3] * (float)s4[3]};
+  } else {
+    float val[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) val[v] = p0 ? tot[v] * (float)s4[v] : 0.0f;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    if (p.ell == 1) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[v] += val[v];
+    } else {
+      for (int ii = 0; ii < p.ell; ++ii) {
+        int src = 16 * g + kParts * (ii * ntok + ct);
+        src = src < 64 ? src : lane;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] += __shfl(val[v], src);
+      }
+    }
+    if (st) {
+      if (p.y_f32) {
+        float* yr = (float*)yrow + r0;
+        if (p.accumulate)
+          for (int e = 0; e < 4; ++e) o[e] += r0 + e < rows ? yr[e] : 0.0f;
+        if (r0 + 4 <= rows) {
+          *(v4f*)yr = v4f{o[0], o[1], o[2], o[3]};
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (r0 + e < rows) yr[e] = o[e];
+        }
+      } else {
+        half_t* yr = (half_t*)yrow + r0;
+        if (p.accumulate)
+          for (int e = 0; e < 4; ++e) o[e] += r0 + e < rows ? (float)yr[e] : 0.0f;
+        if (r0 + 4 <= rows) {
+          *(v4h*)yr = v4h{(half_t)o[0], (half_t)o[1], (half_t)o[2], (half_t)o[3]};
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (r0 + e < rows) yr[e] = (half_t)o[e];
+        }
+      }
+    }
+  }
+}
+
 // Streams one stage of a fused column block: wave wv of NW owns row quads
 // wv, wv+NW, ... (nqw of them) of the stage's sign matrix (S: the wave's first
 // quad); each quad's four tiles are finished by the epilogue right after its
@@ -685,14 +752,14 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
 // fetches the first blocks of `tail` (the wave's first quad of the next
 // stage, tail_nk blocks long), or re-reads the last block when tail is null.
 // B operands and their scales come from LDS (bl, bs: blocks padded to a
-// multiple of D with zero operands); srow points at the LDS output scales of
-// this lane's term.
+// multiple of D with zero operands); the epilogue arguments are those of
+// fused_epilogue.
 template <int STAGE, int D, int NW>
 __device__ inline void fused_stream(const GemvParams& p, const char* S, int nqw, int wv, int lane,
                                     v4u (&ring)[D], const char* tail, int tail_nk,
                                     const uint8_t* bl, const uint8_t* bs, const uint8_t* zslot,
                                     const half_t* srow, int ncols, bool colv, int j, int g,
-                                    int part, int ci, int ct, int ntok, int64_t t0) {
+                                    float* zrow, char* yrow, bool p0, bool st, int ntok, int ct) {
   const int lane16 = lane * 16;
   const int nk = (int)p.nkb, nkp = (nk + D - 1) / D * D;
   const int64_t qstride = (int64_t)NW * nk << 10;
@@ -739,12 +806,13 @@ __device__ inline void fused_stream(const GemvParams& p, const char* S, int nqw,
         acc[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a3, bop, acc[3], 4, 0, 0, 127, 0, bsc);
       }
     }
-    const int64_t q = wv + NW * (int64_t)qi;
+    const int q = wv + NW * qi;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const int64_t tile = q * kQuad + h;
+      const int tile = q * kQuad + h;
       if (tile < p.nrt)
-        gemv_epilogue<STAGE, true>(p, srow, acc[h], tile, lane, g, part, colv, ci, ct, ntok, t0);
+        fused_epilogue<STAGE>(p, acc[h], srow, tile * kRowTile + 4 * g, zrow, yrow, p0, st, g,
+                              lane, ntok, ct);
     }
   }
 }
@@ -752,6 +820,7 @@ __device__ inline void fused_stream(const GemvParams& p, const char* S, int nqw,
 // Inputs of the fused kernel besides the two stages' parameters.
 struct FusedArgs {
   int32_t rows_pad;  // output-scale rows staged per term: max(R, N) rounded up to 64
+  int32_t rz;        // z entries kept per (term, token): R rounded up to 128
   int32_t n_slots;   // column blocks one workgroup can own: ceil(max blocks / grid)
   int32_t chunk;     // tokens per column block at most
   int32_t num_adapters;
@@ -785,8 +854,8 @@ __device__ inline void pad_blocks(uint8_t* bl, uint8_t* bs, int nk, int nkp, int
 // finds the same list) and keeps the column blocks b, b + G, ... (G =
 // workgroups); for each it builds the stage-1 operands gamma_i * x in fp8
 // parts directly in LDS, streams stage 1 over every row quad of its adapter
-// (z = beta * u goes to the workspace, fp32), turns its own z into the
-// stage-2 parts in LDS, and streams stage 2.  No other launch, no other
+// (z = beta * u stays in LDS, fp32; the workspace is not used), turns its
+// z into the stage-2 parts in LDS, and streams stage 2.  No other launch, no other
 // workgroup and no per-item set-up lies between the steps, and the stage-1
 // ring ends by fetching the first stage-2 sign blocks.  The parts are those
 // of the prep kernel, so the result equals the split-phase path's.  p1/p2
@@ -796,8 +865,8 @@ __device__ inline void pad_blocks(uint8_t* bl, uint8_t* bs, int nk, int nkp, int
 // words are read once, so their loads are non-temporal.
 // LDS: B operands [blocks][column][g][32 B] (p1.lds_b bytes), a 48-byte slot
 // (32 zero bytes, 16 bytes of scale code 127), operand scales [blocks][16]
-// (p1.lds_s bytes), output scales [ell][rows_pad] halfs, column blocks
-// [n_slots].
+// (p1.lds_s bytes), output scales of stage 1 and of stage 2 [ell][rows_pad]
+// halfs each, column blocks [n_slots], z [ell * chunk][rz] fp32.
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParams p2,
                                                         FusedArgs fx) {
@@ -805,8 +874,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
   uint8_t* bl = smem;
   uint8_t* zslot = smem + p1.lds_b;
   uint8_t* bs = zslot + 48;
-  half_t* srows = (half_t*)(bs + p1.lds_s);
-  ColBlock* cbs = (ColBlock*)(srows + (int64_t)p1.ell * fx.rows_pad);
+  half_t* srows = (half_t*)(bs + p1.lds_s);                // beta
+  half_t* srows2 = srows + (int64_t)p1.ell * fx.rows_pad;  // alpha
+  ColBlock* cbs = (ColBlock*)(srows2 + (int64_t)p1.ell * fx.rows_pad);
+  float* zl = (float*)(cbs + fx.n_slots);
   if (threadIdx.x < 2) *(v4u*)(zslot + 16 * threadIdx.x) = v4u{0u, 0u, 0u, 0u};
   if (threadIdx.x == 2) *(v4u*)(zslot + 32) = v4u{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
 
@@ -864,8 +935,42 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
     const int ci = colv ? c / ntok : 0, ct = colv ? c - ntok * (c / ntok) : 0;
     const char* S1 = (const char*)B2 + ((int64_t)wv * nkb1 << 10);
     const char* S2 = (const char*)B1 + ((int64_t)wv * nkb2 << 10);
+    const bool p0 = part == 0 && colv;
+    float* zrow = zl + (ci * ntok + ct) * fx.rz;
+    char* yrow = (char*)p2.y + (t0 + ct) * p2.ldy * (p2.y_f32 ? 4 : 2);
 
-    // ---- stage 1: the first D sign loads go out before the operands
+    // ---- stage 1 operands v_i = gamma_i * x (exact in fp32) in fp8 parts:
+    // wave tasks (term, token, block), four tasks' loads requested together.
+    // The first four tasks are requested before the first D sign loads, so
+    // their parts need not wait for the signs.
+    const int ntask1 = ell * ntok * nkb1;
+    const int M = (int)p1.K;
+    auto load_v = [&](int task0, float (&v0)[4], float (&v1)[4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int task = task0 + q * NW;
+        v0[q] = v1[q] = 0.0f;
+        if (task < ntask1) {
+          const int kb = task % nkb1, cc = task / nkb1;  // cc = term * ntok + token
+          const int i = cc / ntok, tt = cc - i * ntok;
+          const int k = kb * kColBlock + 2 * lane;
+          const half_t* xr = fx.x + (t0 + tt) * fx.ldx;
+          const half_t* gi = gamma + (int64_t)i * M;
+          if (k < M) v0[q] = (float)gi[k] * (float)xr[k];
+          if (k + 1 < M) v1[q] = (float)gi[k + 1] * (float)xr[k + 1];
+        }
+      }
+    };
+    auto parts_v = [&](int task0, const float (&v0)[4], const float (&v1)[4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int task = task0 + q * NW;
+        if (task < ntask1)
+          parts_to_lds(v0[q], v1[q], bl, bs, task % nkb1, (task / nkb1) * kParts, ncols, lane);
+      }
+    };
+    float v0[4], v1[4];
+    load_v(wv, v0, v1);
     v4u ring[D];
     if (nqw1 > 0) {
 #pragma unroll
@@ -874,47 +979,24 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // the previous column block's LDS readers are done
-    {
-      // v_i = gamma_i * x (exact in fp32) in fp8 parts; wave tasks (term,
-      // token, block), the loads of four tasks requested together
-      const int ntask = ell * ntok * nkb1;
-      const int M = (int)p1.K;
-      for (int task0 = wv; task0 < ntask; task0 += 4 * NW) {
-        float v0[4], v1[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int task = task0 + q * NW;
-          v0[q] = v1[q] = 0.0f;
-          if (task < ntask) {
-            const int kb = task % nkb1, cc = task / nkb1;  // cc = term * ntok + token
-            const int i = cc / ntok, tt = cc - i * ntok;
-            const int k = kb * kColBlock + 2 * lane;
-            const half_t* xr = fx.x + (t0 + tt) * fx.ldx;
-            const half_t* gi = gamma + (int64_t)i * M;
-            if (k < M) v0[q] = (float)gi[k] * (float)xr[k];
-            if (k + 1 < M) v1[q] = (float)gi[k + 1] * (float)xr[k + 1];
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int task = task0 + q * NW;
-          if (task < ntask)
-            parts_to_lds(v0[q], v1[q], bl, bs, task % nkb1, (task / nkb1) * kParts, ncols, lane);
-        }
-      }
-      pad_blocks(bl, bs, nkb1, nkp1, ncols);
-      for (int e = threadIdx.x; e < ell * fx.rows_pad; e += blockDim.x) {
-        const int i = e / fx.rows_pad, r = e - i * fx.rows_pad;
-        srows[e] = r < p1.rows ? beta[(int64_t)i * p1.rows + r] : (half_t)0.0f;
-      }
+    parts_v(wv, v0, v1);
+    for (int task0 = wv + 4 * NW; task0 < ntask1; task0 += 4 * NW) {
+      load_v(task0, v0, v1);
+      parts_v(task0, v0, v1);
+    }
+    pad_blocks(bl, bs, nkb1, nkp1, ncols);
+    for (int e = threadIdx.x; e < ell * fx.rows_pad; e += blockDim.x) {
+      const int i = e / fx.rows_pad, r = e - i * fx.rows_pad;
+      srows[e] = r < p1.rows ? beta[(int64_t)i * p1.rows + r] : (half_t)0.0f;
+      srows2[e] = r < p2.rows ? alpha[(int64_t)i * p2.rows + r] : (half_t)0.0f;
     }
     __syncthreads();
     fused_stream<1, D, NW>(p1, S1, nqw1, wv, lane, ring, nqw2 > 0 ? S2 : nullptr, nkb2, bl, bs,
-                           zslot, srows + ci * fx.rows_pad, ncols, colv, j, g, part, ci, ct, ntok,
-                           t0);
+                           zslot, srows + ci * fx.rows_pad, ncols, colv, j, g, zrow, yrow, p0, p0,
+                           ntok, ct);
 
-    // ---- z of this column block is complete (and visible to the
-    // workgroup) once every wave is past this barrier
+    // ---- z of this column block is complete once every wave is past this
+    // barrier
     __syncthreads();
     if (nqw1 == 0 && nqw2 > 0) {
 #pragma unroll
@@ -935,7 +1017,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
           if (task < ntask) {
             const int kb = task % nkb2, cc = task / nkb2;
             const int i = cc / ntok, tt = cc - i * ntok;
-            const float* zr = p1.z + i * p1.zstride + (t0 + tt) * p1.ldz;
+            const float* zr = zl + (i * ntok + tt) * fx.rz;
             const int k = kb * kColBlock + 2 * lane;
             if (k < R) v0[q] = zr[k];
             if (k + 1 < R) v1[q] = zr[k + 1];
@@ -949,14 +1031,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
         }
       }
       pad_blocks(bl, bs, nkb2, nkp2, ncols);
-      for (int e = threadIdx.x; e < ell * fx.rows_pad; e += blockDim.x) {
-        const int i = e / fx.rows_pad, r = e - i * fx.rows_pad;
-        srows[e] = r < p2.rows ? alpha[(int64_t)i * p2.rows + r] : (half_t)0.0f;
-      }
     }
     __syncthreads();
     fused_stream<2, D, NW>(p2, S2, nqw2, wv, lane, ring, nullptr, 0, bl, bs, zslot,
-                           srows + ci * fx.rows_pad, ncols, colv, j, g, part, ci, ct, ntok, t0);
+                           srows2 + ci * fx.rows_pad, ncols, colv, j, g, zrow, yrow, p0,
+                           p0 && ci == 0, ntok, ct);
   }
 }
 
@@ -975,7 +1054,7 @@ static hipError_t launch_gemv_stage(const GemvParams& p, int64_t grid, hipStream
 constexpr int kFusedD = 8;                    // fused kernel: sign loads in flight per lane
 constexpr int kFusedNW = 12;                  // fused kernel: waves per workgroup
 constexpr int64_t kFusedMinColBlocks = 256;   // one per compute unit
-constexpr int64_t kFusedLdsMax = 80 * 1024;   // LDS budget per workgroup
+constexpr int64_t kFusedLdsMax = 160 * 1024;  // LDS budget: one workgroup per compute unit
 constexpr int kStreamQPW = 2;  // row quads per wave and item
 constexpr int kStreamD = 8;    // sign loads in flight per lane
 constexpr int64_t kStreamLdsB = 32 * 1024;  // LDS budget for staged B operands
@@ -1097,8 +1176,9 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
     const int64_t n_slots = cdiv(max_colblocks(a.T), grid);
     const int64_t lds_b = (int64_t)kParts * a.ell * tcb * nkp * 128;
     const int64_t lds_s = 16 * nkp;
-    const int64_t lds = lds_b + 48 + lds_s + (int64_t)a.ell * rows_pad * (int64_t)sizeof(half_t) +
-                        n_slots * (int64_t)sizeof(ColBlock);
+    const int64_t rz = cdiv(a.R, kColBlock) * kColBlock;
+    const int64_t lds = lds_b + 48 + lds_s + 2 * (int64_t)a.ell * rows_pad * (int64_t)sizeof(half_t) +
+                        n_slots * (int64_t)sizeof(ColBlock) + (int64_t)a.ell * tcb * rz * 4;
     if (lds <= kFusedLdsMax) {
       g1.nq = cdiv(g1.nrt, kQuad);
       g2.nq = cdiv(g2.nrt, kQuad);
@@ -1106,6 +1186,7 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
       g1.lds_s = g2.lds_s = lds_s;
       FusedArgs fx{};
       fx.rows_pad = (int32_t)rows_pad;
+      fx.rz = (int32_t)rz;
       fx.n_slots = (int32_t)n_slots;
       fx.chunk = tcb;
       fx.num_adapters = a.num_adapters;
