@@ -61,7 +61,8 @@ __device__ inline int32_t norm_id(int32_t id, int32_t n) { return (id >= 0 && id
 // in passes of 64*NW ids.  Within a wave the start of a token's run and the
 // rank of a block start come from ballots; the per-wave last run start and
 // block count go through LDS (double-buffered by pass parity), so a pass has
-// two barriers.  The thread of a block start also ends the previous block.
+// two barriers; the ids of the next pass are requested at the start of a
+// pass.  The thread of a block start also ends the previous block.
 template <int NW, typename OnStart, typename OnEnd>
 __device__ inline int32_t segment_runs(const int32_t* __restrict__ ids, int32_t T,
                                        int32_t n_adapters, int32_t chunk, OnStart&& on_start,
@@ -71,11 +72,17 @@ __device__ inline int32_t segment_runs(const int32_t* __restrict__ ids, int32_t 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int32_t carry_rs = 0, carry_cnt = 0;  // equal in every thread
   int par = 0;
+  int32_t nx_cur = tid < T ? ids[tid] : -1;
+  int32_t nx_prv = (tid >= 1 && tid < T) ? ids[tid - 1] : -1;
   for (int32_t base = 0; base < T; base += 64 * NW, par ^= 1) {
     const int32_t t = base + tid;
     const bool in = t < T;
-    const int32_t id = in ? norm_id(ids[t], n_adapters) : -1;
-    const bool rstart = in && (t == 0 || norm_id(ids[t - 1], n_adapters) != id);
+    const int32_t raw = nx_cur, raw_prv = nx_prv;
+    const int32_t tn = t + 64 * NW;
+    nx_cur = tn < T ? ids[tn] : -1;
+    nx_prv = tn < T ? ids[tn - 1] : -1;
+    const int32_t id = in ? norm_id(raw, n_adapters) : -1;
+    const bool rstart = in && (t == 0 || norm_id(raw_prv, n_adapters) != id);
     const uint64_t M = __ballot(rstart);
     const int32_t wbase = base + 64 * w;
     if (lane == 0) s_last[par][w] = M ? wbase + 63 - __clzll(M) : -1;

@@ -39,7 +39,7 @@ typedef const DBF_GLOBAL v8h* gv8hp;
 
 struct GemmParams {
   int32_t rows, K, T, nq, nkb, ell;
-  int32_t n_cb_host, n_rg;  // column blocks (single adapter), row groups
+  int32_t n_cb_host, n_rg;  // column blocks (single adapter; an estimate with several), row groups
   int32_t y_f32, accumulate, multi, xcd_remap;
   uint32_t msk16, one16;  // 0x80008000, 0x3C003C00 (kept in registers)
   const half_t* opnd;     // this stage's operand tiles (v or z)
@@ -133,8 +133,8 @@ struct PrepVParams {
   const half_t* const* gammas;
   half_t* v;
   int64_t v_term;
-  // multi-adapter column blocks, built by the extra workgroup n_units / 4
-  // (none when seg_cbl is null)
+  // multi-adapter column blocks, built by the extra workgroup 0 (none when
+  // seg_cbl is null)
   ColBlock* seg_cbl;
   WsHeader* seg_hdr;
   int32_t seg_chunk;
@@ -146,12 +146,12 @@ struct PrepVParams {
 // past T and tokens whose adapter id is out of range are zero.  One fp16
 // rounding of the exact product.
 __global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
-  if (p.seg_cbl != nullptr && (int64_t)blockIdx.x == cdiv(p.n_units, 4)) {
+  if (p.seg_cbl != nullptr && blockIdx.x == 0) {
     segment_ids(p.ids, p.T, p.num_adapters, p.seg_chunk, p.seg_cbl, p.seg_hdr);
     return;
   }
   const int lane = threadIdx.x & 63;
-  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t u = ((int64_t)blockIdx.x - (p.seg_cbl != nullptr ? 1 : 0)) * 4 + (threadIdx.x >> 6);
   if (u >= p.n_units) return;  // uniform per wave
   const int kb = (int)(u % p.nkb);
   const int64_t r = u / p.nkb;
@@ -375,7 +375,9 @@ hipError_t launch_one(GemmParams p, hipStream_t s) {
   const int64_t items = (int64_t)p.n_cb_host * p.n_rg;
   int64_t grid = items;
   if (p.multi && grid > 8192) grid = 8192;
-  p.xcd_remap = (grid == items && items % 8 == 0) ? 1 : 0;
+  // with several adapters the item count is known only on the device, so
+  // consecutive items cannot be mapped to one XCD
+  p.xcd_remap = (!p.multi && grid == items && items % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -407,7 +409,9 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   if (a.multi) {
     // column blocks of at most kGemmChunk tokens of one adapter (built by
     // the prep launch)
-    int64_t n_cb = a.T + cdiv(a.T, kGemmChunk);
+    // the grid follows an estimate (one partial block per adapter plus
+    // full blocks); workgroups loop over any further blocks
+    int64_t n_cb = (int64_t)a.num_adapters + cdiv(a.T, kGemmChunk);
     if (n_cb > max_colblocks(a.T)) n_cb = max_colblocks(a.T);
     p.n_cb_host = (int32_t)n_cb;
   }

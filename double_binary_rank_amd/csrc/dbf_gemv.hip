@@ -64,12 +64,11 @@ struct PrepParams {
   const half_t* const* gammas;
   uint32_t* opnd;  // [ell][T][nkb][kParts][4] x 8 words
   uint8_t* oscl;   // [ell][T][nkb][kParts][4]
-  // multi-adapter column blocks, built by the extra workgroup seg_block
-  // (none when seg_cbl is null)
+  // multi-adapter column blocks, built by the extra workgroup 0 (none when
+  // seg_cbl is null)
   ColBlock* seg_cbl;
   WsHeader* seg_hdr;
   int32_t seg_chunk;
-  int64_t seg_block;
 };
 
 // K order of an fp8 operand of v_mfma_scale_f32_16x16x128_f8f6f4 inside a
@@ -134,12 +133,12 @@ __device__ inline void block_parts(float v0, float v1, Put&& put) {
 
 // One wave per (term, token, 128-block); lane l owns entries 2l and 2l+1.
 __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
-  if (p.seg_cbl != nullptr && (int64_t)blockIdx.x == p.seg_block) {
+  if (p.seg_cbl != nullptr && blockIdx.x == 0) {
     segment_ids(p.ids, (int32_t)p.T, p.num_adapters, p.seg_chunk, p.seg_cbl, p.seg_hdr);
     return;
   }
   const int lane = threadIdx.x & 63;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t blk = ((int64_t)blockIdx.x - (p.seg_cbl != nullptr ? 1 : 0)) * 4 + (threadIdx.x >> 6);
   const int64_t nblk = (int64_t)p.ell * p.T * p.nkb;
   if (blk >= nblk) return;  // uniform per wave
   const int64_t kb = blk % p.nkb;
@@ -744,34 +743,40 @@ __device__ inline void fused_epilogue(const GemvParams& p, v4f sum, const half_t
   }
 }
 
-// Streams one stage of a fused column block: wave wv of NW owns row quads
-// wv, wv+NW, ... (nqw of them) of the stage's sign matrix (S: the wave's first
-// quad); each quad's four tiles are finished by the epilogue right after its
-// last block, while the ring's loads for the next quad are in flight.  The
-// ring of D sign loads per lane runs on across quads; after the last quad it
-// fetches the first blocks of `tail` (the wave's first quad of the next
-// stage, tail_nk blocks long), or re-reads the last block when tail is null.
+// Streams one stage of a fused column block.  Wave wv starts with row quad
+// wv of the stage's sign matrix S and takes each further quad from the
+// workgroup's LDS counter *qcnt (which starts at NW) at the start of the
+// current one, so the waves a SIMD serves last simply take fewer quads and
+// all finish together.  Each quad's four tiles are finished by the epilogue
+// right after its last block, while the ring's loads for the next quad are
+// in flight.  The ring of D sign loads per lane runs on across quads; after
+// the last quad it fetches the first blocks of `tail` (the wave's first quad
+// of the next stage, tail_nk blocks long), or re-reads the last block when
+// tail is null.
 // B operands and their scales come from LDS (bl, bs: blocks padded to a
 // multiple of D with zero operands); the epilogue arguments are those of
 // fused_epilogue.
 template <int STAGE, int D, int NW>
-__device__ inline void fused_stream(const GemvParams& p, const char* S, int nqw, int wv, int lane,
+__device__ inline void fused_stream(const GemvParams& p, const char* S, int* qcnt, int wv, int lane,
                                     v4u (&ring)[D], const char* tail, int tail_nk,
                                     const uint8_t* bl, const uint8_t* bs, const uint8_t* zslot,
                                     const half_t* srow, int ncols, bool colv, int j, int g,
                                     float* zrow, char* yrow, bool p0, bool st, int ntok, int ct) {
   const int lane16 = lane * 16;
   const int nk = (int)p.nkb, nkp = (nk + D - 1) / D * D;
-  const int64_t qstride = (int64_t)NW * nk << 10;
+  const int nq = (int)p.nq;
   // lanes of live columns read [kb][j][g]; the others read the zero slot
   const uint8_t* bbase = colv ? bl + (j * 4 + g) * 32 : zslot;
   const int bstride = colv ? ncols * 128 : 0;
   const uint8_t* sbase = colv ? bs + j : zslot + 32;
   const int sstride = colv ? 16 : 0;
-  for (int qi = 0; qi < nqw; ++qi) {
-    const char* cur = S + qi * qstride;
-    const bool lastq = qi + 1 == nqw;
-    const char* nxt = lastq ? tail : cur + qstride;
+  for (int q = wv; q < nq;) {
+    int qn = 0;
+    if (lane == 0) qn = atomicAdd(qcnt, 1);
+    qn = __builtin_amdgcn_readfirstlane(qn);
+    const char* cur = S + ((int64_t)q * nk << 10);
+    const bool lastq = qn >= nq;
+    const char* nxt = lastq ? tail : S + ((int64_t)qn * nk << 10);
     const int nxt_nk = lastq ? tail_nk : nk;
     v4f acc[4];
 #pragma unroll
@@ -806,7 +811,6 @@ __device__ inline void fused_stream(const GemvParams& p, const char* S, int nqw,
         acc[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a3, bop, acc[3], 4, 0, 0, 127, 0, bsc);
       }
     }
-    const int q = wv + NW * qi;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const int tile = q * kQuad + h;
@@ -814,6 +818,7 @@ __device__ inline void fused_stream(const GemvParams& p, const char* S, int nqw,
         fused_epilogue<STAGE>(p, acc[h], srow, tile * kRowTile + 4 * g, zrow, yrow, p0, st, g,
                               lane, ntok, ct);
     }
+    q = qn;
   }
 }
 
@@ -878,6 +883,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
   half_t* srows2 = srows + (int64_t)p1.ell * fx.rows_pad;  // alpha
   ColBlock* cbs = (ColBlock*)(srows2 + (int64_t)p1.ell * fx.rows_pad);
   float* zl = (float*)(cbs + fx.n_slots);
+  __shared__ int qcnt[2];  // next row quad to take, per stage
   if (threadIdx.x < 2) *(v4u*)(zslot + 16 * threadIdx.x) = v4u{0u, 0u, 0u, 0u};
   if (threadIdx.x == 2) *(v4u*)(zslot + 32) = v4u{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
 
@@ -889,8 +895,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
   const int ell = p1.ell;
   const int nkb1 = (int)p1.nkb, nkb2 = (int)p2.nkb;
   const int nkp1 = (nkb1 + D - 1) / D * D, nkp2 = (nkb2 + D - 1) / D * D;
-  const int nqw1 = wv < p1.nq ? (int)((p1.nq - 1 - wv) / NW + 1) : 0;
-  const int nqw2 = wv < p2.nq ? (int)((p2.nq - 1 - wv) / NW + 1) : 0;
+  const bool has1 = wv < p1.nq, has2 = wv < p2.nq;  // a first quad in each stage
   const int G = gridDim.x, b = blockIdx.x;
 
   const int32_t n_cb = segment_runs<NW>(
@@ -933,8 +938,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
     const int ncols = kParts * ell * ntok;
     const bool colv = j < ncols;
     const int ci = colv ? c / ntok : 0, ct = colv ? c - ntok * (c / ntok) : 0;
-    const char* S1 = (const char*)B2 + ((int64_t)wv * nkb1 << 10);
-    const char* S2 = (const char*)B1 + ((int64_t)wv * nkb2 << 10);
+    const char* S1 = (const char*)B2;
+    const char* S2 = (const char*)B1;
+    const char* S1w = S1 + ((int64_t)wv * nkb1 << 10);  // this wave's first quads
+    const char* S2w = S2 + ((int64_t)wv * nkb2 << 10);
     const bool p0 = part == 0 && colv;
     float* zrow = zl + (ci * ntok + ct) * fx.rz;
     char* yrow = (char*)p2.y + (t0 + ct) * p2.ldy * (p2.y_f32 ? 4 : 2);
@@ -972,36 +979,56 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
     float v0[4], v1[4];
     load_v(wv, v0, v1);
     v4u ring[D];
-    if (nqw1 > 0) {
+    if (has1) {
 #pragma unroll
       for (int u = 0; u < D; ++u)
-        ring[u] = *(gv4up)(S1 + ((int64_t)(u < nkb1 ? u : nkb1 - 1) << 10) + lane16);
+        ring[u] = *(gv4up)(S1w + ((int64_t)(u < nkb1 ? u : nkb1 - 1) << 10) + lane16);
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // the previous column block's LDS readers are done
+    if (threadIdx.x == 0) qcnt[0] = qcnt[1] = NW;
     parts_v(wv, v0, v1);
     for (int task0 = wv + 4 * NW; task0 < ntask1; task0 += 4 * NW) {
       load_v(task0, v0, v1);
       parts_v(task0, v0, v1);
     }
     pad_blocks(bl, bs, nkb1, nkp1, ncols);
-    for (int e = threadIdx.x; e < ell * fx.rows_pad; e += blockDim.x) {
-      const int i = e / fx.rows_pad, r = e - i * fx.rows_pad;
-      srows[e] = r < p1.rows ? beta[(int64_t)i * p1.rows + r] : (half_t)0.0f;
-      srows2[e] = r < p2.rows ? alpha[(int64_t)i * p2.rows + r] : (half_t)0.0f;
+    // output scales of both stages, kSc per thread requested together (a
+    // load-then-store loop would pay one loaded round trip per element)
+    {
+      constexpr int kSc = 8;
+      const int nsc = ell * fx.rows_pad;
+      for (int e0 = threadIdx.x; e0 < nsc; e0 += kSc * (int)blockDim.x) {
+        half_t vb[kSc], va[kSc];
+#pragma unroll
+        for (int u = 0; u < kSc; ++u) {
+          const int e = e0 + u * (int)blockDim.x;
+          const int i = e / fx.rows_pad, r = e - i * fx.rows_pad;
+          vb[u] = (e < nsc && r < p1.rows) ? beta[(int64_t)i * p1.rows + r] : (half_t)0.0f;
+          va[u] = (e < nsc && r < p2.rows) ? alpha[(int64_t)i * p2.rows + r] : (half_t)0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kSc; ++u) {
+          const int e = e0 + u * (int)blockDim.x;
+          if (e < nsc) {
+            srows[e] = vb[u];
+            srows2[e] = va[u];
+          }
+        }
+      }
     }
     __syncthreads();
-    fused_stream<1, D, NW>(p1, S1, nqw1, wv, lane, ring, nqw2 > 0 ? S2 : nullptr, nkb2, bl, bs,
+    fused_stream<1, D, NW>(p1, S1, &qcnt[0], wv, lane, ring, has2 ? S2w : nullptr, nkb2, bl, bs,
                            zslot, srows + ci * fx.rows_pad, ncols, colv, j, g, zrow, yrow, p0, p0,
                            ntok, ct);
 
     // ---- z of this column block is complete once every wave is past this
     // barrier
     __syncthreads();
-    if (nqw1 == 0 && nqw2 > 0) {
+    if (!has1 && has2) {
 #pragma unroll
       for (int u = 0; u < D; ++u)
-        ring[u] = *(gv4up)(S2 + ((int64_t)(u < nkb2 ? u : nkb2 - 1) << 10) + lane16);
+        ring[u] = *(gv4up)(S2w + ((int64_t)(u < nkb2 ? u : nkb2 - 1) << 10) + lane16);
     }
     __builtin_amdgcn_sched_barrier(0);
     {
@@ -1033,7 +1060,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
       pad_blocks(bl, bs, nkb2, nkp2, ncols);
     }
     __syncthreads();
-    fused_stream<2, D, NW>(p2, S2, nqw2, wv, lane, ring, nullptr, 0, bl, bs, zslot,
+    fused_stream<2, D, NW>(p2, S2, &qcnt[1], wv, lane, ring, nullptr, 0, bl, bs, zslot,
                            srows2 + ci * fx.rows_pad, ncols, colv, j, g, zrow, yrow, p0,
                            p0 && ci == 0, ntok, ct);
   }
@@ -1094,8 +1121,7 @@ static hipError_t launch_gemv_stage_any(GemvParams p, int64_t n_cb_est, int64_t 
 
 static hipError_t launch_prep(PrepParams p, hipStream_t s) {
   const int64_t nblk = (int64_t)p.ell * p.T * p.nkb;
-  p.seg_block = cdiv(nblk, 4);
-  const int64_t grid = p.seg_block + (p.seg_cbl != nullptr ? 1 : 0);
+  const int64_t grid = cdiv(nblk, 4) + (p.seg_cbl != nullptr ? 1 : 0);
   hipLaunchKernelGGL(k_prep, dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
