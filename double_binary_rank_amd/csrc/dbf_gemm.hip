@@ -369,6 +369,183 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   }
 }
 
+// Stage 2 when every term's whole reduction fits in registers (ell *
+// ceil(R/128) <= KT = 2: short ranks).  A work item is a column block of 32
+// tokens and kKregQG row quads.  The token operands of every (term, block),
+// the sign words of the wave's quads (w, w+4, ... of the group) and the
+// item's alpha rows (into LDS) are requested together at the start, so an
+// item waits for one memory round trip.  alpha_i is folded into the expanded sign
+// operand: alpha_i[row] * (+-1) is exact in fp16 (the sign bits are XORed
+// into alpha's), so one fp32 accumulator per tile sums every term's products
+// and the epilogue only stores.
+constexpr int kKregQG = 16;              // row quads per work item
+constexpr int kKregQPW = kKregQG / 4;     // per wave
+
+template <int s>
+__device__ inline v8h expand_step_scaled(uint32_t w, uint32_t msk, uint32_t apair) {
+  const uint32_t U = w << (7 - s), V = w << (3 - s);
+  v4u o;
+  o[0] = (__builtin_amdgcn_perm(V, U, 0x040C000Cu) & msk) ^ apair;
+  o[1] = (__builtin_amdgcn_perm(V, U, 0x050C010Cu) & msk) ^ apair;
+  o[2] = (__builtin_amdgcn_perm(V, U, 0x060C020Cu) & msk) ^ apair;
+  o[3] = (__builtin_amdgcn_perm(V, U, 0x070C030Cu) & msk) ^ apair;
+  return __builtin_bit_cast(v8h, o);
+}
+
+template <int KT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_kreg(GemmParams p) {
+  constexpr int NC = 2;
+  static_assert(NC == 2, "the second token tile is optional");
+  __shared__ half_t sa[KT * kKregQG * kQuad * kRowTile];  // alpha rows of the item
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c16 = lane & 15;
+  const int n_cb = p.multi ? p.hdr->n_colblocks : p.n_cb_host;
+  const int64_t n_items = (int64_t)n_cb * p.n_rg;
+  const int nkb = p.nkb, ell = p.ell, rows = p.rows;
+
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int cb = (int)(it / p.n_rg), rg = (int)(it % p.n_rg);
+    int t0, t1, ad;
+    Factors f;
+    if (p.multi) {
+      const ColBlock cbk = p.cbl[cb];
+      t0 = cbk.t0;
+      t1 = cbk.t1;
+      ad = cbk.adapter;
+      if (ad >= 0) {
+        f.B1 = p.B1s[ad];
+        f.alpha = p.alphas[ad];
+      }
+    } else {
+      t0 = cb * 16 * NC;
+      t1 = t0 + 16 * NC < p.T ? t0 + 16 * NC : p.T;
+      ad = 0;
+      f = p.single;
+    }
+    const int qlo = rg * kKregQG, qhi = min(p.nq, qlo + kKregQG);
+    if (ad < 0) {
+      // tokens whose adapter id is out of range: y = 0 (or unchanged)
+      if (!p.accumulate) {
+        const int r_lo = qlo * kQuad * kRowTile, nr = min(rows, qhi * kQuad * kRowTile) - r_lo;
+        for (int e = threadIdx.x; e < (t1 - t0) * nr; e += blockDim.x) {
+          const int64_t t = t0 + e / nr, r = r_lo + e % nr;
+          if (p.y_f32)
+            ((float*)p.y)[t * p.ldy + r] = 0.0f;
+          else
+            ((half_t*)p.y)[t * p.ldy + r] = (half_t)0.0f;
+        }
+      }
+      continue;
+    }
+    // token operands of every (term, block): tb = term * nkb + block
+    v8h b[KT][4][NC];
+#pragma unroll
+    for (int tb = 0; tb < KT; ++tb) {
+      const int i = tb / nkb, kb = tb - i * nkb;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int t = min(t0 + 16 * c + c16, t1 - 1);
+        const half_t* orow = p.opnd + (int64_t)i * p.opnd_term +
+                             (int64_t)(t >> 4) * p.opnd_nkb * 2048 + (16 * g + (t & 15)) * 8;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          b[tb][s][c] = i < ell ? *(gv8hp)(orow + (int64_t)kb * 2048 + s * 512) : v8h{};
+      }
+    }
+    const bool two_tiles = t1 - t0 > 16;
+    // sign words of this wave's quads (q = qlo + wv + 4j; one v4u per
+    // block) requested together, and the item's alpha rows staged in LDS
+    const char* sgn = (const char*)f.B1 + lane * 16;
+    v4u w[kKregQPW][KT];
+#pragma unroll
+    for (int jq = 0; jq < kKregQPW; ++jq) {
+      const int q = qlo + wv + 4 * jq;
+#pragma unroll
+      for (int kb = 0; kb < KT; ++kb)
+        w[jq][kb] = (q < qhi && kb < nkb) ? *(gv4up)(sgn + (((int64_t)q * nkb + kb) << 10))
+                                          : v4u{0u, 0u, 0u, 0u};
+    }
+    constexpr int kRowsItem = kKregQG * kQuad * kRowTile;
+    {
+      constexpr int kPer = KT * kRowsItem / 256;
+      half_t av[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = threadIdx.x + 256 * u;
+        const int i = e / kRowsItem, r = qlo * kQuad * kRowTile + e - i * kRowsItem;
+        av[u] = (i < ell && r < rows) ? f.alpha[(int64_t)i * rows + r] : (half_t)0.0f;
+      }
+      __syncthreads();  // the previous item's readers of sa are done
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) sa[threadIdx.x + 256 * u] = av[u];
+      __syncthreads();
+    }
+#pragma unroll
+    for (int jq = 0; jq < kKregQPW; ++jq) {
+      const int q = qlo + wv + 4 * jq;
+      if (q >= qhi) break;
+      // alpha pairs of this lane's rows (tile h, row c16) for every term
+      uint32_t ap[KT][4];
+#pragma unroll
+      for (int i = 0; i < KT; ++i)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t ab = __builtin_bit_cast(
+              uint16_t, sa[i * kRowsItem + (q - qlo) * kQuad * kRowTile + h * kRowTile + c16]);
+          ap[i][h] = ab | (ab << 16);
+        }
+      v4f acc[4][NC];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[h][c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tb = 0; tb < KT; ++tb) {
+        const int i = tb / nkb, kb = tb - i * nkb;
+        // steps wholly past the rank meet zero operands, and so do the
+        // columns of a second token tile the block does not reach: both
+        // are skipped (wave-uniform tests)
+        const int kvalid = p.K - kb * kColBlock;
+        if (i < ell) {
+          auto step = [&](auto sc) {
+            constexpr int st = decltype(sc)::value;
+            if (32 * st >= kvalid) return;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const v8h a = expand_step_scaled<st>(w[jq][kb][h], p.msk16, ap[i][h]);
+              acc[h][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[tb][st][0], acc[h][0], 0, 0, 0);
+              if (two_tiles)
+                acc[h][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[tb][st][1], acc[h][1], 0, 0, 0);
+            }
+          };
+          step(std::integral_constant<int, 0>{});
+          step(std::integral_constant<int, 1>{});
+          step(std::integral_constant<int, 2>{});
+          step(std::integral_constant<int, 3>{});
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int t = t0 + 16 * c + c16;
+          const int r0 = q * kQuad * kRowTile + h * kRowTile + 4 * g;
+          if (t < t1 && r0 < rows) {
+            float o[4] = {acc[h][c][0], acc[h][c][1], acc[h][c][2], acc[h][c][3]};
+            if (p.accumulate) {
+              float old[4];
+              load4(p.y, p.ldy, p.y_f32, t, r0, rows, old);
+#pragma unroll
+              for (int v = 0; v < 4; ++v) o[v] += old[v];
+            }
+            store4(p.y, p.ldy, p.y_f32, t, r0, rows, o);
+          }
+        }
+    }
+  }
+}
+
 template <int STAGE, int NC, bool SPLITK>
 hipError_t launch_one(GemmParams p, hipStream_t s) {
   p.n_rg = SPLITK ? p.nq : (p.nq + 3) / 4;
@@ -388,6 +565,15 @@ hipError_t launch_one(GemmParams p, hipStream_t s) {
 // column blocks take 32.
 template <int STAGE>
 hipError_t launch_stage(GemmParams p, hipStream_t s) {
+  if (STAGE == 2 && (int64_t)p.ell * p.nkb <= 2) {
+    // short reduction: operands held in registers, row quads streamed
+    if (!p.multi) p.n_cb_host = (int32_t)cdiv(p.T, 32);
+    p.n_rg = (int32_t)cdiv(p.nq, kKregQG);
+    int64_t grid = (int64_t)p.n_cb_host * p.n_rg;
+    if (grid > 8192) grid = 8192;
+    hipLaunchKernelGGL((k_gemm_kreg<2>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
   const bool split = p.nkb >= 4;
   if (p.multi) {
     return split ? launch_one<STAGE, 2, true>(p, s) : launch_one<STAGE, 2, false>(p, s);

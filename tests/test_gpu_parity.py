@@ -158,6 +158,31 @@ def test_sign_flip_gauge_bitwise(path):
     assert np.array_equal(H().run_layer(L, path=path), y0)
 
 
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("shape", [(200, 100, 300, 2, 70), (136, 200, 264, 1, 40)])
+def test_signed_scales(shape, path):
+    """Negative entries in alpha, beta and gamma (the large-T path folds
+    alpha into the expanded signs of short-rank stage 2 with a sign XOR),
+    fp16 output, both paths; and the integer case bit for bit."""
+    import dataclasses
+    N, R, M, ell, T = shape
+    rng = np.random.default_rng(95)
+    L = synth.make_layer(N, R, M, ell, T, seed=94)
+
+    def flip(a):
+        return (a * np.where(rng.random(a.shape) < 0.5, -1, 1)).astype(np.float16)
+
+    L = dataclasses.replace(L, alpha=flip(L.alpha), beta=flip(L.beta), gamma=flip(L.gamma))
+    err = oracle.max_norm_error(H().run_layer(L, path=path), ref(L))
+    assert err <= TOL, err
+    Li = synth.make_layer(N, R, M, ell, T, seed=96, alpha="ones", beta="ones", gamma="ones",
+                          x_kind="int3")
+    sgn = lambda a: (a * np.where(rng.random(a.shape) < 0.5, -1, 1)).astype(np.float16)
+    Li = dataclasses.replace(Li, alpha=sgn(Li.alpha), beta=sgn(Li.beta), gamma=sgn(Li.gamma))
+    got = H().run_layer(Li, path=path, y_dtype=torch.float32)
+    assert np.array_equal(got, ref(Li).astype(np.float32).astype(np.float64))
+
+
 def test_paths_agree_on_integers():
     L = synth.make_layer(96, 200, 300, 2, 20, seed=9, alpha="ones", beta="ones", gamma="ones",
                          x_kind="int3")
