@@ -28,6 +28,8 @@
 // column j of an MFMA depends only on operand column j, so columns of tokens
 // past the block's end read a valid token's tile row and are simply not
 // stored.
+#include <climits>
+
 #include "dbf_device.h"
 #include "dbf_launch.h"
 
@@ -41,6 +43,7 @@ struct GemmParams {
   int32_t rows, K, T, nq, nkb, ell;
   int32_t n_cb_host, n_rg;  // column blocks (single adapter; an estimate with several), row groups
   int32_t y_f32, accumulate, multi, xcd_remap;
+  int32_t grid;             // workgroups launched
   uint32_t msk16, one16;  // 0x80008000, 0x3C003C00 (kept in registers)
   const half_t* opnd;     // this stage's operand tiles (v or z)
   int64_t opnd_term;      // halfs per term
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
   }
 }
 
-template <int STAGE, int NC, bool SPLITK>
+template <int STAGE, int NC, bool SPLITK, bool MULTI>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   constexpr int D = 2;  // operand buffers per wave (deeper rings measured slower)
   __shared__ v4f red[SPLITK ? 4 : 1][SPLITK ? 4 * NC : 1][64];
@@ -200,19 +203,20 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const uint32_t one = p.one16;
-  const int n_cb = p.multi ? p.hdr->n_colblocks : p.n_cb_host;
-  const int64_t n_items = (int64_t)n_cb * p.n_rg;
+  // item counts fit 32 bits (the workspace bounds T * R; the host checks)
+  const int n_cb = MULTI ? p.hdr->n_colblocks : p.n_cb_host;
+  const int n_items = n_cb * p.n_rg;
   // consecutive items share a column block; with the remap the items of one
   // XCD (workgroups b, b+8, ...) are consecutive, so they share operand
   // tiles in that XCD's L2
-  int64_t first = blockIdx.x;
-  if (p.xcd_remap) first = (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const int b = blockIdx.x;
+  const int first = p.xcd_remap ? (b & 7) * (p.grid >> 3) + (b >> 3) : b;
 
-  for (int64_t it = first; it < n_items; it += gridDim.x) {
-    const int cb = (int)(it / p.n_rg), rg = (int)(it % p.n_rg);
+  for (int it = first; it < n_items; it += p.grid) {
+    const int cb = it / p.n_rg, rg = it - cb * p.n_rg;
     int t0, t1, ad;
     Factors f;
-    if (p.multi) {
+    if (MULTI) {
       const ColBlock cbk = p.cbl[cb];
       t0 = cbk.t0;
       t1 = cbk.t1;
@@ -401,11 +405,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int n_cb = p.multi ? p.hdr->n_colblocks : p.n_cb_host;
-  const int64_t n_items = (int64_t)n_cb * p.n_rg;
+  const int n_items = n_cb * p.n_rg;  // fits 32 bits (the host checks)
   const int nkb = p.nkb, ell = p.ell, rows = p.rows;
 
-  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int cb = (int)(it / p.n_rg), rg = (int)(it % p.n_rg);
+  for (int it = blockIdx.x; it < n_items; it += p.grid) {
+    const int cb = it / p.n_rg, rg = it - cb * p.n_rg;
     int t0, t1, ad;
     Factors f;
     if (p.multi) {
@@ -550,12 +554,17 @@ template <int STAGE, int NC, bool SPLITK>
 hipError_t launch_one(GemmParams p, hipStream_t s) {
   p.n_rg = SPLITK ? p.nq : (p.nq + 3) / 4;
   const int64_t items = (int64_t)p.n_cb_host * p.n_rg;
+  if (items > INT32_MAX) return hipErrorInvalidValue;
   int64_t grid = items;
   if (p.multi && grid > 8192) grid = 8192;
   // with several adapters the item count is known only on the device, so
   // consecutive items cannot be mapped to one XCD
   p.xcd_remap = (!p.multi && grid == items && items % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  p.grid = (int32_t)grid;
+  if (p.multi)
+    hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -570,7 +579,9 @@ hipError_t launch_stage(GemmParams p, hipStream_t s) {
     if (!p.multi) p.n_cb_host = (int32_t)cdiv(p.T, 32);
     p.n_rg = (int32_t)cdiv(p.nq, kKregQG);
     int64_t grid = (int64_t)p.n_cb_host * p.n_rg;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
     if (grid > 8192) grid = 8192;
+    p.grid = (int32_t)grid;
     hipLaunchKernelGGL((k_gemm_kreg<2>), dim3((unsigned)grid), dim3(256), 0, s, p);
     return hipGetLastError();
   }
