@@ -148,24 +148,24 @@ struct PrepVParams {
 // c16 for each step s (1 KB contiguous per step).  Entries past M, tokens
 // past T and tokens whose adapter id is out of range are zero.  One fp16
 // rounding of the exact product.
+template <bool MULTI>
 __global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
-  if (p.seg_cbl != nullptr && blockIdx.x == 0) {
+  if (MULTI && p.seg_cbl != nullptr && blockIdx.x == 0) {
     segment_ids(p.ids, p.T, p.num_adapters, p.seg_chunk, p.seg_cbl, p.seg_hdr);
     return;
   }
   const int lane = threadIdx.x & 63;
-  const int64_t u = ((int64_t)blockIdx.x - (p.seg_cbl != nullptr ? 1 : 0)) * 4 + (threadIdx.x >> 6);
-  if (u >= p.n_units) return;  // uniform per wave
-  const int kb = (int)(u % p.nkb);
-  const int64_t r = u / p.nkb;
+  // unit counts fit 32 bits (the workspace bounds them; the host checks)
+  const int u = ((int)blockIdx.x - (MULTI && p.seg_cbl != nullptr ? 1 : 0)) * 4 + (threadIdx.x >> 6);
+  if (u >= (int)p.n_units) return;  // uniform per wave
+  const int r = u / p.nkb, kb = u - r * p.nkb;
   const int ntt = (p.T + 15) >> 4;
-  const int tt = (int)(r % ntt);
-  const int i = (int)(r / ntt);
+  const int i = r / ntt, tt = r - i * ntt;
   const int g = lane >> 4, c16 = lane & 15;
   const int t = tt * 16 + c16;
   const half_t* gam = nullptr;
   if (t < p.T) {
-    if (p.multi) {
+    if (MULTI) {
       const int32_t ad = norm_id(p.ids[t], p.num_adapters);
       if (ad >= 0) gam = p.gammas[ad];
     } else {
@@ -672,7 +672,11 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
       pv.seg_chunk = kGemmChunk;
     }
     const int64_t grid = cdiv(pv.n_units, 4) + (a.multi ? 1 : 0);
-    hipLaunchKernelGGL(k_prep_v, dim3((unsigned)grid), dim3(256), 0, s, pv);
+    if (pv.n_units > INT32_MAX - 4) return hipErrorInvalidValue;
+    if (a.multi)
+      hipLaunchKernelGGL(k_prep_v<true>, dim3((unsigned)grid), dim3(256), 0, s, pv);
+    else
+      hipLaunchKernelGGL(k_prep_v<false>, dim3((unsigned)grid), dim3(256), 0, s, pv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

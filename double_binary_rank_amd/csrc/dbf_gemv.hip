@@ -20,6 +20,8 @@
 // Launches: prep(x) (with several adapters one extra workgroup also builds
 // the column blocks) -> stage 1 (writes z = beta*u, fp32) -> prep(z) ->
 // stage 2.
+#include <climits>
+
 #include "dbf_device.h"
 #include "dbf_launch.h"
 
@@ -132,24 +134,25 @@ __device__ inline void block_parts(float v0, float v1, Put&& put) {
 }
 
 // One wave per (term, token, 128-block); lane l owns entries 2l and 2l+1.
+template <bool MULTI>
 __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
-  if (p.seg_cbl != nullptr && blockIdx.x == 0) {
+  if (MULTI && p.seg_cbl != nullptr && blockIdx.x == 0) {
     segment_ids(p.ids, (int32_t)p.T, p.num_adapters, p.seg_chunk, p.seg_cbl, p.seg_hdr);
     return;
   }
   const int lane = threadIdx.x & 63;
-  const int64_t blk = ((int64_t)blockIdx.x - (p.seg_cbl != nullptr ? 1 : 0)) * 4 + (threadIdx.x >> 6);
-  const int64_t nblk = (int64_t)p.ell * p.T * p.nkb;
-  if (blk >= nblk) return;  // uniform per wave
-  const int64_t kb = blk % p.nkb;
-  const int64_t t = (blk / p.nkb) % p.T;
-  const int64_t i = blk / (p.nkb * p.T);
+  // block counts fit 32 bits (the workspace bounds them; the host checks)
+  const int blk = ((int)blockIdx.x - (MULTI && p.seg_cbl != nullptr ? 1 : 0)) * 4 + (threadIdx.x >> 6);
+  const int nkb = (int)p.nkb, T = (int)p.T;
+  if (blk >= p.ell * T * nkb) return;  // uniform per wave
+  const int r = blk / nkb, kb = blk - r * nkb;
+  const int i = r / T, t = r - i * T;
   const int kl = 2 * lane;
-  const int64_t k = kb * kColBlock + kl;
+  const int64_t k = (int64_t)kb * kColBlock + kl;
 
   bool live = true;
   const half_t* gam = p.gamma;
-  if (p.multi) {
+  if (MULTI) {
     const int32_t ad = p.ids[t];
     live = ad >= 0 && ad < p.num_adapters;
     if (live && !p.from_z) gam = p.gammas[ad];
@@ -197,6 +200,7 @@ __device__ inline v8i expand_signs_fp4(uint32_t w, uint32_t msk, uint32_t one) {
 struct GemvParams {
   int64_t rows, K, T, nrt, nkb, n_rg;
   int64_t nq, n_qg;      // streaming kernel: row quads, quad groups per column block
+  int64_t grid;          // workgroups launched (row-tile kernel)
   int64_t lds_b, lds_s;  // streaming kernel: LDS bytes for staged B operands / their scales
   int32_t ell, tcb;
   uint32_t sign_mask, fp4_one;  // 0x88888888, 0x22222222
@@ -295,7 +299,7 @@ __device__ inline void gemv_epilogue(const GemvParams& p, const half_t* srow, v4
 // wave keeps the B operands of its chunk in registers and streams the sign
 // blocks of all RTG row tiles against them.  Partial tiles are summed across
 // waves in a fixed order through LDS.
-template <int STAGE, int RTG, int KC>
+template <int STAGE, int RTG, int KC, bool MULTI>
 __global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
   __shared__ v4f red[4][RTG][64];
   static_assert(RTG % kQuad == 0, "row tiles come in quads");
@@ -304,15 +308,17 @@ __global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15, g = lane >> 4;
   const int c = j / kParts, part = j - kParts * (j / kParts);
-  const int64_t n_cb = p.multi ? (int64_t)p.hdr->n_colblocks : p.n_cb_host;
-  const int64_t n_items = n_cb * p.n_rg;
+  // item counts fit 32 bits (the host checks)
+  const int n_cb = MULTI ? p.hdr->n_colblocks : (int)p.n_cb_host;
+  const int n_items = n_cb * (int)p.n_rg;
+  const int grid = (int)p.grid;
 
-  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int64_t cb = it / p.n_rg, rg = it % p.n_rg;
+  for (int it = blockIdx.x; it < n_items; it += grid) {
+    const int cb = it / (int)p.n_rg, rg = it - cb * (int)p.n_rg;
     int64_t t0, t1;
     int32_t ad;
     Factors f;
-    if (p.multi) {
+    if (MULTI) {
       const ColBlock cbk = p.cbl[cb];
       t0 = cbk.t0;
       t1 = cbk.t1;
@@ -324,12 +330,12 @@ __global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
         f.beta = p.betas[ad];
       }
     } else {
-      t0 = cb * p.tcb;
+      t0 = (int64_t)cb * p.tcb;
       t1 = t0 + p.tcb < p.T ? t0 + p.tcb : p.T;
       ad = 0;
       f = p.single;
     }
-    const int64_t tile0 = rg * RTG;
+    const int64_t tile0 = (int64_t)rg * RTG;
     if (ad < 0) {
       if (STAGE == 2 && !p.accumulate) {
         const int64_t r0 = tile0 * kRowTile;
@@ -1069,8 +1075,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
 // -------------------------------------------------------------- launch ----
 
 template <int STAGE, int RTG, int KC>
-static hipError_t launch_gemv_stage(const GemvParams& p, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv_fp4<STAGE, RTG, KC>), dim3((unsigned)grid), dim3(256), 0, s, p);
+static hipError_t launch_gemv_stage(GemvParams p, int64_t grid, hipStream_t s) {
+  if ((p.multi ? max_colblocks(p.T) : p.n_cb_host) * p.n_rg > INT32_MAX) return hipErrorInvalidValue;
+  p.grid = grid;
+  if (p.multi)
+    hipLaunchKernelGGL((k_gemv_fp4<STAGE, RTG, KC, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemv_fp4<STAGE, RTG, KC, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1121,8 +1132,12 @@ static hipError_t launch_gemv_stage_any(GemvParams p, int64_t n_cb_est, int64_t 
 
 static hipError_t launch_prep(PrepParams p, hipStream_t s) {
   const int64_t nblk = (int64_t)p.ell * p.T * p.nkb;
+  if (nblk > INT32_MAX - 8) return hipErrorInvalidValue;
   const int64_t grid = cdiv(nblk, 4) + (p.seg_cbl != nullptr ? 1 : 0);
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)grid), dim3(256), 0, s, p);
+  if (p.multi)
+    hipLaunchKernelGGL(k_prep<true>, dim3((unsigned)grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_prep<false>, dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
