@@ -261,7 +261,7 @@ def main():
         ach = f_st[dom] / t_ph[dom] / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": committed_traffic(dom[-1]),
-                "kernel": f"k_gemm<{dom[-1]}, 2, true> ({dom} of the T=256 call)",
+                "kernel": f"k_gemm<{dom[-1]}, 2, true, false> ({dom} of the T=256 call)",
                 "launch_us": t_ph[dom] * 1e6, "alg_flops_per_launch": f_st[dom],
                 "phase_launch_us": {k: v * 1e6 for k, v in t_ph.items()}}
         log("phase launches: " + ", ".join(f"{k} {v * 1e6:.2f} us" for k, v in t_ph.items())
