@@ -352,6 +352,34 @@ def main():
         }
         log(f"multi-adapter: {tm * 1e6:.1f} us/call, {bm / tm / 1e9:.1f} GB/s")
 
+    # ------------------- transposed product dW^T g (input gradient) --
+    if want("transposed"):
+        plt = pl.transposed()
+        tt_ = time_calls(lambda i: pl.transposed(), 20, 2) / 20  # both sign matrices
+        gT = np.random.default_rng(7).standard_normal((T, N_)).astype(np.float16)
+        gT = torch.as_tensor(gT).to(dev)
+        yT = torch.empty((T, M_), dtype=torch.float16, device=dev)
+        wsT = torch.empty(dbf.dbf_workspace_bytes(M_, R_, N_, 1, T), dtype=torch.uint8, device=dev)
+        TB1s, TB2s = replicate(plt.B1, n_inst), replicate(plt.B2, n_inst)
+        plt.forward(gT, y=yT, ws=wsT)
+        torch.cuda.synchronize()
+        errT = oracle.max_norm_error(
+            yT.float().cpu().numpy(),
+            oracle.forward_transposed(gT.cpu().numpy(), L.S1, L.S2, L.alpha, L.beta, L.gamma))
+
+        def callT(i):
+            k = i % n_inst
+            dbf.dbf_forward(gT, TB1s[k], TB2s[k], plt.alpha, plt.beta, plt.gamma, M_, R_, N_,
+                            y=yT, ws=wsT)
+
+        tT = time_calls(callT, args.steps, args.warmup) / args.steps
+        out["transposed_T256"] = {
+            "T": T, "us_per_call": tT * 1e6, "tokens_per_s": T / tT,
+            "achieved_TFLOPs": alg_flops(M_, R_, N_, 1, T) / tT / 1e12,
+            "transpose_signs_us": tt_ * 1e6, "parity_err": errT,
+        }
+        log(f"transposed T=256: {tT * 1e6:.2f} us/call (sign transposes {tt_ * 1e6:.1f} us)")
+
     # ------------------------------------------------ copy calibration --
     if args.copy_calibration:
         n = COPY_MIB << 20

@@ -38,6 +38,7 @@ EXPORTS = (
     "dbf_packed_bytes",
     "dbf_pack_signs",
     "dbf_unpack_signs",
+    "dbf_transpose_signs",
     "dbf_workspace_bytes",
     "dbf_forward",
     "dbf_forward_multi_adapter",
@@ -92,6 +93,8 @@ lib.dbf_pack_signs.restype = _i32
 lib.dbf_pack_signs.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp]
 lib.dbf_unpack_signs.restype = _i32
 lib.dbf_unpack_signs.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp]
+lib.dbf_transpose_signs.restype = _i32
+lib.dbf_transpose_signs.argtypes = [_vp, _i64, _i64, _vp, _vp]
 lib.dbf_workspace_bytes.restype = _i32
 lib.dbf_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, ctypes.POINTER(_sz)]
 lib.dbf_forward.restype = _i32

@@ -20,6 +20,7 @@ __all__ = [
     "dbf_packed_bytes",
     "dbf_pack_signs",
     "dbf_unpack_signs",
+    "dbf_transpose_signs",
     "dbf_workspace_bytes",
     "dbf_forward",
     "dbf_forward_multi_adapter",
@@ -40,9 +41,10 @@ def _ptr(t) -> ctypes.c_void_p:
 
 
 def _row_major(t: torch.Tensor, name: str) -> int:
-    if t.dim() != 2 or t.stride(1) != 1:
+    # a size-1 inner dimension may carry any stride
+    if t.dim() != 2 or (t.stride(1) != 1 and t.size(1) != 1):
         raise ValueError(f"{name} must be 2-D with unit inner stride")
-    return t.stride(0)
+    return max(t.stride(0), t.size(1)) if t.size(0) == 1 else t.stride(0)
 
 
 def dbf_abi_version() -> int:
@@ -81,6 +83,18 @@ def dbf_unpack_signs(packed: torch.Tensor, rows: int, cols: int, out: torch.Tens
     ld = _row_major(out, "out")
     check(lib.dbf_unpack_signs(_ptr(packed), rows, cols, _ptr(out), ld, _stream(stream)),
           "dbf_unpack_signs")
+    return out
+
+
+def dbf_transpose_signs(packed: torch.Tensor, rows: int, cols: int,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Packed signs of the cols x rows transpose of the packed rows x cols
+    matrix ``packed``.  Returns a uint8 device tensor of
+    dbf_packed_bytes(cols, rows) bytes."""
+    if out is None:
+        out = torch.empty(dbf_packed_bytes(cols, rows), dtype=torch.uint8, device=packed.device)
+    check(lib.dbf_transpose_signs(_ptr(packed), rows, cols, _ptr(out), _stream(stream)),
+          "dbf_transpose_signs")
     return out
 
 
@@ -204,3 +218,11 @@ class PackedLayer:
     def forward(self, x: torch.Tensor, **kw) -> torch.Tensor:
         return dbf_forward(x, self.B1, self.B2, self.alpha, self.beta, self.gamma, self.N, self.R,
                            self.M, **kw)
+
+    def transposed(self) -> "PackedLayer":
+        """The layer of dW^T = sum_i diag(gamma_i) S2^T diag(beta_i) S1^T
+        diag(alpha_i) (M outputs, N inputs): its forward maps an output
+        gradient g [T][N] to g dW [T][M], the input gradient."""
+        return PackedLayer(dbf_transpose_signs(self.B2, self.R, self.M),
+                           dbf_transpose_signs(self.B1, self.N, self.R),
+                           self.gamma, self.beta, self.alpha, self.M, self.R, self.N)

@@ -101,6 +101,16 @@ dbf_status dbf_unpack_signs(const uint32_t* src, int64_t rows, int64_t cols, int
   return hip_status(dbf::launch_unpack(src, rows, cols, dst, ld_dst, (hipStream_t)stream));
 }
 
+dbf_status dbf_transpose_signs(const uint32_t* src, int64_t rows, int64_t cols, uint32_t* dst,
+                               void* stream) {
+  if (src == nullptr || dst == nullptr || rows <= 0 || cols <= 0 || rows > DBF_MAX_DIM ||
+      cols > DBF_MAX_DIM)
+    return DBF_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(dst)) return DBF_ERR_ALIGNMENT;
+  if (src == dst) return DBF_ERR_INVALID_ARG;
+  return hip_status(dbf::launch_transpose(src, rows, cols, dst, (hipStream_t)stream));
+}
+
 dbf_status dbf_workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T,
                                size_t* bytes) {
   if (N <= 0 || R <= 0 || M <= 0 || ell < 1 || T < 0 || bytes == nullptr)

@@ -62,6 +62,49 @@ __global__ void k_unpack(const uint32_t* __restrict__ src, int64_t rows, int64_t
   }
 }
 
+// Packed words of the cols x rows transpose S^T, gathered bit by bit from the
+// packed words of S (rows x cols): output word gid holds, for its row r'
+// (a column of S) and 32 columns c' (rows of S), the bits of S[c'][r'].
+// The transpose of the update, dW^T = sum_i diag(gamma_i) S2^T diag(beta_i)
+// S1^T diag(alpha_i), is again a double-binary product with S2^T and S1^T
+// as its sign matrices; the input gradient of the LoRDBA training pipeline's
+// backward pass (summary section 2 "Pipeline de Entrenamiento", step 3) is
+// that product applied to the output gradient.  Padding bits are 0 (+1).
+__global__ void k_transpose(const uint32_t* __restrict__ src, int64_t rows, int64_t cols,
+                            int64_t nkb_src, int64_t nkb_dst, int64_t total_words,
+                            uint32_t* __restrict__ dst) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total_words) return;
+  const int64_t unit = gid / kUnitWords;
+  const int w = (int)(gid % kUnitWords);
+  const int lam = w >> 2, h = w & 3;
+  const int64_t drow = ((unit / nkb_dst) * kQuad + h) * kRowTile + (lam & 15);  // a column of S
+  const int64_t k0 = (unit % nkb_dst) * kColBlock;
+  uint32_t word = 0;
+  if (drow < cols) {
+    // where column drow of S sits inside each packed word of S
+    const int c = (int)(drow % kColBlock);
+    const int g = (c >> 3) & 3, ss = 8 * (c >> 5) + (c & 7);
+    const int64_t ublk = drow / kColBlock;
+    for (int s = 0; s < 32; ++s) {
+      const int64_t srow = k0 + slot_col(lam >> 4, s);  // a row of S
+      if (srow >= rows) continue;
+      const int64_t sw = ((srow / (kQuad * kRowTile)) * nkb_src + ublk) * kUnitWords +
+                         4 * (16 * g + (int)(srow % kRowTile)) + (int)((srow % (kQuad * kRowTile)) / kRowTile);
+      word |= ((src[sw] >> slot_bit(ss)) & 1u) << slot_bit(s);
+    }
+  }
+  dst[gid] = word;
+}
+
+hipError_t launch_transpose(const uint32_t* src, int64_t rows, int64_t cols, uint32_t* dst,
+                            hipStream_t s) {
+  const int64_t total = packed_words_total(cols, rows);
+  hipLaunchKernelGGL(k_transpose, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, src, rows,
+                     cols, cdiv(cols, kColBlock), cdiv(rows, kColBlock), total, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const void* src, int dtype, int64_t rows, int64_t cols, int64_t ld,
                        uint32_t* dst, hipStream_t s) {
   const int64_t nkb = cdiv(cols, kColBlock);

@@ -93,6 +93,8 @@ hipError_t launch_pack(const void* src, int dtype, int64_t rows, int64_t cols, i
                        uint32_t* dst, hipStream_t s);
 hipError_t launch_unpack(const uint32_t* src, int64_t rows, int64_t cols, int8_t* dst, int64_t ld,
                          hipStream_t s);
+hipError_t launch_transpose(const uint32_t* src, int64_t rows, int64_t cols, uint32_t* dst,
+                            hipStream_t s);
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s);
 Path choose_path(int64_t T, int64_t tokens_per_segment_estimate);
 // tokens per column block on the small-T path (3 fp8 parts x ell terms

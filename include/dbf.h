@@ -116,6 +116,26 @@ dbf_status dbf_unpack_signs(const uint32_t* src, int64_t rows, int64_t cols, int
                             int64_t ld_dst, void* stream);
 
 /*
+ * Transpose packed signs: from the packed rows x cols matrix S in `src`
+ * (dbf_pack_signs layout) write the packed cols x rows matrix S^T into `dst`
+ * (dbf_packed_bytes(cols, rows) bytes).  Device buffers, 16-byte aligned,
+ * not overlapping; asynchronous on `stream`.
+ *
+ * The transpose of the update, dW^T = sum_i diag(gamma_i) S2^T diag(beta_i)
+ * S1^T diag(alpha_i), is again a double-binary product (LoRDBA summary,
+ * section 2 "Arquitectura Central", with the roles of the two sign matrices
+ * and of alpha and gamma exchanged).  Applied to an output gradient g it is
+ * the input gradient of the training pipeline's backward pass (same summary,
+ * "Pipeline de Entrenamiento", step 3): dbf_forward with B1 = S2^T (M x R),
+ * B2 = S1^T (R x N), alpha = gamma, beta = beta, gamma = alpha and the roles
+ * of N and M exchanged computes g dW, i.e. dW^T g per row of g.
+ * Errors: INVALID_ARG (null pointer, rows/cols <= 0 or > DBF_MAX_DIM,
+ * src == dst), ALIGNMENT, HIP.
+ */
+dbf_status dbf_transpose_signs(const uint32_t* src, int64_t rows, int64_t cols, uint32_t* dst,
+                               void* stream);
+
+/*
  * Workspace bytes needed by dbf_forward and dbf_forward_multi_adapter for
  * these sizes (the same bound serves both).  T may be 0 (returns 0 bytes
  * needed beyond a small header).

@@ -64,6 +64,22 @@ A = 0x10000  # 16-byte aligned
 MIS = 0x10002  # misaligned
 
 
+@pytest.mark.parametrize("args,want", [
+    ((0, 64, 128, A), _lib.DBF_ERR_INVALID_ARG),
+    ((A, 64, 128, 0), _lib.DBF_ERR_INVALID_ARG),
+    ((A, 0, 128, A + 4096), _lib.DBF_ERR_INVALID_ARG),
+    ((A, 64, -3, A + 4096), _lib.DBF_ERR_INVALID_ARG),
+    ((A, (1 << 30) + 1, 128, A + 4096), _lib.DBF_ERR_INVALID_ARG),
+    ((A, 64, 128, A), _lib.DBF_ERR_INVALID_ARG),  # in place
+    ((MIS, 64, 128, A), _lib.DBF_ERR_ALIGNMENT),
+    ((A, 64, 128, MIS), _lib.DBF_ERR_ALIGNMENT),
+])
+def test_transpose_errors(args, want):
+    src, rows, cols, dst = args
+    assert L.dbf_transpose_signs(ctypes.c_void_p(src), rows, cols, ctypes.c_void_p(dst),
+                                 None) == want
+
+
 def _fwd(**kw):
     a = dict(x=A, ldx=64, B1=A, B2=A, alpha=A, beta=A, gamma=A, N=32, R=16, M=64, ell=1, T=4,
              y=A, ldy=32, y_type=_lib.DBF_F16, flags=0, ws=A, ws_bytes=1 << 30, stream=None)

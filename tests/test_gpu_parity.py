@@ -57,6 +57,54 @@ def test_pack_latent_sign(dtype):
     assert np.array_equal(packed.cpu().numpy().view(np.uint32), want)
 
 
+@pytest.mark.parametrize("rows,cols", [(64, 128), (65, 129), (200, 37), (1, 300), (513, 64)])
+def test_transpose_signs(rows, cols):
+    """Transposing packed signs equals packing the transposed matrix (byte
+    for byte, padding included) and unpacks to S^T."""
+    import double_binary_rank_amd as dbf
+    S = synth.make_signs(np.random.default_rng(rows * 7 + cols), rows, cols)
+    P = dbf.dbf_pack_signs(H().to_dev(S))
+    PT = dbf.dbf_transpose_signs(P, rows, cols)
+    want = dbf.dbf_pack_signs(H().to_dev(np.ascontiguousarray(S.T)))
+    torch.cuda.synchronize()
+    assert torch.equal(PT, want)
+    assert np.array_equal(dbf.dbf_unpack_signs(PT, cols, rows).cpu().numpy(), S.T)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("shape", [(72, 40, 136, 2, 9), (300, 130, 260, 1, 37)])
+def test_transposed_forward(shape, path):
+    """The transposed layer's forward maps g [T][N] to dW^T g per row
+    (oracle.forward_transposed): fp16 inputs within the bar, integer inputs
+    bit for bit, and <g, dW x> = <dW^T g, x> between the two GPU products."""
+    N, R, M, ell, T = shape
+    L = synth.make_layer(N, R, M, ell, T, seed=97)
+    pl = H().upload(L)
+    plt = pl.transposed()
+    assert (plt.N, plt.R, plt.M) == (M, R, N)
+    g = np.random.default_rng(99).standard_normal((T, N)).astype(np.float16)
+    got = plt.forward(H().to_dev_rows(g), path=path, y=H().empty_rows(T, M, torch.float32),
+                      y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = oracle.forward_transposed(g, L.S1, L.S2, L.alpha, L.beta, L.gamma)
+    got = got.cpu().numpy().astype(np.float64)
+    assert oracle.max_norm_error(got, want) <= TOL
+    y = H().run_layer(L, path=path, y_dtype=torch.float32, pl=pl)
+    lhs = float(np.sum(g.astype(np.float64) * y))
+    rhs = float(np.sum(got * L.x.astype(np.float64)))
+    assert abs(lhs - rhs) <= 4 * TOL * (np.abs(g).sum() * np.abs(y).max() + 1.0)
+    Li = synth.make_layer(N, R, M, ell, T, seed=100, alpha="ones", beta="ones", gamma="ones",
+                          x_kind="int3")
+    gi = np.random.default_rng(101).integers(-3, 4, (T, N)).astype(np.float16)
+    pli = H().upload(Li).transposed()
+    goti = pli.forward(H().to_dev_rows(gi), path=path, y=H().empty_rows(T, M, torch.float32),
+                       y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    wanti = oracle.forward_transposed(gi, Li.S1, Li.S2, Li.alpha, Li.beta, Li.gamma)
+    assert np.array_equal(goti.cpu().numpy().astype(np.float64),
+                          wanti.astype(np.float32).astype(np.float64))
+
+
 @pytest.mark.parametrize("rows,cols", [(37, 300), (128, 64), (3, 1)])
 def test_unpack_roundtrip(rows, cols):
     rng = np.random.default_rng(rows + cols)

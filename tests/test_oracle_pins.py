@@ -260,6 +260,18 @@ def test_adjoint():
     assert pin_adjoint(oracle.forward, oracle.forward_transposed)
 
 
+def test_transposed_equals_dense():
+    """dW^T g row by row equals g times the dense update (delta_w is pinned
+    by the hand example and the Hadamard closed form), for ell = 2 and
+    ragged sizes."""
+    L = _rand_layer(12, 21, 13, 29, 2, 4)
+    g = np.random.default_rng(13).standard_normal((4, 21))
+    got = oracle.forward_transposed(g, L.S1, L.S2, L.alpha, L.beta, L.gamma)
+    dense = g @ oracle.delta_w(L.S1, L.S2, L.alpha, L.beta, L.gamma)
+    assert got.shape == (4, 29)
+    assert np.allclose(got, dense, rtol=1e-12, atol=1e-12)
+
+
 def test_sign_convention():
     assert pin_sign_convention(oracle.sign_of_latent)
 
