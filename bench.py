@@ -352,6 +352,57 @@ def main():
         }
         log(f"multi-adapter: {tm * 1e6:.1f} us/call, {bm / tm / 1e9:.1f} GB/s")
 
+    # ------------------------------- the other configurations, timed --
+    if want("configs"):
+        cfgs = {}
+        for cfg, Tc in ((1, 4), (2, 1), (2, 8), (4, 1), (4, 16), (4, 256), (40, 1), (40, 16),
+                        (40, 256)):
+            Lc = synth.make_config_layer(cfg, Tc)
+            Nc, Rc, Mc = Lc.S1.shape[0], Lc.S1.shape[1], Lc.S2.shape[1]
+            plc = dbf.PackedLayer.from_signs(Lc.S1, Lc.S2, Lc.alpha, Lc.beta, Lc.gamma,
+                                             device=dev)
+            lb = plc.B1.numel() + plc.B2.numel()
+            k_inst = max(1, min(4096, -(-(512 << 20) // lb)))  # cold: >= 512 MiB of signs
+            cB1, cB2 = replicate(plc.B1, k_inst), replicate(plc.B2, k_inst)
+            xc = torch.as_tensor(Lc.x).to(dev)
+            yc = torch.empty((Tc, Nc), dtype=torch.float16, device=dev)
+            wsc = torch.empty(dbf.dbf_workspace_bytes(Nc, Rc, Mc, 1, Tc), dtype=torch.uint8,
+                              device=dev)
+            plc.forward(xc, y=yc, ws=wsc)
+            torch.cuda.synchronize()
+            if Nc * Rc * Mc <= 4096 * 64 * 4096:
+                errc = oracle.max_norm_error(
+                    yc.float().cpu().numpy(),
+                    oracle.forward(Lc.x, Lc.S1, Lc.S2, Lc.alpha, Lc.beta, Lc.gamma))
+                chk = "full"
+            else:  # sampled: 4 tokens x 64 outputs
+                ts = np.arange(min(Tc, 4))
+                ns = np.random.default_rng(cfg + Tc).choice(Nc, 64, replace=False)
+                want_s = oracle.forward_rows(Lc.x[ts], Lc.S1, Lc.S2, Lc.alpha, Lc.beta, Lc.gamma,
+                                             ns)
+                errc = oracle.max_norm_error(yc.float().cpu().numpy()[ts][:, ns], want_s)
+                chk = "4 tokens x 64 outputs"
+
+            def callc(i, cB1=cB1, cB2=cB2, plc=plc, xc=xc, yc=yc, wsc=wsc, k=k_inst, n=(Nc, Rc, Mc)):
+                dbf.dbf_forward(xc, cB1[i % k], cB2[i % k], plc.alpha, plc.beta, plc.gamma, *n,
+                                y=yc, ws=wsc)
+
+            nc = max(args.steps, 100)
+            tc = time_calls(callc, nc, args.warmup) / nc
+            bc, fc = alg_bytes(Nc, Rc, Mc, 1, Tc), alg_flops(Nc, Rc, Mc, 1, Tc)
+            name = f"{synth.CONFIGS[cfg].name}_T{Tc}"
+            cfgs[name] = {
+                "N": Nc, "R": Rc, "M": Mc, "T": Tc, "us_per_call": tc * 1e6,
+                "tokens_per_s": Tc / tc, "effective_GBs": bc / tc / 1e9,
+                "hbm_frac": bc / tc / 1e9 / HBM_PEAK_GBS,
+                "mfma_frac": fc / tc / 1e12 / MFMA_F16_PEAK_TFLOPS, "cold_instances": k_inst,
+                "parity_err": errc, "parity_check": chk,
+            }
+            log(f"{name}: {tc * 1e6:.2f} us/call, {bc / tc / 1e9:.1f} GB/s, "
+                f"{fc / tc / 1e12:.1f} TFLOP/s, err {errc:.2e}")
+            del cB1, cB2
+        out["configs"] = cfgs
+
     # ------------------- transposed product dW^T g (input gradient) --
     if want("transposed"):
         plt = pl.transposed()
