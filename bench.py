@@ -241,9 +241,9 @@ def main():
         achieved_tflops = flops / t_call / 1e12
         log(f"prefill T=256: {t_call * 1e6:.2f} us/call, {achieved_tflops:.1f} TFLOP/s")
 
-        # each phase alone (one kernel each on this path): prep (v = gamma*x
-        # in operand order), stage 1 (z = beta * B2 v), stage 2 (y = alpha *
-        # B1 z); a phase reads what the earlier phases left in ws
+        # each launch alone: stage 1 (z = beta * B2 (gamma x), reading x in
+        # place; the prep phase launches nothing on this layer) and stage 2
+        # (y = alpha * B1 z), which reads the z stage 1 left in ws
         def phase_call(ph):
             def f(i):
                 k = i % n_inst
@@ -252,7 +252,7 @@ def main():
             return f
 
         t_ph = {}
-        for ph in ("prep", "stage1", "stage2"):
+        for ph in ("stage1", "stage2"):
             call256(0)
             torch.cuda.synchronize()
             t_ph[ph] = time_graph(phase_call(ph), 64, max(args.steps // 16, 4), 2)
@@ -261,7 +261,9 @@ def main():
         ach = f_st[dom] / t_ph[dom] / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": committed_traffic(dom[-1]),
-                "kernel": f"k_gemm<{dom[-1]}, 2, true, false> ({dom} of the T=256 call)",
+                "kernel": {"stage1": "k_gemm<1, 2, true, false, true, 8>",
+                           "stage2": "k_gemm<2, 2, true, false, false, 4>"}[dom]
+                          + f" ({dom} of the T=256 call)",
                 "launch_us": t_ph[dom] * 1e6, "alg_flops_per_launch": f_st[dom],
                 "phase_launch_us": {k: v * 1e6 for k, v in t_ph.items()}}
         log("phase launches: " + ", ".join(f"{k} {v * 1e6:.2f} us" for k, v in t_ph.items())

@@ -9,7 +9,12 @@
 //
 // Launches: prep (v_i = gamma_i * x; with several adapters one extra
 // workgroup also builds the column blocks) -> stage 1 (z_i = beta_i * B2 v_i)
-// -> stage 2 (y = sum_i alpha_i * B1 z_i).  v and z live in the workspace in
+// -> stage 2 (y = sum_i alpha_i * B1 z_i).  With one adapter, M a multiple
+// of 8 and gamma 16-byte aligned there is no prep launch: stage 1 reads x in
+// place as its token operand and folds gamma_i into the expanded signs,
+// +-gamma_i[m] being exact in fp16, so the products gamma*x*(+-1) are exact
+// in the fp32 accumulation (the prep path rounds gamma*x to fp16 once).
+// v and z live in the workspace in
 // MFMA operand order: tiles of 16 tokens x 128 reduction entries, 4 KB each
 // (4 steps x 64 lanes x 8), so every operand load of a wave is 1 KB
 // contiguous, and entries past the reduction length are zero, so the last
@@ -22,9 +27,11 @@
 // step s, so both operands see the same k and no lane exchange is needed.
 //
 // Work item: a column block of 16*NC tokens and either one row quad (64
-// rows) whose reduction the four waves split (SPLITK: interleaved 128-blocks,
-// partial tiles summed in a fixed order through LDS), or four row quads, one
-// per wave, each over the whole reduction (for short reductions).  Output
+// rows) whose reduction the NWV waves split (SPLITK: interleaved 128-blocks,
+// partial tiles summed in a fixed order through LDS; 8 waves when there are
+// no more items than compute units, so two waves share each SIMD), or four
+// row quads, one per wave, each over the whole reduction (for short
+// reductions).  Output
 // column j of an MFMA depends only on operand column j, so columns of tokens
 // past the block's end read a valid token's tile row and are simply not
 // stored.
@@ -45,6 +52,8 @@ struct GemmParams {
   int32_t y_f32, accumulate, multi, xcd_remap;
   int32_t grid;             // workgroups launched
   uint32_t msk16, one16;  // 0x80008000, 0x3C003C00 (kept in registers)
+  const half_t* x;        // stage 1 reading x in place: token rows, stride ldx
+  int64_t ldx;
   const half_t* opnd;     // this stage's operand tiles (v or z)
   int64_t opnd_term;      // halfs per term
   int32_t opnd_nkb;       // 128-blocks per token tile row of the operand
@@ -79,19 +88,35 @@ __device__ inline v8h expand_step_f16(uint32_t w, uint32_t msk, uint32_t one) {
   return __builtin_bit_cast(v8h, o);
 }
 
-// Operands of one 128-block: sign words of the four row tiles and the
-// operand b[s][c] of step s for token column c.
-template <int NC>
+// As expand_step_f16 with the magnitudes of a scale vector along K: the
+// sign bits are XORed into gam (the lane's 8 entries of gamma_i for this
+// step, two per word), giving +-gamma exactly.
+template <int s>
+__device__ inline v8h expand_step_gamma(uint32_t w, uint32_t msk, const v4u& gam) {
+  const uint32_t U = w << (7 - s), V = w << (3 - s);
+  v4u o;
+  o[0] = (__builtin_amdgcn_perm(V, U, 0x040C000Cu) & msk) ^ gam[0];
+  o[1] = (__builtin_amdgcn_perm(V, U, 0x050C010Cu) & msk) ^ gam[1];
+  o[2] = (__builtin_amdgcn_perm(V, U, 0x060C020Cu) & msk) ^ gam[2];
+  o[3] = (__builtin_amdgcn_perm(V, U, 0x070C030Cu) & msk) ^ gam[3];
+  return __builtin_bit_cast(v8h, o);
+}
+
+// Operands of one 128-block: sign words of the four row tiles, the operand
+// b[s][c] of step s for token column c and, when stage 1 reads x in place,
+// gamma_i at the lane's 8 entries of each step.
+template <int NC, bool XIN>
 struct Block {
   v4u a;
   v8h b[4][NC];
+  v4u gm[XIN ? 4 : 1];
 };
 
 // orow[c]: the lane's 16 bytes of token column c's tile row; step s of
 // block kb sits at orow[c] + kb*2048 + s*512.
 template <int NC>
-__device__ inline void load_block(Block<NC>& B, const char* sq, const half_t* const (&orow)[NC],
-                                  int kb) {
+__device__ inline void load_block(Block<NC, false>& B, const char* sq,
+                                  const half_t* const (&orow)[NC], int kb) {
   B.a = *(gv4up)(sq + ((int64_t)kb << 10));
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -99,14 +124,68 @@ __device__ inline void load_block(Block<NC>& B, const char* sq, const half_t* co
     for (int c = 0; c < NC; ++c) B.b[s][c] = *(gv8hp)(orow[c] + (int64_t)kb * 2048 + s * 512);
 }
 
+// x read in place.  The MFMA operand puts 16 tokens in 16 adjacent lanes, so
+// loading it straight from the rows of x would touch 16 half-used cache
+// lines per 16 lanes.  Instead lane L loads 16-byte chunk L%16 of rows L/16,
+// L/16 + 4, ... of the block's 16*NC tokens (b, read as a flat array: 256
+// contiguous bytes per 16 lanes), and x_to_operand passes them through the
+// wave's own LDS area into operand order.  grow is entry 8g of gamma_i, so
+// step s of block kb needs the 8 gamma entries at kb*128 + 32s (16 bytes,
+// aligned as M is a multiple of 8).  A whole block (128 kb + 128 <= M):
 template <int NC>
-__device__ inline void mma_block(v4f (&acc)[4][NC], const Block<NC>& B, uint32_t msk,
+__device__ inline void load_block(Block<NC, true>& B, const char* sq,
+                                  const half_t* const (&xrow)[4 * NC], const half_t* grow,
+                                  int kb) {
+  B.a = *(gv4up)(sq + ((int64_t)kb << 10));
+  const int k0 = kb * kColBlock;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) B.gm[s] = *(gv4up)(grow + k0 + 32 * s);
+#pragma unroll
+  for (int j = 0; j < 4 * NC; ++j) (&B.b[0][0])[j] = *(gv8hp)(xrow[j] + k0);
+}
+
+// The last, partial block: lim = M - 128 kb < 128 entries exist; chunks past
+// them are zero (not read).  xrow[j] already includes the lane's chunk, 8 *
+// (lane % 16) entries.
+template <int NC>
+__device__ inline void load_block_tail(Block<NC, true>& B, const char* sq,
+                                       const half_t* const (&xrow)[4 * NC], const half_t* grow,
+                                       int kb, int lim, int g, int chunk) {
+  B.a = *(gv4up)(sq + ((int64_t)kb << 10));
+  const int k0 = kb * kColBlock;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bool ok = 32 * s + 8 * g < lim;
+    B.gm[s] = ok ? *(gv4up)(grow + k0 + 32 * s) : v4u{0u, 0u, 0u, 0u};
+  }
+  const bool ok = 8 * chunk < lim;
+#pragma unroll
+  for (int j = 0; j < 4 * NC; ++j) (&B.b[0][0])[j] = ok ? *(gv8hp)(xrow[j] + k0) : v8h{};
+}
+
+// Row-chunk order -> operand order through the wave's LDS area: row r of
+// the block is 256 bytes, its chunk c stored at position c ^ (r % 16), so
+// the 8 or 16 lanes an LDS pass serves hit distinct banks on both sides.
+// wr[j] / rd[s*NC + c] are the lane's byte offsets (loop invariant).
+template <int NC>
+__device__ inline void x_to_operand(Block<NC, true>& B, char* area, const int (&wr)[4 * NC],
+                                    const int (&rd)[4 * NC]) {
+#pragma unroll
+  for (int j = 0; j < 4 * NC; ++j) *(v8h*)(area + wr[j]) = (&B.b[0][0])[j];
+#pragma unroll
+  for (int j = 0; j < 4 * NC; ++j) (&B.b[0][0])[j] = *(const v8h*)(area + rd[j]);
+}
+
+template <int NC, bool XIN>
+__device__ inline void mma_block(v4f (&acc)[4][NC], const Block<NC, XIN>& B, uint32_t msk,
                                  uint32_t one) {
   auto step = [&](auto sc) {
     constexpr int s = decltype(sc)::value;
     v8h a[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) a[h] = expand_step_f16<s>(B.a[h], msk, one);
+    for (int h = 0; h < 4; ++h)
+      a[h] = XIN ? expand_step_gamma<s>(B.a[h], msk, B.gm[XIN ? s : 0])
+                 : expand_step_f16<s>(B.a[h], msk, one);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -195,10 +274,15 @@ __global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
   }
 }
 
-template <int STAGE, int NC, bool SPLITK, bool MULTI>
-__global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
+template <int STAGE, int NC, bool SPLITK, bool MULTI, bool XIN, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
+  static_assert(!XIN || (STAGE == 1 && !MULTI), "x is read in place by single-adapter stage 1");
+  static_assert(NWV == 4 || (SPLITK && NC == 2 && NWV == 8), "8 waves only split a reduction");
   constexpr int D = 2;  // operand buffers per wave (deeper rings measured slower)
-  __shared__ v4f red[SPLITK ? 4 : 1][SPLITK ? 4 * NC : 1][64];
+  constexpr int TPW = 4 * NC / NWV;  // SPLITK: output tiles each wave finishes
+  __shared__ v4f red[SPLITK ? NWV : 1][SPLITK ? 4 * NC : 1][64];
+  // x staging (XIN): 16*NC rows of 256 bytes per wave
+  __shared__ v8h xst[XIN ? NWV : 1][XIN ? 16 * NC * 16 : 1];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
@@ -254,11 +338,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     const bool active = SPLITK || q < p.nq;  // idle waves still reach every barrier
     const char* sq =
         (const char*)(STAGE == 1 ? f.B2 : f.B1) + ((int64_t)(active ? q : 0) * p.nkb << 10) + lane * 16;
-    // this wave's 128-blocks: wv, wv+4, ... (SPLITK) or all of them
-    const int kb0 = SPLITK ? wv : 0, kst = SPLITK ? 4 : 1;
-    const int nkw = SPLITK ? (p.nkb - wv + 3) / 4 : p.nkb;
+    // this wave's 128-blocks: wv, wv+NWV, ... (SPLITK) or all of them; with
+    // x read in place a partial last block is taken apart from the others
+    const int nfull = XIN ? p.K / kColBlock : p.nkb;
+    const int kb0 = SPLITK ? wv : 0, kst = SPLITK ? NWV : 1;
+    const int nkw = SPLITK ? (nfull - wv + NWV - 1) / NWV : nfull;
     const bool run = active && nkw > 0;
-    float ys[SPLITK ? NC : 4 * NC][4];  // stage 2: running sum over the terms
+    const bool tail = XIN && active && nfull < p.nkb && (!SPLITK || nfull % NWV == wv);
+    float ys[SPLITK ? TPW : 4 * NC][4];  // stage 2: running sum over the terms
 
     for (int i = 0; i < p.ell; ++i) {
       // row scales of this wave's quad (lane L: row 64q + L), loaded first
@@ -267,13 +354,41 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
       const half_t* sv = (STAGE == 1 ? f.beta : f.alpha) + (int64_t)i * p.rows;
       const int srow = q * kQuad * kRowTile + lane;
       const half_t sclh = sv[min(srow, p.rows - 1)];
-      const half_t* orow[NC];
+      // operand rows: tile rows of v / z, or (XIN) lane's chunk of x row
+      // L/16 + 4j of the column block
+      const half_t* orow[XIN ? 4 * NC : NC];
+      if constexpr (XIN) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int t = min(t0 + 16 * c + c16, t1 - 1);
-        orow[c] = p.opnd + i * p.opnd_term + (int64_t)(t >> 4) * p.opnd_nkb * 2048 +
-                  (16 * g + (t & 15)) * 8;
+        for (int j = 0; j < 4 * NC; ++j) {
+          const int t = min(t0 + (lane >> 4) + 4 * j, t1 - 1);
+          orow[j] = p.x + (int64_t)t * p.ldx + 8 * c16;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int t = min(t0 + 16 * c + c16, t1 - 1);
+          orow[c] = p.opnd + i * p.opnd_term + (int64_t)(t >> 4) * p.opnd_nkb * 2048 +
+                    (16 * g + (t & 15)) * 8;
+        }
       }
+      const half_t* grow = XIN ? f.gamma + (int64_t)i * p.K + 8 * g : nullptr;
+      // XIN: LDS byte offsets of the lane's chunk writes (row L/16 + 4j,
+      // chunk L%16) and operand reads (step s, token column c: row 16c + c16,
+      // chunk 4s + g)
+      int wr[XIN ? 4 * NC : 1], rd[XIN ? 4 * NC : 1];
+      if constexpr (XIN) {
+#pragma unroll
+        for (int j = 0; j < 4 * NC; ++j) {
+          const int r = (lane >> 4) + 4 * j;
+          wr[j] = r * 256 + ((c16 ^ (r & 15)) << 4);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            rd[s * NC + c] = (16 * c + c16) * 256 + (((4 * s + g) ^ c16) << 4);
+      }
+      char* xarea = (char*)&xst[XIN ? wv : 0][0];
 
       v4f acc[4][NC];
 #pragma unroll
@@ -288,22 +403,39 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         // loads (clamped at the end), so each in-order wait covers exactly
         // the buffer about to be used.
         auto kb_of = [&](int j) { return kb0 + min(j, nkw - 1) * kst; };
-        Block<NC> buf[D];
+        auto load = [&](Block<NC, XIN>& B, int kb) {
+          if constexpr (XIN)
+            load_block<NC>(B, sq, orow, grow, kb);
+          else
+            load_block<NC>(B, sq, orow, kb);
+        };
+        Block<NC, XIN> buf[D];
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_block<NC>(buf[d], sq, orow, kb_of(d));
+        for (int d = 0; d < D; ++d) load(buf[d], kb_of(d));
         for (int j = 0; j < nkw; j += D) {
 #pragma unroll
           for (int d = 0; d < D; ++d) {
-            if (j + d < nkw) mma_block<NC>(acc, buf[d], p.msk16, one);
+            if (j + d < nkw) {
+              if constexpr (XIN) x_to_operand<NC>(buf[d], xarea, wr, rd);
+              mma_block<NC, XIN>(acc, buf[d], p.msk16, one);
+            }
             __builtin_amdgcn_sched_barrier(0);
-            load_block<NC>(buf[d], sq, orow, kb_of(j + d + D));
+            load(buf[d], kb_of(j + d + D));
           }
+        }
+      }
+      if constexpr (XIN) {
+        if (tail) {
+          Block<NC, true> B;
+          load_block_tail<NC>(B, sq, orow, grow, nfull, p.K - nfull * kColBlock, g, c16);
+          x_to_operand<NC>(B, xarea, wr, rd);
+          mma_block<NC, true>(acc, B, p.msk16, one);
         }
       }
 
       if (SPLITK) {
-        // fixed-order sum of the four waves' partial tiles; wave w finishes
-        // tiles w*NC .. w*NC + NC-1 (tile = h*NC + c)
+        // fixed-order sum of the waves' partial tiles; wave w finishes
+        // tiles w*TPW .. w*TPW + TPW-1 (tile = h*NC + c)
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
@@ -312,14 +444,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
       }
       if (active) {
         const float scl = srow < p.rows ? (float)sclh : 0.0f;
-        constexpr int NE = SPLITK ? NC : 4 * NC;
+        constexpr int NE = SPLITK ? TPW : 4 * NC;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-          const int tile = SPLITK ? wv * NC + e : e, h = tile / NC, c = tile % NC;
+          const int tile = SPLITK ? wv * TPW + e : e, h = tile / NC, c = tile % NC;
           v4f sum;
           if (SPLITK) {
-            sum = ((red[0][tile][lane] + red[1][tile][lane]) + red[2][tile][lane]) +
-                  red[3][tile][lane];
+            sum = red[0][tile][lane];
+#pragma unroll
+            for (int w = 1; w < NWV; ++w) sum += red[w][tile][lane];
           } else {
             sum = acc[h][c];
           }
@@ -382,6 +515,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 // operand: alpha_i[row] * (+-1) is exact in fp16 (the sign bits are XORed
 // into alpha's), so one fp32 accumulator per tile sums every term's products
 // and the epilogue only stores.
+constexpr int64_t kComputeUnits = 256;  // MI355X
 constexpr int kKregQG = 16;              // row quads per work item
 constexpr int kKregQPW = kKregQG / 4;     // per wave
 
@@ -550,6 +684,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 }
 
+// Whether a single-adapter stage takes 64-token column blocks.
+inline bool wide_blocks(const GemmParams& p) {
+  return p.nkb >= 4 && cdiv(p.T, 64) * p.nq >= 512;
+}
+
+// Whether a split-reduction stage runs 8 waves per workgroup: single
+// adapter, 32-token blocks and no more items than compute units.
+inline bool eight_waves(const GemmParams& p) {
+  return !p.multi && p.nkb >= 4 && !wide_blocks(p) && cdiv(p.T, 32) * p.nq <= kComputeUnits;
+}
+
+template <int STAGE, int NC, bool SPLITK, bool MULTI, bool XIN>
+hipError_t launch_k(const GemmParams& p, int64_t grid, bool wide, hipStream_t s) {
+  if constexpr (SPLITK && !MULTI && NC == 2) {  // 64-token blocks would spill at 8 waves
+    if (wide) {
+      hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK, MULTI, XIN, 8>), dim3((unsigned)grid), dim3(512),
+                         0, s, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK, MULTI, XIN, 4>), dim3((unsigned)grid), dim3(256), 0,
+                     s, p);
+  return hipGetLastError();
+}
+
 template <int STAGE, int NC, bool SPLITK>
 hipError_t launch_one(GemmParams p, hipStream_t s) {
   p.n_rg = SPLITK ? p.nq : (p.nq + 3) / 4;
@@ -561,17 +720,14 @@ hipError_t launch_one(GemmParams p, hipStream_t s) {
   // consecutive items cannot be mapped to one XCD
   p.xcd_remap = (!p.multi && grid == items && items % 8 == 0) ? 1 : 0;
   p.grid = (int32_t)grid;
-  if (p.multi)
-    hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
-  return hipGetLastError();
+  const bool wide = eight_waves(p);
+  if (p.multi) return launch_k<STAGE, NC, SPLITK, true, false>(p, grid, false, s);
+  if constexpr (STAGE == 1 && NC == 2) {
+    if (p.x != nullptr) return launch_k<1, NC, SPLITK, false, true>(p, grid, wide, s);
+  }
+  return launch_k<STAGE, NC, SPLITK, false, false>(p, grid, wide, s);
 }
 
-// Tokens per column block: 64 feeds each expanded sign operand to more
-// MFMAs, 32 doubles the number of work items when 64 would leave compute
-// units idle; the row-split variant (short reductions) and the multi-adapter
-// column blocks take 32.
 template <int STAGE>
 hipError_t launch_stage(GemmParams p, hipStream_t s) {
   if (STAGE == 2 && (int64_t)p.ell * p.nkb <= 2) {
@@ -589,7 +745,7 @@ hipError_t launch_stage(GemmParams p, hipStream_t s) {
   if (p.multi) {
     return split ? launch_one<STAGE, 2, true>(p, s) : launch_one<STAGE, 2, false>(p, s);
   }
-  if (split && cdiv(p.T, 64) * p.nq >= 512) {
+  if (wide_blocks(p)) {
     p.n_cb_host = (int32_t)cdiv(p.T, 64);
     return launch_one<STAGE, 4, true>(p, s);
   }
@@ -649,8 +805,20 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   p2.opnd = zt;
   p2.opnd_term = zt_term_halfs(a.R, a.T);
   p2.opnd_nkb = p2.nkb;
+  // Stage 1 reads x in place when every 8-entry chunk of x and gamma is a
+  // whole aligned 16-byte load (x and ldx are checked by the caller), with
+  // 32-token column blocks (64 would not fit the registers), and when each
+  // wave has at most 8 blocks of the reduction: passing x through LDS costs
+  // about 0.3 us per block, the prep launch it replaces about 3 us.
+  const int nwv1 = eight_waves(p1) ? 8 : 4;
+  const bool xin = !a.multi && a.M % 8 == 0 && (((uintptr_t)a.single.gamma) & 15u) == 0 &&
+                   !wide_blocks(p1) && cdiv(p1.nkb, nwv1) <= 8;
+  if (xin) {
+    p1.x = a.x;
+    p1.ldx = a.ldx;
+  }
 
-  if (a.phases & 1) {
+  if ((a.phases & 1) && !xin) {
     PrepVParams pv{};
     pv.x = a.x;
     pv.ldx = a.ldx;

@@ -65,7 +65,9 @@ typedef int32_t dbf_dtype;
                      adapters, the token runs) into ws
      DBF_RUN_STAGE1  z_i = beta_i * (B2 (gamma_i * x)) into ws
      DBF_RUN_STAGE2  y from z (the only phase that writes y)
-   On the large-T path each phase is one kernel launch. */
+   On the large-T path each phase is at most one kernel launch; with one
+   adapter, a short reduction over M (a multiple of 8) and gamma 16-byte
+   aligned, stage 1 reads x itself and DBF_RUN_PREP launches nothing. */
 #define DBF_RUN_PREP 8u
 #define DBF_RUN_STAGE1 16u
 #define DBF_RUN_STAGE2 32u

@@ -231,6 +231,43 @@ def test_signed_scales(shape, path):
     assert np.array_equal(got, ref(Li).astype(np.float32).astype(np.float64))
 
 
+@pytest.mark.parametrize("shape", [(136, 200, 520, 2, 70), (64, 130, 904, 1, 33),
+                                   (40, 72, 264, 1, 5), (40, 8448, 520, 1, 70)])
+def test_stage1_x_in_place_and_operand_tiles(shape):
+    """Large-T stage 1 reads x in place, with gamma folded into the expanded
+    signs, when M is a multiple of 8 and gamma is 16-byte aligned; a gamma
+    one element off alignment takes the gamma*x operand tiles instead.  Both
+    give the exact value on integers with signed unit gamma, and fp16
+    results within the bar.  M = 520 and 904 end in a partial 128-block,
+    taken by waves 4 and 7 of an 8-wave split reduction, and (R = 8448: more
+    work items than compute units) by wave 0 of a 4-wave one; M = 264 runs
+    unsplit."""
+    import dataclasses
+    N, R, M, ell, T = shape
+    rng = np.random.default_rng(98)
+
+    def misaligned(pl):
+        buf = torch.empty(pl.gamma.numel() + 1, dtype=torch.float16, device="cuda")
+        buf[1:] = pl.gamma.reshape(-1)
+        return dataclasses.replace(pl, gamma=buf[1:].view(pl.gamma.shape))
+
+    Li = synth.make_layer(N, R, M, ell, T, seed=99, alpha="ones", beta="ones", gamma="ones",
+                          x_kind="int3")
+    Li = dataclasses.replace(
+        Li, gamma=(Li.gamma * np.where(rng.random(Li.gamma.shape) < 0.5, -1, 1)).astype(np.float16))
+    want = ref(Li).astype(np.float32).astype(np.float64)
+    pl = H().upload(Li)
+    assert pl.gamma.data_ptr() % 16 == 0
+    for q in (pl, misaligned(pl)):
+        got = H().run_layer(Li, path="mfma", y_dtype=torch.float32, pl=q)
+        assert np.array_equal(got, want)
+    L = synth.make_layer(N, R, M, ell, T, seed=100)
+    pl = H().upload(L)
+    for q in (pl, misaligned(pl)):
+        err = oracle.max_norm_error(H().run_layer(L, path="mfma", pl=q), ref(L))
+        assert err <= TOL, err
+
+
 def test_paths_agree_on_integers():
     L = synth.make_layer(96, 200, 300, 2, 20, seed=9, alpha="ones", beta="ones", gamma="ones",
                          x_kind="int3")
