@@ -33,23 +33,13 @@ __device__ inline int floor_log2_pos(float m) {
   return (int)((__float_as_uint(m) >> 23) & 0xFFu) - 127;
 }
 
-// Round a (|a| < 256) to OCP e4m3 (3 mantissa bits, subnormal step 2^-9),
-// nearest-even.  Returns the code; q receives the rounded value.  The code
-// of a binade carry (mantissa 8 -> next exponent) follows from the encoding
-// being monotonic in the magnitude.
-__device__ inline uint32_t e4m3_rne(float a, float& q) {
-  const uint32_t sgn = (__float_as_uint(a) >> 31) << 7;
-  const float m = fabsf(a);
-  const int e = floor_log2_pos(m);
-  if (e < -6) {  // zero and the subnormal range
-    const float qn = __builtin_rintf(m * 512.0f);  // 0..8; 8 encodes 2^-6 (0x08)
-    q = __builtin_copysignf(qn * (1.0f / 512.0f), a);
-    return sgn | (uint32_t)qn;
-  }
-  const float qn = __builtin_rintf(__builtin_ldexpf(m, 3 - e));  // 8..16, m / 2^(e-3) exactly
-  q = __builtin_copysignf(__builtin_ldexpf(qn, e - 3), a);
-  return sgn | (((uint32_t)(e + 7) << 3) + (uint32_t)(qn - 8.0f));
-}
+// fp8 parts use the hardware conversion v_cvt_pk_fp8_f32: OCP e4m3 (3
+// mantissa bits, subnormal step 2^-9), round to nearest even, for the
+// scaled values |a| < 256 given here; v_cvt_f32_fp8 decodes a code exactly.
+// On gfx950 it agrees, code and value, with the direct definition (round
+// m / 2^(e-3), or m * 512 below 2^-6, to an integer, nearest even) on every
+// 2^-12 step of [-256, 256), which holds every tie, and on 8M random fp32
+// values.
 
 struct PrepParams {
   int64_t K, T, nkb;
@@ -125,11 +115,11 @@ __device__ inline void block_parts(float v0, float v1, Put&& put) {
     int s = mx > 0.0f ? floor_log2_pos(mx) - 7 : 0;  // scaled block max in [128, 256)
     s = s < -127 ? -127 : (s > 127 ? 127 : s);
     const float down = __builtin_ldexpf(1.0f, -s), up = __builtin_ldexpf(1.0f, s);
-    float q0, q1;
-    const uint32_t c0 = e4m3_rne(v0 * down, q0), c1 = e4m3_rne(v1 * down, q1);
+    const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(v0 * down, v1 * down, 0, false);
+    const float q0 = __builtin_amdgcn_cvt_f32_fp8(codes, 0), q1 = __builtin_amdgcn_cvt_f32_fp8(codes, 1);
     v0 -= q0 * up;  // exact: q*up is v rounded on a grid no finer than v's own
     v1 -= q1 * up;
-    put(part, (uint16_t)(c0 | (c1 << 8)), s);
+    put(part, (uint16_t)codes, s);
   }
 }
 
@@ -206,6 +196,8 @@ struct GemvParams {
   uint32_t sign_mask, fp4_one;  // 0x88888888, 0x22222222
   const uint32_t* opnd;
   const uint8_t* oscl;
+  const half_t* x;  // stage 1 building its own operand parts: x, stride ldx
+  int64_t ldx;
   float* z;
   int64_t ldz, zstride;
   void* y;
@@ -295,13 +287,27 @@ __device__ inline void gemv_epilogue(const GemvParams& p, const half_t* srow, v4
 }
 
 // Work item: (column block of <= tcb tokens, group of RTG row tiles).  The
-// four waves split the reduction into interleaved chunks of KC blocks; each
+// NW waves split the reduction into interleaved chunks of KC blocks; each
 // wave keeps the B operands of its chunk in registers and streams the sign
 // blocks of all RTG row tiles against them.  Partial tiles are summed across
 // waves in a fixed order through LDS.
-template <int STAGE, int RTG, int KC, bool MULTI>
-__global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
-  __shared__ v4f red[4][RTG][64];
+// PIN (one adapter, few columns): instead of reading operand parts built by
+// a prep launch, each wave requests its sign words, then builds the fp8 parts
+// of its own blocks from gamma_i * x (stage 1) or z (stage 2) with the prep
+// kernel's arithmetic (block_parts) into its LDS area, so the operands are
+// bit for bit those of the two-launch stage.  Every workgroup repeats this
+// for its blocks: worth it while a wave's chunk is a few blocks.
+constexpr int kPinColTokens = 2;                // PIN: ell * tokens per column block
+constexpr int kPinCols = kParts * kPinColTokens;  // PIN: live operand columns
+
+template <int STAGE, int RTG, int KC, bool MULTI, bool PIN = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
+  static_assert(!PIN || !MULTI, "operand parts are built in place for one adapter");
+  __shared__ v4f red[NW][RTG][64];
+  // PIN: the wave's parts, [block][column][128 bytes], and their scale codes
+  // (at most kPinCols live columns)
+  __shared__ uint8_t pin_b[PIN ? NW : 1][PIN ? KC * kPinCols * 128 : 1];
+  __shared__ uint8_t pin_s[PIN ? NW : 1][PIN ? KC * kPinCols : 1];
   static_assert(RTG % kQuad == 0, "row tiles come in quads");
   constexpr int RQ = RTG / kQuad;
   const int lane = threadIdx.x & 63;
@@ -359,35 +365,77 @@ __global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
     const int64_t nrt_here = (p.nrt - tile0) < RTG ? (p.nrt - tile0) : RTG;
     const int nq_here = (int)((nrt_here + kQuad - 1) / kQuad);
     bool first_chunk = true;
-    for (int64_t kbase = 0; kbase < p.nkb; kbase += 4 * KC) {
+    for (int64_t kbase = 0; kbase < p.nkb; kbase += NW * KC) {
       const int64_t kw0 = kbase + wv * KC;
       const int nk = (int)((p.nkb - kw0) < KC ? ((p.nkb - kw0) > 0 ? (p.nkb - kw0) : 0) : KC);
-      v8i bop[KC];
-      int bsc[KC];
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        const int64_t kb = kw0 + kk;
-        if (colv && kk < nk) {
-          const int64_t idx = (((ci * p.T + t0 + ct) * p.nkb + kb) * kParts + part) * 4 + g;
-          bop[kk] = *(gv8ip)(p.opnd + idx * 8);
-          bsc[kk] = p.oscl[idx];
-        } else {
-          bop[kk] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-          bsc[kk] = 127;
-        }
-      }
       // lane's 16 bytes of unit (quad, block): the A words of its 4 row tiles
       gv4up base = (gv4up)S + ((tile0 / kQuad) * p.nkb + kw0) * (kUnitWords / 4) + lane;
-      if (nk > 0) {
+      v8i bop[KC];
+      int bsc[KC];
+      v4u wd[RQ][KC];
+      auto load_signs = [&]() {
         // every sign word of this round is requested before the first MFMA:
         // RQ*KC 16-byte loads (16 KB per wave at RTG*KC = 64) in flight at once
-        v4u wd[RQ][KC];
 #pragma unroll
         for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
           for (int kk = 0; kk < KC; ++kk)
             wd[rq][kk] = (rq < nq_here && kk < nk) ? base[(rq * p.nkb + kk) * (kUnitWords / 4)]
                                                    : v4u{0u, 0u, 0u, 0u};
+      };
+      if constexpr (PIN) {
+        if (nk > 0) load_signs();
+        uint8_t* pb = pin_b[wv];
+        uint8_t* ps = pin_s[wv];
+        // lane l holds entries 2l, 2l+1 of the block; they meet adjacent
+        // operand bytes
+        const int boff = fp8_operand_byte(operand_k_of_col(2 * lane));
+        for (int kk = 0; kk < nk; ++kk) {
+          const int64_t k = (kw0 + kk) * kColBlock + 2 * lane;
+          for (int ci2 = 0; ci2 < p.ell; ++ci2)
+            for (int ct2 = 0; ct2 < ntok; ++ct2) {
+              const int64_t t = t0 + ct2;
+              float v0 = 0.0f, v1 = 0.0f;
+              if (STAGE == 1) {
+                const half_t* gi = f.gamma + ci2 * p.K;
+                const half_t* xr = p.x + t * p.ldx;
+                if (k < p.K) v0 = (float)gi[k] * (float)xr[k];
+                if (k + 1 < p.K) v1 = (float)gi[k + 1] * (float)xr[k + 1];
+              } else {
+                const float* zr = p.z + ci2 * p.zstride + t * p.ldz;
+                if (k < p.K) v0 = zr[k];
+                if (k + 1 < p.K) v1 = zr[k + 1];
+              }
+              const int col0 = kParts * (ci2 * ntok + ct2);
+              block_parts(v0, v1, [&](int pp, uint16_t code, int sc) {
+                *(uint16_t*)(pb + (kk * kPinCols + col0 + pp) * 128 + boff) = code;
+                if (lane == 0) ps[kk * kPinCols + col0 + pp] = (uint8_t)(sc + 127);
+              });
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+          const bool live = colv && kk < nk;
+          bop[kk] = live ? *(const v8i*)(pb + (kk * kPinCols + j) * 128 + g * 32)
+                         : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          bsc[kk] = live ? (int)ps[kk * kPinCols + j] : 127;
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+          const int64_t kb = kw0 + kk;
+          if (colv && kk < nk) {
+            const int64_t idx = (((ci * p.T + t0 + ct) * p.nkb + kb) * kParts + part) * 4 + g;
+            bop[kk] = *(gv8ip)(p.opnd + idx * 8);
+            bsc[kk] = p.oscl[idx];
+          } else {
+            bop[kk] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            bsc[kk] = 127;
+          }
+        }
+        if (nk > 0) load_signs();
+      }
+      if (nk > 0) {
 #pragma unroll
         for (int rq = 0; rq < RQ; ++rq) {
           v4f a4[4];
@@ -414,10 +462,12 @@ __global__ __launch_bounds__(256) void k_gemv_fp4(GemvParams p) {
     }
 
     __syncthreads();
-    for (int rt = wv; rt < RTG; rt += 4) {
+    for (int rt = wv; rt < RTG; rt += NW) {
       const int64_t tile = tile0 + rt;
       if (tile >= p.nrt) break;
-      const v4f sum = ((red[0][rt][lane] + red[1][rt][lane]) + red[2][rt][lane]) + red[3][rt][lane];
+      v4f sum = red[0][rt][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += red[w][rt][lane];
       const half_t* srow = (STAGE == 1 ? f.beta : f.alpha) + (int64_t)ci * p.rows;
       gemv_epilogue<STAGE>(p, srow, sum, tile, lane, g, part, colv, ci, ct, ntok, t0);
     }
@@ -1097,6 +1147,24 @@ constexpr int kStreamQPW = 2;  // row quads per wave and item
 constexpr int kStreamD = 8;    // sign loads in flight per lane
 constexpr int64_t kStreamLdsB = 32 * 1024;  // LDS budget for staged B operands
 
+// A stage that builds its own operand parts: 16 waves per workgroup, so a
+// wave's chunk is kc <= 2 blocks, one quad of row tiles per item.
+template <int STAGE>
+static hipError_t launch_gemv_pin(GemvParams p, int kc, hipStream_t s) {
+  p.nq = cdiv(p.nrt, kQuad);
+  p.n_rg = cdiv(p.nrt, kQuad);
+  const int64_t grid = p.n_cb_host * p.n_rg;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  p.grid = grid;
+  if (kc == 1)
+    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 1, false, true, 16>), dim3((unsigned)grid), dim3(1024),
+                       0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 2, false, true, 16>), dim3((unsigned)grid), dim3(1024),
+                       0, s, p);
+  return hipGetLastError();
+}
+
 template <int STAGE>
 static hipError_t launch_gemv_stage_any(GemvParams p, int64_t n_cb_est, int64_t n_cb_max,
                                         bool multi, hipStream_t s) {
@@ -1241,25 +1309,45 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
     }
   }
 
-  // stage 1: z = beta * (S2 . (gamma * x))
-  pp.K = a.M;
-  pp.nkb = cdiv(a.M, kColBlock);
-  pp.from_z = 0;
-  pp.opnd = (uint32_t*)(ws + L.p1o);
-  pp.oscl = (uint8_t*)(ws + L.p1s);
-  if (a.multi) {  // the first prep launch also builds the column blocks
-    pp.seg_cbl = (ColBlock*)(ws + L.cbl);
-    pp.seg_hdr = (WsHeader*)ws;
-    pp.seg_chunk = tcb;
-  }
-  if ((a.phases & 1) && (e = launch_prep(pp, s)) != hipSuccess) return e;
-  pp.seg_cbl = nullptr;
-  g1.opnd = pp.opnd;
-  g1.oscl = pp.oscl;
+  // With one adapter and at most two columns per operand part (ell *
+  // tokens <= 2, the decode case), a stage whose reduction is at most 32
+  // blocks builds its operand parts itself (0: a prep launch does).  Every
+  // workgroup builds the parts of the whole reduction, so this pays only
+  // while that is short: at 50 blocks (4 per wave) it measured slower than
+  // the prep launch.
+  auto pin_kc = [&](int64_t nkb) -> int {
+    const int64_t ntok = a.T < tcb ? a.T : tcb;
+    if (a.multi || (int64_t)a.ell * ntok > kPinColTokens) return 0;
+    return nkb <= 16 ? 1 : nkb <= 32 ? 2 : 0;
+  };
+  const int kc1 = pin_kc(g1.nkb), kc2 = pin_kc(g2.nkb);
 
-  if ((a.phases & 2) && (e = launch_gemv_stage_any<1>(g1, n_cb_est, n_cb_max, a.multi, s)) != hipSuccess)
-    return e;
+  // stage 1: z = beta * (S2 . (gamma * x))
+  if (kc1 > 0) {
+    g1.x = a.x;
+    g1.ldx = a.ldx;
+    if ((a.phases & 2) && (e = launch_gemv_pin<1>(g1, kc1, s)) != hipSuccess) return e;
+  } else {
+    pp.K = a.M;
+    pp.nkb = cdiv(a.M, kColBlock);
+    pp.from_z = 0;
+    pp.opnd = (uint32_t*)(ws + L.p1o);
+    pp.oscl = (uint8_t*)(ws + L.p1s);
+    if (a.multi) {  // the first prep launch also builds the column blocks
+      pp.seg_cbl = (ColBlock*)(ws + L.cbl);
+      pp.seg_hdr = (WsHeader*)ws;
+      pp.seg_chunk = tcb;
+    }
+    if ((a.phases & 1) && (e = launch_prep(pp, s)) != hipSuccess) return e;
+    pp.seg_cbl = nullptr;
+    g1.opnd = pp.opnd;
+    g1.oscl = pp.oscl;
+    if ((a.phases & 2) &&
+        (e = launch_gemv_stage_any<1>(g1, n_cb_est, n_cb_max, a.multi, s)) != hipSuccess)
+      return e;
+  }
   if (!(a.phases & 4)) return hipSuccess;
+  if (kc2 > 0) return launch_gemv_pin<2>(g2, kc2, s);
 
   // stage 2: y = sum_i alpha_i * (S1 . z_i)
   pp.K = a.R;

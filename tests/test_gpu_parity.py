@@ -268,6 +268,32 @@ def test_stage1_x_in_place_and_operand_tiles(shape):
         assert err <= TOL, err
 
 
+@pytest.mark.parametrize("shape", [(300, 130, 260, 1, 1), (4096, 2048, 4096, 1, 1),
+                                   (96, 200, 8000, 1, 2), (72, 40, 136, 2, 1), (1, 1, 1, 1, 1)])
+def test_decode_stages_build_parts(shape):
+    """With one adapter and ell * tokens <= 2 the small-T stages build their
+    fp8 operand parts themselves, from gamma*x and from z, with no prep
+    launch (reductions of 1..32 blocks: 1 or 2 blocks per wave; the
+    63-block stage 1 of M = 8000 takes a prep launch).  Exact
+    on integer inputs with unit scales, within the bar on fp16, and equal to
+    the result of the adapter-table call, whose prep launches build the same
+    parts, on integers."""
+    N, R, M, ell, T = shape
+    Li = synth.make_layer(N, R, M, ell, T, seed=101, alpha="ones", beta="ones", gamma="ones",
+                          x_kind="int3")
+    want = ref(Li).astype(np.float32).astype(np.float64)
+    got = H().run_layer(Li, path="gemv", y_dtype=torch.float32)
+    assert np.array_equal(got, want)
+    D = H().DeviceAdapters([Li])
+    ids = H().to_dev(np.zeros(T, np.int32))
+    y = D.forward(H().to_dev_rows(Li.x), ids, path="gemv", y=H().empty_rows(T, N, torch.float32))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), want)
+    L = synth.make_layer(N, R, M, ell, T, seed=102)
+    err = oracle.max_norm_error(H().run_layer(L, path="gemv"), ref(L))
+    assert err <= TOL, err
+
+
 def test_paths_agree_on_integers():
     L = synth.make_layer(96, 200, 300, 2, 20, seed=9, alpha="ones", beta="ones", gamma="ones",
                          x_kind="int3")
@@ -499,7 +525,7 @@ def test_segmentation_blocks(path, ell, chunk):
 
 # ------------------------------------------------------- split phases --
 @pytest.mark.parametrize("path", PATHS)
-@pytest.mark.parametrize("shape", [(300, 130, 260, 1, 37), (64, 16, 8, 3, 70)])
+@pytest.mark.parametrize("shape", [(300, 130, 260, 1, 37), (64, 16, 8, 3, 70), (96, 200, 8000, 1, 2)])
 def test_stage_split_equals_whole(shape, path):
     """The three phases run one at a time on one workspace give the whole
     call's result bit for bit, and the phases before stage 2 leave y
