@@ -49,6 +49,8 @@ __all__ = [
     "forward_rows",
     "forward_transposed",
     "forward_multi_adapter",
+    "backward",
+    "soft_sign_slope",
     "stage1",
     "fp16_rne",
     "max_norm_error",
@@ -185,6 +187,64 @@ def forward_transposed(gvec, S1, S2, alpha, beta, gamma) -> np.ndarray:
         p = (gv * a[i][None, :]) @ _f64(S1)
         p = p * b[i][None, :]
         out += (p @ _f64(S2)) * gm[i][None, :]
+    return out
+
+
+def soft_sign_slope(h, tau) -> np.ndarray:
+    """[LoRDBA] "Pipeline de Entrenamiento", step 3: the backward pass lets the
+    gradient through sign() with a soft-sign straight-through estimator under
+    a temperature schedule.  Reading (the page gives no formula): the surrogate
+    is tanh(h / tau), so d sign(h)/dh is replaced by its slope
+    (1 - tanh(h / tau)^2) / tau; tau > 0 is the current temperature (the
+    schedule belongs to the caller)."""
+    th = np.tanh(_f64(h) / float(tau))
+    return (1.0 - th * th) / float(tau)
+
+
+def backward(x, gout, S1, S2, alpha, beta, gamma, H1=None, H2=None, tau=None) -> dict:
+    """Backward pass of one layer for quantisation-aware training ([LoRDBA]
+    "Pipeline de Entrenamiento", steps 3 and 4: the sign carriers and the
+    scale vectors are trained together).  With G = dL/dY [T][N] for
+    Y = forward(x, ...), and for each term i (ascending) the forward's steps
+        V_i = X . gamma_i,  U_i = V_i S2^T,  Z_i = U_i . beta_i,  W_i = Z_i S1^T
+    and the adjoint's steps (the transposed product)
+        P_i = (G . alpha_i) S1,  Q_i = (P_i . beta_i) S2,
+    the chain rule on the update equation ("Arquitectura Central") gives
+        dalpha_i[n] = sum_t G[t,n] W_i[t,n]
+        dbeta_i[r]  = sum_t U_i[t,r] P_i[t,r]
+        dgamma_i[m] = sum_t X[t,m] Q_i[t,m]
+        dX  = sum_i Q_i . gamma_i                       [T][M]
+        dS1 = sum_i (G . alpha_i)^T Z_i                 [N][R]
+        dS2 = sum_i (P_i . beta_i)^T V_i                [R][M]
+    (the signs are shared by the terms, so their gradients sum over i).  With
+    latents H1, H2 (S = sign(H)) and a temperature tau, the straight-through
+    gradients are dH = dS * soft_sign_slope(H, tau).  Returns a dict of
+    float64 arrays; dalpha, dbeta, dgamma are [ell][*]."""
+    a, b, g = _terms(alpha, beta, gamma)
+    x, G = _f64(x), _f64(gout)
+    s1, s2 = _f64(S1), _f64(S2)
+    ell = a.shape[0]
+    out = {"dalpha": np.zeros_like(a), "dbeta": np.zeros_like(b), "dgamma": np.zeros_like(g),
+           "dx": np.zeros_like(x), "dS1": np.zeros_like(s1), "dS2": np.zeros_like(s2)}
+    for i in range(ell):
+        v = x * g[i][None, :]
+        u = v @ s2.T
+        z = u * b[i][None, :]
+        w = z @ s1.T
+        ga = G * a[i][None, :]
+        p = ga @ s1
+        pb = p * b[i][None, :]
+        q = pb @ s2
+        out["dalpha"][i] = (G * w).sum(axis=0)
+        out["dbeta"][i] = (u * p).sum(axis=0)
+        out["dgamma"][i] = (x * q).sum(axis=0)
+        out["dx"] += q * g[i][None, :]
+        out["dS1"] += ga.T @ z
+        out["dS2"] += pb.T @ v
+    if H1 is not None:
+        out["dH1"] = out["dS1"] * soft_sign_slope(H1, tau)
+    if H2 is not None:
+        out["dH2"] = out["dS2"] * soft_sign_slope(H2, tau)
     return out
 
 

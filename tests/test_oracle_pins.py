@@ -434,3 +434,185 @@ def test_pins_reject_mutants(mutant):
 
 def test_pins_reject_sign_convention_mutant():
     assert not pin_sign_convention(lambda h: np.where(np.asarray(h) <= 0, -1, 1).astype(np.int8))
+
+
+# ------------------------------------------------------------- backward ----
+# The layer's loss L = <G, Y> is linear in each scale vector, in x and in every
+# sign entry taken as a real number, so a central difference with step 1 is
+# exact up to fp64 rounding: it pins every gradient coordinate of ``backward``
+# to the (already pinned) forward product alone.
+
+def _bwd_case(seed=7, N=5, R=4, M=6, ell=2, T=3):
+    rng = np.random.default_rng(seed)
+    S1 = np.where(rng.random((N, R)) < 0.5, -1, 1).astype(np.int8)
+    S2 = np.where(rng.random((R, M)) < 0.5, -1, 1).astype(np.int8)
+    a, b, c = (rng.standard_normal((ell, n)) for n in (N, R, M))
+    x, G = rng.standard_normal((T, M)), rng.standard_normal((T, N))
+    return x, G, S1, S2, a, b, c
+
+
+def _loss(x, G, S1, S2, a, b, c):
+    return float((np.asarray(G) * oracle.forward(x, S1, S2, a, b, c)).sum())
+
+
+def pin_backward_finite_differences(bwd):
+    x, G, S1, S2, a, b, c = _bwd_case()
+    d = bwd(x, G, S1, S2, a, b, c)
+    args = {"x": x, "S1": S1.astype(float), "S2": S2.astype(float), "a": a, "b": b, "c": c}
+    names = {"x": "dx", "S1": "dS1", "S2": "dS2", "a": "dalpha", "b": "dbeta", "c": "dgamma"}
+    for key, out in names.items():
+        base = args[key]
+        fd = np.zeros_like(base)
+        def f(v):
+            kw = dict(args, **{key: v})
+            return _loss(kw["x"], G, kw["S1"], kw["S2"], kw["a"], kw["b"], kw["c"])
+
+        for idx in np.ndindex(base.shape):
+            hi, lo = base.copy(), base.copy()
+            hi[idx] += 1.0
+            lo[idx] -= 1.0
+            fd[idx] = (f(hi) - f(lo)) / 2.0
+        got = np.asarray(d[out])
+        if got.shape != fd.shape or np.abs(got - fd).max() > 1e-9 * max(1.0, np.abs(fd).max()):
+            return False
+    return True
+
+
+def pin_backward_dense(bwd):
+    """Matrix calculus on the dense update: with D_i = S1 diag(beta_i) S2
+    diag(gamma_i) (the term without alpha), Y = sum_i X D_i^T diag(alpha_i), so
+    dX = G dW, dalpha_i = colsum(G . (X D_i^T)),
+    dS1 = sum_i diag(alpha_i) G^T X diag(gamma_i) S2^T diag(beta_i),
+    dS2 = sum_i diag(beta_i) S1^T diag(alpha_i) G^T X diag(gamma_i),
+    dbeta_i[r] = (S1^T diag(alpha_i) G^T X diag(gamma_i) S2^T)[r][r],
+    dgamma_i[m] = (X^T G diag(alpha_i) S1 diag(beta_i) S2)[m][m]."""
+    x, G, S1, S2, a, b, c = _bwd_case(seed=8, N=6, R=3, M=5, ell=2, T=4)
+    d = bwd(x, G, S1, S2, a, b, c)
+    s1, s2 = S1.astype(float), S2.astype(float)
+    dw = oracle.delta_w(S1, S2, a, b, c)
+    ok = np.allclose(d["dx"], G @ dw, rtol=0, atol=1e-10)
+    dS1 = sum(np.diag(a[i]) @ G.T @ x @ np.diag(c[i]) @ s2.T @ np.diag(b[i]) for i in range(2))
+    dS2 = sum(np.diag(b[i]) @ s1.T @ np.diag(a[i]) @ G.T @ x @ np.diag(c[i]) for i in range(2))
+    ok &= np.allclose(d["dS1"], dS1, rtol=0, atol=1e-10)
+    ok &= np.allclose(d["dS2"], dS2, rtol=0, atol=1e-10)
+    for i in range(2):
+        Di = s1 @ np.diag(b[i]) @ s2 @ np.diag(c[i])
+        ok &= np.allclose(d["dalpha"][i], (G * (x @ Di.T)).sum(axis=0), rtol=0, atol=1e-10)
+        ok &= np.allclose(d["dbeta"][i],
+                          np.diag(s1.T @ np.diag(a[i]) @ G.T @ x @ np.diag(c[i]) @ s2.T),
+                          rtol=0, atol=1e-10)
+        ok &= np.allclose(d["dgamma"][i],
+                          np.diag(x.T @ G @ np.diag(a[i]) @ s1 @ np.diag(b[i]) @ s2),
+                          rtol=0, atol=1e-10)
+    return bool(ok)
+
+
+def pin_soft_slope(slope):
+    """The slope of tanh(h/tau): 1/tau at 0, even in h, (1 - 1/4)/tau where
+    tanh(h/tau) = 1/2, and a central difference of numpy's tanh elsewhere."""
+    ok = True
+    for tau in (0.05, 0.5, 2.0):
+        ok &= abs(float(slope(np.array(0.0), tau)) - 1.0 / tau) < 1e-12 / tau
+        h = tau * math.atanh(0.5)
+        ok &= abs(float(slope(np.array(h), tau)) - 0.75 / tau) < 1e-12 / tau
+        hs = np.linspace(-3 * tau, 3 * tau, 13)
+        ok &= np.allclose(slope(hs, tau), slope(-hs, tau), rtol=0, atol=1e-15)
+        eps = 1e-6 * tau
+        num = (np.tanh((hs + eps) / tau) - np.tanh((hs - eps) / tau)) / (2 * eps)
+        ok &= np.allclose(slope(hs, tau), num, rtol=1e-7, atol=0)
+    return bool(ok)
+
+
+def pin_backward_latents(bwd):
+    """With the soft signs S = tanh(H/tau) themselves in the product, the
+    straight-through formula dH = dS(S) * slope(H) is the exact gradient of
+    L(tanh(H1/tau), tanh(H2/tau)) with respect to H: a central difference
+    (step 1e-6) matches it."""
+    x, G, S1, S2, a, b, c = _bwd_case(seed=9, N=4, R=3, M=5, ell=2, T=3)
+    rng = np.random.default_rng(10)
+    tau = 0.7
+    H1, H2 = rng.standard_normal(S1.shape), rng.standard_normal(S2.shape)
+    soft = lambda H: np.tanh(H / tau)  # noqa: E731
+    d = bwd(x, G, soft(H1), soft(H2), a, b, c, H1=H1, H2=H2, tau=tau)
+    eps, ok = 1e-6, True
+    for which, H, key in ((1, H1, "dH1"), (2, H2, "dH2")):
+        fd = np.zeros_like(H)
+        for idx in np.ndindex(H.shape):
+            hi, lo = H.copy(), H.copy()
+            hi[idx] += eps
+            lo[idx] -= eps
+            if which == 1:
+                fd[idx] = (_loss(x, G, soft(hi), soft(H2), a, b, c)
+                           - _loss(x, G, soft(lo), soft(H2), a, b, c)) / (2 * eps)
+            else:
+                fd[idx] = (_loss(x, G, soft(H1), soft(hi), a, b, c)
+                           - _loss(x, G, soft(H1), soft(lo), a, b, c)) / (2 * eps)
+        ok &= np.allclose(d[key], fd, rtol=1e-6, atol=1e-7)
+    return bool(ok)
+
+
+def test_backward_finite_differences():
+    assert pin_backward_finite_differences(oracle.backward)
+
+
+def test_backward_dense_matrix_calculus():
+    assert pin_backward_dense(oracle.backward)
+
+
+def test_soft_sign_slope():
+    assert pin_soft_slope(oracle.soft_sign_slope)
+
+
+def test_backward_latents_match_soft_gradient():
+    assert pin_backward_latents(oracle.backward)
+
+
+def test_backward_integer_case_exact():
+    """Integer x and G with unit scales: every output is an integer (a sum of
+    products of integers), as the GPU bit-exactness tests assume."""
+    L = _rand_layer(11, 16, 8, 24, 1, 4, integer=True)
+    G = np.random.default_rng(12).integers(-3, 4, size=(4, 16)).astype(np.float64)
+    d = oracle.backward(L.x, G, L.S1, L.S2, L.alpha, L.beta, L.gamma)
+    for k in ("dx", "dalpha", "dbeta", "dgamma", "dS1", "dS2"):
+        assert np.array_equal(d[k], np.round(d[k])), k
+
+
+# Plausible slips in the backward; at least one pin must reject each.
+
+def _bmut_dgamma_without_beta(x, G, S1, S2, a, b, c, **kw):
+    d = oracle.backward(x, G, S1, S2, a, b, c, **kw)
+    d["dgamma"] = oracle.backward(x, G, S1, S2, a, np.ones_like(b), c, **kw)["dgamma"]
+    return d
+
+
+def _bmut_dS2_unscaled(x, G, S1, S2, a, b, c, **kw):
+    d = oracle.backward(x, G, S1, S2, a, b, c, **kw)
+    a2, b2, c2 = (np.atleast_2d(v) for v in (a, b, c))
+    d["dS2"] = sum(((np.asarray(G) * a2[i]) @ np.asarray(S1, float)).T @ np.asarray(x)
+                   for i in range(a2.shape[0]))
+    return d
+
+
+def _bmut_dS1_transposed_scales(x, G, S1, S2, a, b, c, **kw):
+    return oracle.backward(x, G, S1, S2, np.roll(np.atleast_2d(a), 1, axis=0), b, c, **kw) | {
+        k: v for k, v in oracle.backward(x, G, S1, S2, a, b, c, **kw).items() if k != "dS1"}
+
+
+def _bmut_slope_without_tau(x, G, S1, S2, a, b, c, H1=None, H2=None, tau=None):
+    d = oracle.backward(x, G, S1, S2, a, b, c)
+    if H1 is not None:
+        d["dH1"] = d["dS1"] * (1 - np.tanh(H1 / tau) ** 2)
+        d["dH2"] = d["dS2"] * (1 - np.tanh(H2 / tau) ** 2)
+    return d
+
+
+@pytest.mark.parametrize("mutant", [_bmut_dgamma_without_beta, _bmut_dS2_unscaled,
+                                    _bmut_dS1_transposed_scales, _bmut_slope_without_tau])
+def test_backward_pins_reject_mutants(mutant):
+    results = [pin_backward_finite_differences(mutant), pin_backward_dense(mutant),
+               pin_backward_latents(mutant)]
+    assert not all(results)
+
+
+def test_soft_slope_pin_rejects_mutant():
+    assert not pin_soft_slope(lambda h, tau: 1.0 - np.tanh(np.asarray(h) / tau) ** 2)
