@@ -6,8 +6,10 @@ N = M = 4096, R = 2048, ell = 1, Bernoulli signs, log-normal fp16 scales,
 x ~ N(0,1) fp16 (synthetic, seeded).  One step is one ``dbf_forward`` call
 over a batch of T = 256 tokens (the prefill case, matrix-core path); the same
 JSON line also reports the decode case (T = 1, the sign-GEMV path), a grouped
-decode over 256 distinct layers in one dispatch, and the 64-adapter serving
-batch (T = 2048, R = 64, ell = 2, Zipf ids).
+decode over 256 distinct layers in one dispatch, the 64-adapter serving batch
+(T = 2048, R = 64, ell = 2, Zipf ids), the layer's QAT backward at T = 256
+(every gradient and the soft-sign straight-through latent gradients), the
+transposed product, and every configuration's single call.
 
 Every timed call reads factors that are not in any cache: calls rotate over
 distinct device copies of the layer whose total size exceeds twice the 256 MB
@@ -15,11 +17,11 @@ Infinity Cache.  Times come from HIP events on the stream the library
 launches on.  Prints ONE JSON line on stdout.
 
 The roofline object is for the dominant kernel of the timed call: each of the
-three phases is also timed alone (DBF_RUN_PREP / DBF_RUN_STAGE1 /
-DBF_RUN_STAGE2, one kernel each on this path; 64 calls captured in a HIP
-graph and replayed between HIP events, so the host's launch rate does not
-set the time), and the slower of the two matrix-core stages is reported
-against the fp16 matrix-core peak.  Its HBM traffic comes from the rocprofv3 FETCH_SIZE /
+two launches is also timed alone (DBF_RUN_STAGE1 / DBF_RUN_STAGE2; stage 1
+reads x in place on this layer, so DBF_RUN_PREP launches nothing; 64 calls
+captured in a HIP graph and replayed between HIP events, so the host's launch
+rate does not set the time), and the slower of the two matrix-core stages is
+reported against the fp16 matrix-core peak.  Its HBM traffic comes from the rocprofv3 FETCH_SIZE /
 WRITE_SIZE summary committed under profiles/ (scaled by what the counters
 read for a device copy of known size), and is reported only while the kernel
 source still matches the one the counters were taken on.
@@ -432,6 +434,43 @@ def main():
             "transpose_signs_us": tt_ * 1e6, "parity_err": errT,
         }
         log(f"transposed T=256: {tT * 1e6:.2f} us/call (sign transposes {tt_ * 1e6:.1f} us)")
+
+    # ------------------------------ QAT backward, attention layer T=256 --
+    if want("backward"):
+        rngb = np.random.default_rng(8)
+        gB = torch.as_tensor(oracle.fp16_rne(rngb.standard_normal((T, N_))).astype(np.float16)).to(dev)
+        H1 = torch.as_tensor(rngb.standard_normal((N_, R_)), dtype=torch.float32).to(dev)
+        H2 = torch.as_tensor(rngb.standard_normal((R_, M_)), dtype=torch.float32).to(dev)
+        tau = 0.5
+        B1ts = [dbf.dbf_transpose_signs(b, N_, R_) for b in B1s]
+        B2ts = [dbf.dbf_transpose_signs(b, R_, M_) for b in B2s]
+        wsB = torch.empty(dbf.dbf_backward_workspace_bytes(N_, R_, M_, 1, T), dtype=torch.uint8,
+                          device=dev)
+
+        def callB(i):
+            k = i % n_inst
+            return dbf.dbf_backward(x256, gB, B1s[k], B2s[k], B1ts[k], B2ts[k], pl.alpha, pl.beta,
+                                    pl.gamma, N_, R_, M_, sign_grads=True, H1=H1, H2=H2, tau=tau,
+                                    ws=wsB)
+
+        gotB = callB(0)
+        torch.cuda.synchronize()
+        t_o = time.perf_counter()
+        refB = oracle.backward(L.x, gB.cpu().numpy(), L.S1, L.S2, L.alpha, L.beta, L.gamma,
+                               H1=H1.cpu().numpy(), H2=H2.cpu().numpy(), tau=tau)
+        t_o = time.perf_counter() - t_o
+        errB = {k: oracle.max_norm_error(v.float().cpu().numpy(), refB[k]) for k, v in gotB.items()}
+        nB = max(args.steps // 4, 20)
+        tB = time_calls(callB, nB, 3) / nB
+        flB = 3 * alg_flops(N_, R_, M_, 1, T)  # U, P, W, Q and the two sign gradients
+        out["backward_T256"] = {
+            "T": T, "us_per_call": tB * 1e6, "tokens_per_s": T / tB,
+            "achieved_TFLOPs": flB / tB / 1e12, "mfma_frac": flB / tB / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "alg_flops_per_call": flB, "outputs": sorted(gotB), "parity_err": errB,
+            "oracle_s_per_call": t_o,
+        }
+        log(f"backward T=256: {tB * 1e6:.1f} us/call, {flB / tB / 1e12:.1f} TFLOP/s, "
+            f"max err {max(errB.values()):.2e}; fp64 oracle {t_o:.2f} s")
 
     # ------------------------------------------------ copy calibration --
     if args.copy_calibration:

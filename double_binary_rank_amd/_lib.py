@@ -42,6 +42,8 @@ EXPORTS = (
     "dbf_workspace_bytes",
     "dbf_forward",
     "dbf_forward_multi_adapter",
+    "dbf_backward_workspace_bytes",
+    "dbf_backward",
 )
 
 
@@ -113,6 +115,21 @@ lib.dbf_forward_multi_adapter.argtypes = [
     _vp, _sz, _vp,  # ws, ws_bytes, stream
 ]
 
+lib.dbf_backward_workspace_bytes.restype = _i32
+lib.dbf_backward_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, ctypes.POINTER(_sz)]
+lib.dbf_backward.restype = _i32
+lib.dbf_backward.argtypes = [
+    _vp, _i64, _vp, _i64,  # x, ldx, g, ldg
+    _vp, _vp, _vp, _vp,  # B1, B2, B1t, B2t
+    _vp, _vp, _vp,  # alpha, beta, gamma
+    _i64, _i64, _i64, _i32, _i64,  # N, R, M, ell, T
+    _vp, _i64, _i32,  # dx, lddx, dx_type
+    _vp, _vp, _vp,  # dalpha, dbeta, dgamma
+    _vp, _vp,  # dS1, dS2
+    _vp, _vp, ctypes.c_float, _vp, _vp,  # H1, H2, tau, dH1, dH2
+    _vp, _sz, _vp,  # ws, ws_bytes, stream
+]
+
 
 def status_string(status: int) -> str:
     return lib.dbf_status_string(status).decode()
@@ -136,4 +153,11 @@ def packed_bytes(rows: int, cols: int) -> int:
 def workspace_bytes(N: int, R: int, M: int, ell: int, T: int) -> int:
     out = _sz(0)
     check(lib.dbf_workspace_bytes(N, R, M, ell, T, ctypes.byref(out)), "dbf_workspace_bytes")
+    return out.value
+
+
+def backward_workspace_bytes(N: int, R: int, M: int, ell: int, T: int) -> int:
+    out = _sz(0)
+    check(lib.dbf_backward_workspace_bytes(N, R, M, ell, T, ctypes.byref(out)),
+          "dbf_backward_workspace_bytes")
     return out.value

@@ -24,6 +24,8 @@ __all__ = [
     "dbf_workspace_bytes",
     "dbf_forward",
     "dbf_forward_multi_adapter",
+    "dbf_backward_workspace_bytes",
+    "dbf_backward",
     "PackedLayer",
     "pointer_table",
 ]
@@ -152,6 +154,51 @@ def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torc
     return y
 
 
+def dbf_backward_workspace_bytes(N: int, R: int, M: int, ell: int, T: int) -> int:
+    return _lib.backward_workspace_bytes(N, R, M, ell, T)
+
+
+def dbf_backward(x: torch.Tensor, g: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor,
+                 B1t: torch.Tensor, B2t: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                 gamma: torch.Tensor, N: int, R: int, M: int, *, dx_dtype=torch.float16,
+                 sign_grads: bool = False, H1: torch.Tensor | None = None,
+                 H2: torch.Tensor | None = None, tau: float | None = None,
+                 ws: torch.Tensor | None = None, stream=None) -> dict:
+    """Gradients of one layer given the output gradient g = dL/dy [T][N] for
+    the input x [T][M] (fp16): dx [T][M] (dx_dtype), dalpha [ell][N], dbeta
+    [ell][R], dgamma [ell][M] (fp32); with ``sign_grads`` also dS1 [N][R] and
+    dS2 [R][M]; with fp32 latents H1 [N][R] / H2 [R][M] and a temperature tau,
+    the straight-through gradients dH1 / dH2.  B1t and B2t are the packed
+    transposes (``dbf_transpose_signs``)."""
+    T = x.shape[0]
+    ell = alpha.shape[0] if alpha.dim() == 2 else 1
+    dev = x.device
+    ldx, ldg = _row_major(x, "x"), _row_major(g, "g")
+    dx = torch.empty((T, M), dtype=dx_dtype, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": dx, "dalpha": torch.empty((ell, N), **f32), "dbeta": torch.empty((ell, R), **f32),
+           "dgamma": torch.empty((ell, M), **f32)}
+    if sign_grads:
+        out["dS1"] = torch.empty((N, R), **f32)
+        out["dS2"] = torch.empty((R, M), **f32)
+    for name, H, shape in (("dH1", H1, (N, R)), ("dH2", H2, (R, M))):
+        if H is not None:
+            if H.dtype != torch.float32 or tuple(H.shape) != shape or not H.is_contiguous():
+                raise ValueError(f"{name[1:]} must be contiguous fp32 of shape {shape}")
+            out[name] = torch.empty(shape, **f32)
+    need = dbf_backward_workspace_bytes(N, R, M, ell, T)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    check(lib.dbf_backward(
+        _ptr(x), ldx, _ptr(g), ldg, _ptr(B1), _ptr(B2), _ptr(B1t), _ptr(B2t), _ptr(alpha),
+        _ptr(beta), _ptr(gamma), N, R, M, ell, T, _ptr(dx), M, _DTYPE[dx_dtype],
+        _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dgamma"]), _ptr(out.get("dS1")),
+        _ptr(out.get("dS2")), _ptr(H1), _ptr(H2), 0.0 if tau is None else float(tau),
+        _ptr(out.get("dH1")), _ptr(out.get("dH2")), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "dbf_backward")
+    return out
+
+
 def pointer_table(tensors, device) -> torch.Tensor:
     """Device int64 array of the tensors' device addresses."""
     return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
@@ -218,6 +265,20 @@ class PackedLayer:
     def forward(self, x: torch.Tensor, **kw) -> torch.Tensor:
         return dbf_forward(x, self.B1, self.B2, self.alpha, self.beta, self.gamma, self.N, self.R,
                            self.M, **kw)
+
+    def transposed_signs(self):
+        """Packed S1^T (R x N) and S2^T (M x R), built once per layer."""
+        if getattr(self, "_signs_t", None) is None:
+            self._signs_t = (dbf_transpose_signs(self.B1, self.N, self.R),
+                             dbf_transpose_signs(self.B2, self.R, self.M))
+        return self._signs_t
+
+    def backward(self, x: torch.Tensor, g: torch.Tensor, **kw) -> dict:
+        """Gradients for the output gradient g of ``forward(x)``; see
+        ``dbf_backward``."""
+        B1t, B2t = self.transposed_signs()
+        return dbf_backward(x, g, self.B1, self.B2, B1t, B2t, self.alpha, self.beta, self.gamma,
+                            self.N, self.R, self.M, **kw)
 
     def transposed(self) -> "PackedLayer":
         """The layer of dW^T = sum_i diag(gamma_i) S2^T diag(beta_i) S1^T

@@ -199,4 +199,82 @@ dbf_status dbf_forward_multi_adapter(const void* x, int64_t ldx, int64_t T, cons
   return hip_status(dbf::launch_forward(a, (hipStream_t)stream));
 }
 
+dbf_status dbf_backward_workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T,
+                                        size_t* bytes) {
+  if (N <= 0 || R <= 0 || M <= 0 || ell < 1 || T <= 0 || bytes == nullptr)
+    return DBF_ERR_INVALID_ARG;
+  if (N > DBF_MAX_DIM || R > DBF_MAX_DIM || M > DBF_MAX_DIM || T > DBF_MAX_DIM)
+    return DBF_ERR_INVALID_ARG;
+  *bytes = dbf::bwd_layout(N, R, M, ell, T).total;
+  return DBF_OK;
+}
+
+dbf_status dbf_backward(const void* x, int64_t ldx, const void* g, int64_t ldg, const uint32_t* B1,
+                        const uint32_t* B2, const uint32_t* B1t, const uint32_t* B2t,
+                        const void* alpha, const void* beta, const void* gamma, int64_t N,
+                        int64_t R, int64_t M, int32_t ell, int64_t T, void* dx, int64_t lddx,
+                        dbf_dtype dx_type, float* dalpha, float* dbeta, float* dgamma, float* dS1,
+                        float* dS2, const float* H1, const float* H2, float tau, float* dH1,
+                        float* dH2, void* ws, size_t ws_bytes, void* stream) {
+  if (N <= 0 || R <= 0 || M <= 0 || ell < 1 || T <= 0) return DBF_ERR_INVALID_ARG;
+  if (N > DBF_MAX_DIM || R > DBF_MAX_DIM || M > DBF_MAX_DIM || T > DBF_MAX_DIM)
+    return DBF_ERR_INVALID_ARG;
+  // the feature-major tiles index the tokens of all terms with 32 bits
+  if ((int64_t)ell * cdiv(T, 128) * 128 > INT32_MAX) return DBF_ERR_INVALID_ARG;
+  if (x == nullptr || g == nullptr || B1 == nullptr || B2 == nullptr || B1t == nullptr ||
+      B2t == nullptr || alpha == nullptr || beta == nullptr || gamma == nullptr || dx == nullptr ||
+      dalpha == nullptr || dbeta == nullptr || dgamma == nullptr)
+    return DBF_ERR_INVALID_ARG;
+  if ((H1 == nullptr) != (dH1 == nullptr) || (H2 == nullptr) != (dH2 == nullptr))
+    return DBF_ERR_INVALID_ARG;
+  if ((H1 != nullptr || H2 != nullptr) && !(tau > 0.0f && tau < 3.0e38f)) return DBF_ERR_INVALID_ARG;
+  if (dx_type != DBF_F16 && dx_type != DBF_F32) return DBF_ERR_INVALID_ARG;
+  if (ldx < M || ldg < N || lddx < M) return DBF_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(g) || (ldx % 8) != 0 || (ldg % 8) != 0)
+    return DBF_ERR_ALIGNMENT;
+  if (!aligned16(B1) || !aligned16(B2) || !aligned16(B1t) || !aligned16(B2t))
+    return DBF_ERR_ALIGNMENT;
+  if ((((uintptr_t)alpha) | ((uintptr_t)beta) | ((uintptr_t)gamma)) & 1u) return DBF_ERR_ALIGNMENT;
+  if ((((uintptr_t)dx) & (dx_type == DBF_F32 ? 3u : 1u)) != 0) return DBF_ERR_ALIGNMENT;
+  if ((((uintptr_t)dalpha) | ((uintptr_t)dbeta) | ((uintptr_t)dgamma) | ((uintptr_t)dS1) |
+       ((uintptr_t)dS2) | ((uintptr_t)H1) | ((uintptr_t)H2) | ((uintptr_t)dH1) | ((uintptr_t)dH2)) &
+      3u)
+    return DBF_ERR_ALIGNMENT;
+  if (ws == nullptr || ws_bytes < dbf::bwd_layout(N, R, M, ell, T).total) return DBF_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DBF_ERR_ALIGNMENT;
+
+  dbf::BackwardArgs a{};
+  a.x = (const dbf::half_t*)x;
+  a.ldx = ldx;
+  a.g = (const dbf::half_t*)g;
+  a.ldg = ldg;
+  a.B1 = B1;
+  a.B2 = B2;
+  a.B1t = B1t;
+  a.B2t = B2t;
+  a.alpha = (const dbf::half_t*)alpha;
+  a.beta = (const dbf::half_t*)beta;
+  a.gamma = (const dbf::half_t*)gamma;
+  a.N = N;
+  a.R = R;
+  a.M = M;
+  a.T = T;
+  a.ell = ell;
+  a.dx = dx;
+  a.lddx = lddx;
+  a.dx_f32 = (dx_type == DBF_F32);
+  a.dalpha = dalpha;
+  a.dbeta = dbeta;
+  a.dgamma = dgamma;
+  a.dS1 = dS1;
+  a.dS2 = dS2;
+  a.H1 = H1;
+  a.H2 = H2;
+  a.tau = tau;
+  a.dH1 = dH1;
+  a.dH2 = dH2;
+  a.ws = ws;
+  return hip_status(dbf::launch_backward(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

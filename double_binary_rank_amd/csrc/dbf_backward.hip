@@ -1,0 +1,440 @@
+// Backward pass of one layer for quantisation-aware training (LoRDBA
+// summary, section 2, "Pipeline de Entrenamiento", steps 3 and 4: sign
+// carriers and scale vectors are trained together, the gradient passing
+// sign() through a soft-sign straight-through estimator).
+//
+// With G = dL/dy [T][N] and, per term i, the forward's steps V_i = x.gamma_i,
+// U_i = V_i S2^T, Z_i = U_i.beta_i, W_i = Z_i S1^T and the adjoint's steps
+// P_i = (G.alpha_i) S1, Q_i = (P_i.beta_i) S2 (the chain rule on the update
+// equation, "Arquitectura Central"):
+//   dalpha_i = colsum(G . W_i),  dbeta_i = colsum(U_i . P_i),
+//   dgamma_i = colsum(x . Q_i),  dx = sum_i Q_i . gamma_i,
+//   dS1 = sum_i (G.alpha_i)^T Z_i,  dS2 = sum_i (P_i.beta_i)^T V_i,
+//   dH = dS * (1 - tanh(H/tau)^2) / tau  (soft sign tanh(h/tau)).
+//
+// Launch sequence (one stream):
+//   1. fp16 operand tiles of V_i and of G.alpha_i (k_prep_v);
+//   2. U_i = S2 V_i and P_i = S1^T (G.alpha_i): the large-T sign-product
+//      kernel with raw fp32 output (k_gemm stage 3), P from the transposed
+//      packing of S1;
+//   3. tiles of Z_i = beta_i.U_i and of beta_i.P_i (k_tiles_f32);
+//   4. W_i = S1 Z_i and Q_i = S2^T (beta_i.P_i), again stage 3;
+//   5. the column dot products (k_coldot, k_colsum) and dx (k_dx);
+//   6. dS1, dS2 as dense fp16 matrix-core contractions over the tokens of
+//      all terms (k_dense_tn) from feature-major tiles (k_tiles_fm), with the
+//      straight-through slope applied in the same epilogue.
+// Every matrix-core operand is rounded to fp16 once from its exact fp32
+// value, as on the forward large-T path; accumulation is fp32.
+#include "dbf_device.h"
+#include "dbf_launch.h"
+
+namespace dbf {
+
+namespace {
+
+typedef const DBF_GLOBAL v8h* gv8hp;
+
+// Token-major tiles (16 tokens x 128 reduction entries; entry (t, k) at
+// half ((t/16 * nkb + k/128) * 4 + (k%128)/32) * 512 + (16 * (k/8 % 4) +
+// t%16) * 8 + k%8 of its term) of fp16(scale_i[k] * src_i[t][k]), src fp32
+// [ell][T][ld].  One thread per (term, token tile, 128-block, lane); it
+// writes the lane's 8 entries of each of the 4 steps.
+struct TilesF32Params {
+  const float* src;
+  int64_t ld, src_term;
+  int32_t T, K, ell, nkb;
+  int64_t n_units;
+  const half_t* scale;  // [ell][K]
+  half_t* out;
+  int64_t out_term;
+};
+
+__global__ __launch_bounds__(256) void k_tiles_f32(TilesF32Params p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (u >= p.n_units) return;
+  const int kb = (int)(u % p.nkb);
+  const int64_t r = u / p.nkb;
+  const int ntt = (p.T + 15) >> 4;
+  const int i = (int)(r / ntt), tt = (int)(r - (int64_t)i * ntt);
+  const int g = lane >> 4, t = tt * 16 + (lane & 15);
+  const float* row = p.src + i * p.src_term + (int64_t)t * p.ld;
+  const half_t* sc = p.scale + (int64_t)i * p.K;
+  half_t* out = p.out + i * p.out_term + ((int64_t)tt * p.nkb + kb) * 2048 + lane * 8;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int k0 = kb * kColBlock + 32 * s + 8 * g;
+    v8h o = {};
+    if (t < p.T)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k0 + e < p.K) o[e] = (half_t)((float)sc[k0 + e] * row[k0 + e]);
+    *(v8h*)(out + s * 512) = o;
+  }
+}
+
+// Feature-major tiles for the sign gradients: the rows are the C features and
+// the reduction runs over kappa = i * Tp + t (Tp = T rounded up to 128), each
+// tile 16 features x 128 kappa in the same lane order, so a wave's 1 KB of a
+// step is one MFMA operand.  Value fp16(scale_i[c] * src_i[t][c]); src is fp16
+// [T][ld] shared by the terms (src16) or fp32 [ell][T][ld] (src32).  One
+// thread per (feature tile, 128-block, step, lane): 8 tokens of one feature.
+struct TilesFmParams {
+  const half_t* src16;
+  const float* src32;
+  int64_t ld, src_term;
+  int32_t T, C, Tp, nkb;  // nkb = ell * Tp / 128
+  int64_t n_threads;
+  const half_t* scale;  // [ell][C]
+  half_t* out;
+};
+
+__global__ __launch_bounds__(256) void k_tiles_fm(TilesFmParams p) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= p.n_threads) return;
+  const int lane = (int)(id & 63), s = (int)((id >> 6) & 3);
+  const int64_t blk = id >> 8;  // tile-major: (feature tile, 128-block)
+  const int kb = (int)(blk % p.nkb);
+  const int ct = (int)(blk / p.nkb);
+  const int c = ct * 16 + (lane & 15);
+  const int kappa = kb * kColBlock + 32 * s + 8 * (lane >> 4);
+  const int i = kappa / p.Tp, t0 = kappa - i * p.Tp;
+  v8h o = {};
+  if (c < p.C) {
+    const float sc = (float)p.scale[(int64_t)i * p.C + c];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = t0 + e;
+      if (t < p.T) {
+        const float v = p.src16 != nullptr ? (float)p.src16[(int64_t)t * p.ld + c]
+                                           : p.src32[i * p.src_term + (int64_t)t * p.ld + c];
+        o[e] = (half_t)(sc * v);
+      }
+    }
+  }
+  *(v8h*)(p.out + blk * 2048 + s * 512 + lane * 8) = o;
+}
+
+// d_i[c] = sum_t a_i[t][c] * b_i[t][c] in fp32, deterministic: workgroup
+// (column group of 64, token chunk of kColdotChunk) has 4 waves, wave w
+// summing tokens w, w+4, ... of the chunk for 64 columns; the 4 partials are
+// added in wave order and stored per chunk, and k_colsum adds the chunks in
+// ascending order.  a is fp16 [T][lda] shared by the terms (a16) or fp32 per
+// term (a32); b is fp32 [ell][T][ldb].
+struct ColdotParams {
+  const half_t* a16;
+  const float* a32;
+  int64_t lda, a_term;
+  const float* b;
+  int64_t ldb, b_term;
+  int32_t T, C, ell, n_cg;  // n_cg: 64-column groups per term
+  float* part;              // [chunks][ell][C]
+  float* d;                 // [ell][C]
+};
+
+__global__ __launch_bounds__(256) void k_coldot(ColdotParams p) {
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int cg = blockIdx.x % p.n_cg, i = (blockIdx.x / p.n_cg) % p.ell;
+  const int chunk = blockIdx.x / (p.n_cg * p.ell);
+  const int c = cg * 64 + lane;
+  float acc = 0.0f;
+  if (c < p.C) {
+    const float* b = p.b + i * p.b_term + c;
+    const int t1 = min(p.T, (chunk + 1) * kColdotChunk);
+    if (p.a16 != nullptr) {
+      const half_t* a = p.a16 + c;
+      for (int t = chunk * kColdotChunk + wv; t < t1; t += 4)
+        acc += (float)a[(int64_t)t * p.lda] * b[(int64_t)t * p.ldb];
+    } else {
+      const float* a = p.a32 + i * p.a_term + c;
+      for (int t = chunk * kColdotChunk + wv; t < t1; t += 4)
+        acc += a[(int64_t)t * p.lda] * b[(int64_t)t * p.ldb];
+    }
+  }
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0 && c < p.C)
+    p.part[((int64_t)chunk * p.ell + i) * p.C + c] =
+        ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+}
+
+__global__ __launch_bounds__(256) void k_colsum(const float* part, int32_t n_chunks, int64_t n,
+                                                float* d) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= n) return;
+  float acc = 0.0f;
+  for (int k = 0; k < n_chunks; ++k) acc += part[(int64_t)k * n + id];
+  d[id] = acc;
+}
+
+// dx[t][m] = sum_i gamma_i[m] * Q_i[t][m] (terms ascending), stored as fp16
+// (nearest even) or fp32.
+struct DxParams {
+  const float* q;
+  int64_t ldq, q_term;
+  const half_t* gamma;
+  int32_t T, M, ell;
+  void* dx;
+  int64_t lddx;
+  int32_t f32;
+};
+
+__global__ __launch_bounds__(256) void k_dx(DxParams p) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= (int64_t)p.T * p.M) return;
+  const int64_t t = id / p.M, m = id - t * p.M;
+  float acc = 0.0f;
+  for (int i = 0; i < p.ell; ++i)
+    acc += (float)p.gamma[(int64_t)i * p.M + m] * p.q[i * p.q_term + t * p.ldq + m];
+  if (p.f32)
+    ((float*)p.dx)[t * p.lddx + m] = acc;
+  else
+    ((half_t*)p.dx)[t * p.lddx + m] = (half_t)acc;
+}
+
+// Slope of the soft sign at y = h / tau, written as sech^2(y) =
+// 4 e / (1 + e)^2 with e = exp(-2 |y|) (no cancellation for large |y|; e
+// underflows to 0 there): one hardware exp2 and one reciprocal.
+__device__ inline float sech2(float y) {
+  const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * fabsf(y));  // -2 / ln 2
+  const float d = 1.0f + e;
+  return 4.0f * e * __builtin_amdgcn_rcpf(d * d);
+}
+
+// C[a][b] = sum_kappa A[a][kappa] * B[b][kappa] from feature-major tiles, on
+// v_mfma_f32_16x16x32_f16.  A workgroup owns 128 A-rows x 128 B-rows, each
+// of its 4 waves 64 x 64 (4 x 4 tiles) over the whole reduction; tiles past
+// the matrices read as zero.  Epilogue: C (OUT) and the straight-through
+// gradient C * sech^2(H * inv_tau) * inv_tau (STE).  A wave whose 64 x 64
+// block lies inside both matrices stores without per-element checks.
+struct DenseParams {
+  const half_t* A;
+  const half_t* B;
+  int32_t nta, ntb, nkb;  // 16-row tiles of A and B, 128-blocks of the reduction
+  int32_t rows_a, rows_b, n_ga;  // n_ga: 128-row groups of A
+  float* out;
+  const float* H;
+  float inv_tau;
+  float* dH;  // all three [rows_a][rows_b]
+};
+
+template <bool OUT, bool STE>
+__global__ __launch_bounds__(256) void k_dense_tn(DenseParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c16 = lane & 15;
+  const int ga = blockIdx.x % p.n_ga, gb = blockIdx.x / p.n_ga;
+  const int ta0 = (ga * 2 + (wv & 1)) * 4, tb0 = (gb * 2 + (wv >> 1)) * 4;
+  v4f acc[4][4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[h][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < p.nkb; ++kb) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v8h a[4], b[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int ta = ta0 + h, tb = tb0 + h;
+        a[h] = ta < p.nta ? *(gv8hp)(p.A + ((int64_t)ta * p.nkb + kb) * 2048 + s * 512 + lane * 8)
+                          : v8h{};
+        b[h] = tb < p.ntb ? *(gv8hp)(p.B + ((int64_t)tb * p.nkb + kb) * 2048 + s * 512 + lane * 8)
+                          : v8h{};
+      }
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[h][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[h], b[c], acc[h][c], 0, 0, 0);
+    }
+  }
+  // lane (g, c16), register v of tile (h, c): row 4g + v of A-tile h, row c16
+  // of B-tile c
+  float* __restrict__ out = p.out;
+  float* __restrict__ dH = p.dH;
+  const float* __restrict__ Hm = p.H;
+  const int64_t ldo = p.rows_b;
+  // interior waves (all 16 tiles inside both matrices) store through one row
+  // pointer per register, the 4 column tiles at 64-byte immediate offsets
+  const bool interior = (ta0 + 4) * 16 <= p.rows_a && (tb0 + 4) * 16 <= p.rows_b;
+  if (interior) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t o = (int64_t)((ta0 + h) * 16 + 4 * g + v) * ldo + tb0 * 16 + c16;
+        float hv[4];
+        if (STE)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) hv[c] = Hm[o + 16 * c];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float val = acc[h][c][v];
+          if (OUT) out[o + 16 * c] = val;
+          if (STE) dH[o + 16 * c] = val * (sech2(hv[c] * p.inv_tau) * p.inv_tau);
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int rb = (tb0 + c) * 16 + c16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ra = (ta0 + h) * 16 + 4 * g + v;
+        if (ra < p.rows_a && rb < p.rows_b) {
+          const int64_t o = (int64_t)ra * ldo + rb;
+          const float val = acc[h][c][v];
+          if (OUT) out[o] = val;
+          if (STE) dH[o] = val * (sech2(Hm[o] * p.inv_tau) * p.inv_tau);
+        }
+      }
+    }
+}
+
+hipError_t launch_tiles_f32(const float* src, int64_t ld, int64_t src_term, int64_t T, int64_t K,
+                            int32_t ell, const half_t* scale, half_t* out, hipStream_t s) {
+  TilesF32Params p{};
+  p.src = src;
+  p.ld = ld;
+  p.src_term = src_term;
+  p.T = (int32_t)T;
+  p.K = (int32_t)K;
+  p.ell = ell;
+  p.nkb = (int32_t)cdiv(K, kColBlock);
+  p.n_units = (int64_t)ell * cdiv(T, 16) * p.nkb;
+  p.scale = scale;
+  p.out = out;
+  p.out_term = zt_term_halfs(K, T);
+  hipLaunchKernelGGL(k_tiles_f32, dim3((unsigned)cdiv(p.n_units, 4)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiles_fm(const half_t* src16, const float* src32, int64_t ld, int64_t src_term,
+                           int64_t T, int64_t C, int32_t ell, const half_t* scale, half_t* out,
+                           hipStream_t s) {
+  TilesFmParams p{};
+  p.src16 = src16;
+  p.src32 = src32;
+  p.ld = ld;
+  p.src_term = src_term;
+  p.T = (int32_t)T;
+  p.C = (int32_t)C;
+  p.Tp = (int32_t)(cdiv(T, 128) * 128);
+  p.nkb = (int32_t)(bwd_kf(ell, T) / 128);
+  p.n_threads = cdiv(C, 16) * p.nkb * 256;
+  p.scale = scale;
+  p.out = out;
+  hipLaunchKernelGGL(k_tiles_fm, dim3((unsigned)cdiv(p.n_threads, 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_coldot(const half_t* a16, const float* a32, int64_t lda, int64_t a_term,
+                         const float* b, int64_t ldb, int64_t b_term, int64_t T, int64_t C,
+                         int32_t ell, float* part, float* d, hipStream_t s) {
+  const int32_t n_cg = (int32_t)cdiv(C, 64);
+  const int64_t n_chunks = cdiv(T, kColdotChunk);
+  ColdotParams p{a16, a32, lda, a_term, b, ldb, b_term, (int32_t)T, (int32_t)C, ell, n_cg, part, d};
+  const int64_t grid = (int64_t)n_cg * ell * n_chunks;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_coldot, dim3((unsigned)grid), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)ell * C;
+  hipLaunchKernelGGL(k_colsum, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, (const float*)part,
+                     (int32_t)n_chunks, n, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense(const half_t* A, const half_t* B, int64_t rows_a, int64_t rows_b,
+                        int64_t kf, float* out, const float* H, float tau, float* dH,
+                        hipStream_t s) {
+  DenseParams p{};
+  p.A = A;
+  p.B = B;
+  p.nta = (int32_t)cdiv(rows_a, 16);
+  p.ntb = (int32_t)cdiv(rows_b, 16);
+  p.nkb = (int32_t)(kf / 128);
+  p.rows_a = (int32_t)rows_a;
+  p.rows_b = (int32_t)rows_b;
+  p.n_ga = (int32_t)cdiv(rows_a, 128);
+  p.out = out;
+  p.H = H;
+  p.inv_tau = H != nullptr ? 1.0f / tau : 0.0f;
+  p.dH = dH;
+  const int64_t grid = (int64_t)p.n_ga * cdiv(rows_b, 128);
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (out != nullptr && H != nullptr)
+    hipLaunchKernelGGL((k_dense_tn<true, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  else if (out != nullptr)
+    hipLaunchKernelGGL((k_dense_tn<true, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_dense_tn<false, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
+  const BwdLayout L = bwd_layout(a.N, a.R, a.M, a.ell, a.T);
+  char* ws = (char*)a.ws;
+  half_t* vt = (half_t*)(ws + L.vt);
+  half_t* gt = (half_t*)(ws + L.gt);
+  float* u = (float*)(ws + L.u);
+  float* pp = (float*)(ws + L.p);
+  half_t* zt = (half_t*)(ws + L.zt);
+  half_t* pt = (half_t*)(ws + L.pt);
+  float* w = (float*)(ws + L.w);
+  float* q = (float*)(ws + L.q);
+  const int64_t T = a.T, N = a.N, R = a.R, M = a.M;
+  const int32_t ell = a.ell;
+  hipError_t e;
+#define DBF_TRY(x) \
+  if ((e = (x)) != hipSuccess) return e
+  const int64_t lr = bwd_ld(R), ln = bwd_ld(N), lm = bwd_ld(M);
+  // 1-2: U_i = S2 (gamma_i x), P_i = S1^T (alpha_i G)
+  DBF_TRY(launch_tiles_f16(a.x, a.ldx, T, M, ell, a.gamma, vt, s));
+  DBF_TRY(launch_sign_product(a.B2, R, M, ell, T, vt, u, lr, s));
+  DBF_TRY(launch_tiles_f16(a.g, a.ldg, T, N, ell, a.alpha, gt, s));
+  DBF_TRY(launch_sign_product(a.B1t, R, N, ell, T, gt, pp, lr, s));
+  // 3-4: W_i = S1 (beta_i U_i), Q_i = S2^T (beta_i P_i)
+  DBF_TRY(launch_tiles_f32(u, lr, T * lr, T, R, ell, a.beta, zt, s));
+  DBF_TRY(launch_tiles_f32(pp, lr, T * lr, T, R, ell, a.beta, pt, s));
+  DBF_TRY(launch_sign_product(a.B1, N, R, ell, T, zt, w, ln, s));
+  DBF_TRY(launch_sign_product(a.B2t, M, R, ell, T, pt, q, lm, s));
+  // 5: scale gradients and dx
+  float* part = (float*)(ws + L.part);
+  DBF_TRY(launch_coldot(a.g, nullptr, a.ldg, 0, w, ln, T * ln, T, N, ell, part, a.dalpha, s));
+  DBF_TRY(launch_coldot(nullptr, u, lr, T * lr, pp, lr, T * lr, T, R, ell, part, a.dbeta, s));
+  DBF_TRY(launch_coldot(a.x, nullptr, a.ldx, 0, q, lm, T * lm, T, M, ell, part, a.dgamma, s));
+  {
+    DxParams p{q, lm, T * lm, a.gamma, (int32_t)T, (int32_t)M, ell, a.dx, a.lddx, a.dx_f32 ? 1 : 0};
+    hipLaunchKernelGGL(k_dx, dim3((unsigned)cdiv(T * M, 256)), dim3(256), 0, s, p);
+    DBF_TRY(hipGetLastError());
+  }
+  // 6: sign gradients over the tokens of every term
+  const int64_t kf = bwd_kf(ell, T);
+  if (a.dS1 != nullptr || a.dH1 != nullptr) {
+    half_t* gf = (half_t*)(ws + L.gf);
+    half_t* zf = (half_t*)(ws + L.zf);
+    DBF_TRY(launch_tiles_fm(a.g, nullptr, a.ldg, 0, T, N, ell, a.alpha, gf, s));
+    DBF_TRY(launch_tiles_fm(nullptr, u, lr, T * lr, T, R, ell, a.beta, zf, s));
+    DBF_TRY(launch_dense(gf, zf, N, R, kf, a.dS1, a.H1, a.tau, a.dH1, s));
+  }
+  if (a.dS2 != nullptr || a.dH2 != nullptr) {
+    half_t* pf = (half_t*)(ws + L.pf);
+    half_t* vf = (half_t*)(ws + L.vf);
+    DBF_TRY(launch_tiles_fm(nullptr, pp, lr, T * lr, T, R, ell, a.beta, pf, s));
+    DBF_TRY(launch_tiles_fm(a.x, nullptr, a.ldx, 0, T, M, ell, a.gamma, vf, s));
+    DBF_TRY(launch_dense(pf, vf, R, M, kf, a.dS2, a.H2, a.tau, a.dH2, s));
+  }
+#undef DBF_TRY
+  return hipSuccess;
+}
+
+}  // namespace dbf

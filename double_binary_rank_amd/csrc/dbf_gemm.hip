@@ -26,6 +26,10 @@
 // The operand tiles put entry 32s + 8g + e of token c16 in lane 16g + c16 of
 // step s, so both operands see the same k and no lane exchange is needed.
 //
+// Stage 3 (the backward pass's sign products) is stage 2 without output
+// scales: each term's raw fp32 product S * opnd_i is written to its own
+// [T][ldy] block of y.
+//
 // Work item: a column block of 16*NC tokens and either one row quad (64
 // rows) whose reduction the NWV waves split (SPLITK: interleaved 128-blocks,
 // partial tiles summed in a fixed order through LDS; 8 waves when there are
@@ -62,6 +66,7 @@ struct GemmParams {
   int64_t z_term;
   void* y;
   int64_t ldy;
+  int64_t y_term;  // stage 3: floats per term of the output
   Factors single;
   const ColBlock* cbl;
   const WsHeader* hdr;
@@ -351,9 +356,12 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
       // row scales of this wave's quad (lane L: row 64q + L), loaded first
       // and kept as loaded (converting here would wait for the load); lanes
       // fetch the ones they need with a cross-lane read at the end
-      const half_t* sv = (STAGE == 1 ? f.beta : f.alpha) + (int64_t)i * p.rows;
       const int srow = q * kQuad * kRowTile + lane;
-      const half_t sclh = sv[min(srow, p.rows - 1)];
+      half_t sclh = (half_t)1.0f;  // stage 3 scales nothing
+      if constexpr (STAGE != 3) {
+        const half_t* sv = (STAGE == 1 ? f.beta : f.alpha) + (int64_t)i * p.rows;
+        sclh = sv[min(srow, p.rows - 1)];
+      }
       // operand rows: tile rows of v / z, or (XIN) lane's chunk of x row
       // L/16 + 4j of the column block
       const half_t* orow[XIN ? 4 * NC : NC];
@@ -469,6 +477,11 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
               *(v4h*)(p.z + i * p.z_term + tile_off(t, r0, p.z_nkb)) =
                   v4h{(half_t)(sum[0] * sc[0]), (half_t)(sum[1] * sc[1]),
                       (half_t)(sum[2] * sc[2]), (half_t)(sum[3] * sc[3])};
+          } else if (STAGE == 3) {
+            if (t < t1 && r0 < p.rows) {
+              const float o[4] = {sum[0], sum[1], sum[2], sum[3]};
+              store4((float*)p.y + i * p.y_term, p.ldy, true, t, r0, p.rows, o);
+            }
           } else {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -754,6 +767,46 @@ hipError_t launch_stage(GemmParams p, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_tiles_f16(const half_t* src, int64_t ld, int64_t T, int64_t K, int32_t ell,
+                            const half_t* scale, half_t* out, hipStream_t s) {
+  PrepVParams pv{};
+  pv.x = src;
+  pv.ldx = ld;
+  pv.T = (int32_t)T;
+  pv.M = (int32_t)K;
+  pv.ell = ell;
+  pv.nkb = (int32_t)cdiv(K, kColBlock);
+  pv.n_units = (int64_t)ell * cdiv(T, 16) * pv.nkb;
+  pv.gamma = scale;
+  pv.v = out;
+  pv.v_term = zt_term_halfs(K, T);
+  if (pv.n_units > INT32_MAX - 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_prep_v<false>, dim3((unsigned)cdiv(pv.n_units, 4)), dim3(256), 0, s, pv);
+  return hipGetLastError();
+}
+
+hipError_t launch_sign_product(const uint32_t* S, int64_t rows, int64_t K, int32_t ell, int64_t T,
+                               const half_t* tiles, float* out, int64_t ldo, hipStream_t s) {
+  GemmParams p{};
+  p.rows = (int32_t)rows;
+  p.K = (int32_t)K;
+  p.T = (int32_t)T;
+  p.ell = ell;
+  p.nq = (int32_t)cdiv(rows, kRowTile * kQuad);
+  p.nkb = (int32_t)cdiv(K, kColBlock);
+  p.msk16 = 0x80008000u;
+  p.one16 = 0x3C003C00u;
+  p.y_f32 = 1;
+  p.y = out;
+  p.ldy = ldo;
+  p.y_term = T * ldo;
+  p.single.B1 = S;
+  p.opnd = tiles;
+  p.opnd_term = zt_term_halfs(K, T);
+  p.opnd_nkb = p.nkb;
+  return launch_stage<3>(p, s);
+}
 
 hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   const WsLayout L = ws_layout(a.N, a.R, a.M, a.ell, a.T);

@@ -105,5 +105,89 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s);
 // column blocks hold at most kGemmChunk tokens of one adapter
 constexpr int kGemmChunk = 32;
 hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s);
+// Token-major fp16 operand tiles (the large-T layout above) of
+// scale_i[k] * src[t][k] for each of ell terms (src fp16 [T][ld], shared).
+hipError_t launch_tiles_f16(const half_t* src, int64_t ld, int64_t T, int64_t K, int32_t ell,
+                            const half_t* scale, half_t* out, hipStream_t s);
+// Raw per-term sign products out[i][t][r] = sum_k S[r][k] * tiles_i[t][k]
+// (fp32, [ell][T][ldo]); S is a packed rows x K sign matrix.
+hipError_t launch_sign_product(const uint32_t* S, int64_t rows, int64_t K, int32_t ell, int64_t T,
+                               const half_t* tiles, float* out, int64_t ldo, hipStream_t s);
+
+// ------------------------------------------------------------ backward ----
+struct BackwardArgs {
+  const half_t* x;  // [T][ldx]
+  int64_t ldx;
+  const half_t* g;  // upstream gradient dL/dy, [T][ldg]
+  int64_t ldg;
+  const uint32_t* B1;   // N x R, packed along R
+  const uint32_t* B2;   // R x M, packed along M
+  const uint32_t* B1t;  // R x N, packed along N (transpose of B1)
+  const uint32_t* B2t;  // M x R, packed along R (transpose of B2)
+  const half_t* alpha;
+  const half_t* beta;
+  const half_t* gamma;
+  int64_t N, R, M, T;
+  int32_t ell;
+  void* dx;
+  int64_t lddx;
+  bool dx_f32;
+  float* dalpha;  // [ell][N]
+  float* dbeta;   // [ell][R]
+  float* dgamma;  // [ell][M]
+  float* dS1;     // [N][R] or null
+  float* dS2;     // [R][M] or null
+  const float* H1;  // latents [N][R], [R][M], or null
+  const float* H2;
+  float tau;
+  float* dH1;
+  float* dH2;
+  void* ws;
+};
+
+// Byte offsets of the backward workspace regions.
+struct BwdLayout {
+  size_t vt, gt, u, p, zt, pt, w, q, gf, zf, pf, vf, part, total;
+};
+
+// Tokens per chunk of the column dot products (partial sums per chunk, then
+// summed over the chunks in order).
+constexpr int kColdotChunk = 32;
+
+// Reduction length of the feature-major tiles: the ell terms' tokens, each
+// term padded to a multiple of 128.
+inline int64_t bwd_kf(int32_t ell, int64_t T) { return (int64_t)ell * cdiv(T, 128) * 128; }
+// Row stride of the fp32 intermediates U, P ([T][R]), W ([T][N]), Q ([T][M]):
+// a multiple of 4 floats, for the 16-byte stores of the sign-product kernel.
+inline int64_t bwd_ld(int64_t cols) { return cdiv(cols, 4) * 4; }
+
+inline BwdLayout bwd_layout(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T) {
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const int64_t kf = bwd_kf(ell, T);
+  L.vt = take((size_t)ell * zt_term_halfs(M, T) * sizeof(half_t));
+  L.gt = take((size_t)ell * zt_term_halfs(N, T) * sizeof(half_t));
+  L.u = take((size_t)ell * T * bwd_ld(R) * sizeof(float));
+  L.p = take((size_t)ell * T * bwd_ld(R) * sizeof(float));
+  L.zt = take((size_t)ell * zt_term_halfs(R, T) * sizeof(half_t));
+  L.pt = take((size_t)ell * zt_term_halfs(R, T) * sizeof(half_t));
+  L.w = take((size_t)ell * T * bwd_ld(N) * sizeof(float));
+  L.q = take((size_t)ell * T * bwd_ld(M) * sizeof(float));
+  L.gf = take((size_t)cdiv(N, 16) * kf * 16 * sizeof(half_t));
+  L.zf = take((size_t)cdiv(R, 16) * kf * 16 * sizeof(half_t));
+  L.pf = take((size_t)cdiv(R, 16) * kf * 16 * sizeof(half_t));
+  L.vf = take((size_t)cdiv(M, 16) * kf * 16 * sizeof(half_t));
+  const int64_t cmax = N > R ? (N > M ? N : M) : (R > M ? R : M);
+  L.part = take((size_t)cdiv(T, kColdotChunk) * ell * cmax * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 
 }  // namespace dbf

@@ -151,9 +151,11 @@ dbf_status dbf_workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int
  * (with DBF_ACCUMULATE: y += ...).  Inputs as described at the top.
  * Precision: fp32 accumulation.  On the small-T path gamma_i*x (exact in
  * fp32) and the R-vector beta_i*u stay fp32 up to the matrix-core operand
- * encoding (see the design notes); on the large-T path the matrix-core
- * operands gamma_i*x and beta_i*u are rounded to fp16.  The fp16 output is
- * rounded to nearest-even and overflows to +-inf.
+ * encoding (three e4m3 parts per value, one power-of-two scale per 128
+ * values); on the large-T path beta_i*u is rounded to fp16, and gamma_i*x
+ * too unless stage 1 reads x in place (then gamma is folded into the signs
+ * and the products are exact).  The fp16 output is rounded to nearest-even
+ * and overflows to +-inf.
  * Alignment: x, y, B1, B2 and ws 16-byte aligned; ldx a multiple of 8;
  * ldy a multiple of 8 (fp16 y) or 4 (fp32 y).
  * T == 0 is a successful no-op (x, y and ws may then be NULL).
@@ -188,6 +190,54 @@ dbf_status dbf_forward_multi_adapter(const void* x, int64_t ldx, int64_t T, cons
                                      int64_t N, int64_t R, int64_t M, int32_t ell, void* y,
                                      int64_t ldy, dbf_dtype y_type, uint32_t flags, void* ws,
                                      size_t ws_bytes, void* stream);
+
+/*
+ * Workspace bytes needed by dbf_backward for these sizes.
+ * Errors: INVALID_ARG if N, R, M <= 0 (or above DBF_MAX_DIM), ell < 1,
+ * T <= 0 or bytes == NULL.
+ */
+dbf_status dbf_backward_workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T,
+                                        size_t* bytes);
+
+/*
+ * Backward pass of one layer for quantisation-aware training (LoRDBA
+ * summary, section 2, "Pipeline de Entrenamiento", steps 3-4: the sign
+ * carriers B = sign(H) and the scale vectors are trained together; the
+ * gradient passes sign() through a soft-sign straight-through estimator
+ * with a temperature).  With g = dL/dy [T][N] for y = dbf_forward(x), per
+ * term i: V_i = x.gamma_i, U_i = V_i B2^T, Z_i = U_i.beta_i,
+ * W_i = Z_i B1^T, P_i = (g.alpha_i) B1, Q_i = (P_i.beta_i) B2; then
+ *   dalpha_i[n] = sum_t g[t][n] W_i[t][n]     dalpha [ell][N] fp32
+ *   dbeta_i[r]  = sum_t U_i[t][r] P_i[t][r]   dbeta  [ell][R] fp32
+ *   dgamma_i[m] = sum_t x[t][m] Q_i[t][m]     dgamma [ell][M] fp32
+ *   dx = sum_i Q_i.gamma_i                    dx [T][lddx], dx_type F16|F32
+ *   dS1 = sum_i (g.alpha_i)^T Z_i             [N][R] fp32, row-major, or NULL
+ *   dS2 = sum_i (P_i.beta_i)^T V_i            [R][M] fp32, row-major, or NULL
+ *   dH1 = dS1 * (1 - tanh(H1/tau)^2) / tau    with latents H1 [N][R], H2
+ *   dH2 = dS2 * (1 - tanh(H2/tau)^2) / tau    [R][M] (fp32, row-major)
+ * (reading of the estimator: the soft sign is tanh(h/tau); tau > 0 is the
+ * caller's current temperature).  H1 and dH1 are both given or both NULL,
+ * likewise H2 and dH2; dS1/dS2 may be NULL whether or not dH is wanted.
+ *   x [T][ldx], g [T][ldg] fp16; B1, B2 packed as for dbf_forward; B1t and
+ *   B2t the packed transposes (dbf_transpose_signs of B1 as N x R, of B2 as
+ *   R x M); alpha, beta, gamma [ell][*] fp16.
+ * Precision: fp32 accumulation; every matrix-core operand (V, g.alpha, Z,
+ * P.beta) is rounded to fp16 once.  Outputs are written, not accumulated.
+ * All device memory is the caller's; work is asynchronous on `stream`.
+ * Alignment: x, g, B1, B2, B1t, B2t and ws 16-byte aligned; ldx and ldg
+ * multiples of 8; fp32 outputs and latents 4-byte aligned.
+ * Errors: INVALID_ARG (null required pointer, sizes <= 0 or above
+ * DBF_MAX_DIM, ell * T too large, ld below the width, unpaired H/dH, tau
+ * not positive and finite, bad dtype), ALIGNMENT, WORKSPACE (ws_bytes below
+ * dbf_backward_workspace_bytes), HIP.
+ */
+dbf_status dbf_backward(const void* x, int64_t ldx, const void* g, int64_t ldg, const uint32_t* B1,
+                        const uint32_t* B2, const uint32_t* B1t, const uint32_t* B2t,
+                        const void* alpha, const void* beta, const void* gamma, int64_t N,
+                        int64_t R, int64_t M, int32_t ell, int64_t T, void* dx, int64_t lddx,
+                        dbf_dtype dx_type, float* dalpha, float* dbeta, float* dgamma, float* dS1,
+                        float* dS2, const float* H1, const float* H2, float tau, float* dH1,
+                        float* dH2, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

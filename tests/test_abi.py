@@ -159,3 +159,57 @@ def test_pack_rejects():
     assert L.dbf_pack_signs(A, _lib.DBF_F32, 4, 4, 4, MIS, None) == _lib.DBF_ERR_ALIGNMENT
     assert L.dbf_unpack_signs(MIS, 4, 4, A, 4, None) == _lib.DBF_ERR_ALIGNMENT
     assert L.dbf_unpack_signs(A, 4, 4, A, 3, None) == _lib.DBF_ERR_INVALID_ARG
+
+
+def _bwd(**kw):
+    a = dict(x=A, ldx=64, g=A, ldg=32, B1=A, B2=A, B1t=A, B2t=A, alpha=A, beta=A, gamma=A,
+             N=32, R=16, M=64, ell=1, T=4, dx=A, lddx=64, dx_type=_lib.DBF_F16, dalpha=A,
+             dbeta=A, dgamma=A, dS1=None, dS2=None, H1=None, H2=None, tau=0.0, dH1=None,
+             dH2=None, ws=A, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.dbf_backward(*a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(T=0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(ell=0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(M=(1 << 30) + 1), _lib.DBF_ERR_INVALID_ARG),
+    (dict(ell=1 << 20, T=1 << 12), _lib.DBF_ERR_INVALID_ARG),
+    (dict(g=None), _lib.DBF_ERR_INVALID_ARG),
+    (dict(B2t=None), _lib.DBF_ERR_INVALID_ARG),
+    (dict(dgamma=None), _lib.DBF_ERR_INVALID_ARG),
+    (dict(dx=None), _lib.DBF_ERR_INVALID_ARG),
+    (dict(H1=A), _lib.DBF_ERR_INVALID_ARG),            # latent without its output
+    (dict(dH2=A), _lib.DBF_ERR_INVALID_ARG),           # output without its latent
+    (dict(H1=A, dH1=A, tau=0.0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(H1=A, dH1=A, tau=-1.0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(H1=A, dH1=A, tau=float("inf")), _lib.DBF_ERR_INVALID_ARG),
+    (dict(dx_type=_lib.DBF_I8), _lib.DBF_ERR_INVALID_ARG),
+    (dict(ldx=63), _lib.DBF_ERR_INVALID_ARG),
+    (dict(ldg=31), _lib.DBF_ERR_INVALID_ARG),
+    (dict(lddx=10), _lib.DBF_ERR_INVALID_ARG),
+    (dict(x=MIS), _lib.DBF_ERR_ALIGNMENT),
+    (dict(ldg=36), _lib.DBF_ERR_ALIGNMENT),
+    (dict(B1t=MIS), _lib.DBF_ERR_ALIGNMENT),
+    (dict(beta=A + 1), _lib.DBF_ERR_ALIGNMENT),
+    (dict(dS1=A + 2), _lib.DBF_ERR_ALIGNMENT),
+    (dict(dx=A + 2, dx_type=_lib.DBF_F32), _lib.DBF_ERR_ALIGNMENT),
+    (dict(ws=None), _lib.DBF_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), _lib.DBF_ERR_WORKSPACE),
+    (dict(ws=MIS), _lib.DBF_ERR_ALIGNMENT),
+])
+def test_backward_rejects(kw, want):
+    assert _bwd(**kw) == want
+
+
+def test_backward_workspace_bytes():
+    out = ctypes.c_size_t(0)
+    assert L.dbf_backward_workspace_bytes(32, 16, 64, 1, 4, ctypes.byref(out)) == _lib.DBF_OK
+    assert out.value > 0
+    small = out.value
+    assert L.dbf_backward_workspace_bytes(32, 16, 64, 2, 300, ctypes.byref(out)) == _lib.DBF_OK
+    assert out.value > small
+    for bad in ((0, 16, 64, 1, 4), (32, 16, 64, 0, 4), (32, 16, 64, 1, 0)):
+        assert L.dbf_backward_workspace_bytes(*bad, ctypes.byref(out)) == _lib.DBF_ERR_INVALID_ARG
+    assert L.dbf_backward_workspace_bytes(32, 16, 64, 1, 4, None) == _lib.DBF_ERR_INVALID_ARG

@@ -564,3 +564,77 @@ def test_stage_split_multi_adapter(path):
 def dbf_ws(N, R, M, ell, T):
     import double_binary_rank_amd as dbf
     return dbf.dbf_workspace_bytes(N, R, M, ell, T)
+
+
+# ------------------------------------------------------------ backward --
+def _bwd_ref(L, G, **kw):
+    return oracle.backward(L.x, G, L.S1, L.S2, L.alpha, L.beta, L.gamma, **kw)
+
+
+def _run_bwd(L, G, dx_dtype=torch.float32, H1=None, H2=None, tau=None):
+    pl = H().upload(L)
+    x = H().to_dev_rows(L.x)
+    g = H().to_dev_rows(np.asarray(G, np.float16))
+    kw = {}
+    if H1 is not None:
+        kw = dict(H1=torch.as_tensor(H1, dtype=torch.float32).cuda(),
+                  H2=torch.as_tensor(H2, dtype=torch.float32).cuda(), tau=tau)
+    out = pl.backward(x, g, dx_dtype=dx_dtype, sign_grads=True, **kw)
+    torch.cuda.synchronize()
+    return {k: v.float().cpu().numpy().astype(np.float64) for k, v in out.items()}
+
+
+# every reduction's worst case stays below 2^24 and every fp16 operand value
+# below 2048 (x, g in -3..3, unit scales), so the exact result is an fp32 value
+BWD_INT_SHAPES = [(40, 24, 72, 1, 5), (300, 130, 260, 2, 9), (17, 129, 127, 2, 5),
+                  (64, 16, 8, 3, 70), (1, 1, 1, 1, 1), (96, 200, 136, 1, 40), (24, 16, 40, 2, 200)]
+
+
+@pytest.mark.parametrize("shape", BWD_INT_SHAPES)
+def test_backward_integer_bitexact(shape):
+    """Integer x and g with unit scales: dx, dalpha, dbeta, dgamma, dS1 and
+    dS2 equal the oracle's exact values bit for bit (ragged sizes, several
+    terms, token counts across the 128-token blocks of the sign gradients)."""
+    N, R, M, ell, T = shape
+    L = synth.make_layer(N, R, M, ell, T, seed=200 + sum(shape), alpha="ones", beta="ones",
+                         gamma="ones", x_kind="int3")
+    G = np.random.default_rng(201).integers(-3, 4, size=(T, N)).astype(np.float64)
+    want = _bwd_ref(L, G)
+    got = _run_bwd(L, G)
+    for k in ("dx", "dalpha", "dbeta", "dgamma", "dS1", "dS2"):
+        assert np.array_equal(got[k], want[k].astype(np.float32).astype(np.float64)), k
+
+
+BWD_FP_SHAPES = [(300, 130, 260, 2, 37), (64, 16, 8, 3, 70), (96, 200, 136, 1, 300),
+                 (520, 256, 384, 1, 129)]
+
+
+@pytest.mark.parametrize("shape", BWD_FP_SHAPES)
+def test_backward_fp16(shape):
+    """fp16 data: every gradient, including the straight-through latent
+    gradients (tau = 0.5), within max|d - d_ref| / max|d_ref| <= 2e-3; dx as
+    fp16 and as fp32."""
+    N, R, M, ell, T = shape
+    L = synth.make_layer(N, R, M, ell, T, seed=210 + sum(shape))
+    rng = np.random.default_rng(211)
+    G = oracle.fp16_rne(rng.standard_normal((T, N)))
+    H1, H2 = rng.standard_normal((N, R)), rng.standard_normal((R, M))
+    H1f, H2f = H1.astype(np.float32), H2.astype(np.float32)
+    want = _bwd_ref(L, G, H1=H1f, H2=H2f, tau=0.5)
+    for dx_dtype in (torch.float32, torch.float16):
+        got = _run_bwd(L, G, dx_dtype=dx_dtype, H1=H1f, H2=H2f, tau=0.5)
+        for k in ("dx", "dalpha", "dbeta", "dgamma", "dS1", "dS2", "dH1", "dH2"):
+            err = oracle.max_norm_error(got[k], want[k])
+            assert err <= TOL, (k, err)
+
+
+def test_backward_attention_layer():
+    """The attention projection (4096 x 4096, R = 2048, log-normal scales) at
+    T = 64 tokens: every gradient within the bar."""
+    L = synth.make_config_layer(3, 64)
+    G = oracle.fp16_rne(np.random.default_rng(212).standard_normal((64, L.N)))
+    want = _bwd_ref(L, G)
+    got = _run_bwd(L, G)
+    for k in ("dx", "dalpha", "dbeta", "dgamma", "dS1", "dS2"):
+        err = oracle.max_norm_error(got[k], want[k])
+        assert err <= TOL, (k, err)
