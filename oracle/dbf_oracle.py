@@ -51,6 +51,9 @@ __all__ = [
     "forward_multi_adapter",
     "backward",
     "soft_sign_slope",
+    "svid",
+    "admm_scaled_sign",
+    "factorize",
     "stage1",
     "fp16_rne",
     "max_norm_error",
@@ -246,6 +249,88 @@ def backward(x, gout, S1, S2, alpha, beta, gamma, H1=None, H2=None, tau=None) ->
     if H2 is not None:
         out["dH2"] = out["dS2"] * soft_sign_slope(H2, tau)
     return out
+
+
+def svid(Y):
+    """[DBF] section 2 "Algoritmo de Optimizacion", the SVID projection: the
+    sign of Y times the best rank-1 approximation of its magnitude |Y|.  The
+    rank-1 factor is the top singular triplet (sigma, u, v) of |Y| (u, v >= 0:
+    |Y| has no negative entry), split as u' = sqrt(sigma) u, v' = sqrt(sigma) v.
+    Returns (u', S, v') with S = sign(Y) (h < 0 -> -1, else +1) as int8, so the
+    projection is diag(u') S diag(v')."""
+    Y = _f64(Y)
+    S = np.where(Y < 0, -1, 1).astype(np.int8)
+    uu, sig, vt = np.linalg.svd(np.abs(Y), full_matrices=False)
+    u, v = uu[:, 0], vt[0]
+    if u.sum() < 0:  # the singular pair is defined up to a joint sign
+        u, v = -u, -v
+    r = np.sqrt(sig[0])
+    return r * u, S, r * v
+
+
+def _svid_matrix(Y):
+    u, S, v = svid(Y)
+    return u[:, None] * S * v[None, :]
+
+
+def admm_scaled_sign(W, F, side, Z, iters, rho0):
+    """[DBF] "Algoritmo de Optimizacion", one alternating-minimisation half
+    step: with the other factor F fixed, ADMM on
+        min ||W - X F||^2 (side "A": X is N x k, F is k x M)  or
+        min ||W - F X||^2 (side "B": X is k x M, F is N x k)
+    subject to X in the set of scaled sign matrices diag(u) S diag(v), in the
+    scaled form (dual U, penalty rho = rho0 * trace(G) / k with G the Gram
+    matrix of F):
+        X <- argmin_X ||W - X F||^2 + rho ||X - Z + U||^2   (a linear solve)
+        Z <- SVID(X + U)
+        U <- U + X - Z
+    starting from the feasible Z given and U = 0.  Returns the final Z."""
+    W, F, Z = _f64(W), _f64(F), _f64(Z)
+    k = F.shape[0] if side == "A" else F.shape[1]
+    G = F @ F.T if side == "A" else F.T @ F
+    rho = rho0 * np.trace(G) / k
+    reg = G + rho * np.eye(k)
+    base = W @ F.T if side == "A" else F.T @ W  # N x k, or k x M
+    U = np.zeros_like(Z)
+    for _ in range(iters):
+        rhs = base + rho * (Z - U)
+        X = np.linalg.solve(reg, rhs.T).T if side == "A" else np.linalg.solve(reg, rhs)
+        Z = _svid_matrix(X + U)
+        U = U + X - Z
+    return Z
+
+
+def factorize(W, k, omega, outer, admm_iters, rho0=1.0, start=None):
+    """[DBF] "Algoritmo de Optimizacion": W (N x M) ~ X Y with X = diag(a) A
+    diag(m) (N x k) and Y = diag(r) B diag(b) (k x M), A and B sign matrices,
+    by alternating minimisation (fix Y and solve for X, then fix X and solve
+    for Y), each half step an ADMM run projecting with SVID.  Readings (the
+    page gives the method, not its constants): the start is Y0 = SVID(omega W)
+    for a Gaussian k x N sketch omega (drawn by the caller), X0 = 0; each half
+    step starts its ADMM from the side's current value (X0's first run from
+    SVID of the unconstrained least-squares solution) and ends on the
+    projection Z, so both factors stay feasible; r is folded into m at the end.
+    Returns dict(alpha=a, S1=A, beta=m*r, S2=B, gamma=b, rel_err), the
+    factors of the layer y = diag(a) A diag(beta) B diag(b) x.  ``start``
+    (X0, Y0), both scaled sign matrices, replaces the sketch start."""
+    W = _f64(W)
+    if start is None:
+        Y = _svid_matrix(_f64(omega) @ W)
+        X = None
+    else:
+        X, Y = _f64(start[0]), _f64(start[1])
+    for _ in range(outer):
+        if X is None:
+            G = Y @ Y.T
+            rho = rho0 * np.trace(G) / k
+            X = _svid_matrix(np.linalg.solve(G + rho * np.eye(k), (W @ Y.T).T).T)
+        X = admm_scaled_sign(W, Y, "A", X, admm_iters, rho0)
+        Y = admm_scaled_sign(W, X, "B", Y, admm_iters, rho0)
+    a, A, m = svid(X)
+    r, B, b = svid(Y)
+    rel = float(np.linalg.norm(W - (a[:, None] * A * (m * r)[None, :]) @ (B * b[None, :]))
+                / np.linalg.norm(W))
+    return {"alpha": a, "S1": A, "beta": m * r, "S2": B, "gamma": b, "rel_err": rel}
 
 
 def forward_multi_adapter(x, ids, adapters, y_old=None) -> np.ndarray:

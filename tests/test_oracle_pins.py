@@ -616,3 +616,128 @@ def test_backward_pins_reject_mutants(mutant):
 
 def test_soft_slope_pin_rejects_mutant():
     assert not pin_soft_slope(lambda h, tau: 1.0 - np.tanh(np.asarray(h) / tau) ** 2)
+
+
+# ------------------------------------------------------- factorisation ----
+# SVID and the ADMM half step are pinned to closed forms, to the first-order
+# conditions of the stated minimisation and to a fixed point; factorize to
+# exact recovery when started at a factorisation.
+
+def _scaled_sign(rng, n, k):
+    u, v = np.exp(rng.normal(0, 0.3, n)), np.exp(rng.normal(0, 0.3, k))
+    S = np.where(rng.random((n, k)) < 0.5, -1, 1)
+    return u, S, v
+
+
+def pin_svid(svid):
+    rng = np.random.default_rng(40)
+    ok = True
+    # a scaled sign matrix is its own projection
+    u, S, v = _scaled_sign(rng, 7, 5)
+    Y = u[:, None] * S * v[None, :]
+    uu, SS, vv = svid(Y)
+    ok &= np.array_equal(SS, S) and np.allclose(uu[:, None] * SS * vv[None, :], Y, rtol=1e-12)
+    # Eckart-Young: the rank-1 residual of |Y| is the square root of the sum
+    # of all but the largest eigenvalue of |Y|^T |Y| (eigvalsh, not an SVD)
+    Y = rng.standard_normal((9, 6))
+    uu, SS, vv = svid(Y)
+    ok &= np.array_equal(SS, np.where(Y < 0, -1, 1))
+    ev = np.sort(np.linalg.eigvalsh(np.abs(Y).T @ np.abs(Y)))
+    res = np.linalg.norm(np.abs(Y) - np.outer(uu, vv))
+    ok &= abs(res - math.sqrt(max(ev[:-1].sum(), 0.0))) < 1e-10
+    ok &= bool((uu >= -1e-15).all() and (vv >= -1e-15).all())
+    # and no nonnegative rank-1 guess does better
+    for _ in range(20):
+        p, q = np.abs(rng.standard_normal(9)), np.abs(rng.standard_normal(6))
+        c = (p @ np.abs(Y) @ q) / ((p @ p) * (q @ q))
+        ok &= res <= np.linalg.norm(np.abs(Y) - c * np.outer(p, q)) + 1e-12
+    # sign(0) = +1
+    ok &= bool(svid(np.zeros((2, 3)))[1].min() == 1)
+    return bool(ok)
+
+
+def pin_admm_step(admm):
+    """One iteration from (Z, U = 0): X solves the stated least squares, so
+    its gradient vanishes, (X F - W) F^T + rho (X - Z) = 0 (side A), and the
+    returned Z is the SVID projection of X (checked through its own closed
+    form: sign pattern of X, rank-1 magnitudes)."""
+    rng = np.random.default_rng(41)
+    N, M, k = 8, 7, 3
+    W = rng.standard_normal((N, M))
+    u, S, v = _scaled_sign(rng, k, M)
+    F = u[:, None] * S * v[None, :]
+    u0, S0, v0 = _scaled_sign(rng, N, k)
+    Z0 = u0[:, None] * S0 * v0[None, :]
+    G = F @ F.T
+    rho = 1.0 * np.trace(G) / k
+    Z1 = admm(W, F, "A", Z0, 1, 1.0)
+    # reconstruct X from the optimality condition and compare its sign pattern
+    X = np.linalg.lstsq(np.vstack([F.T, math.sqrt(rho) * np.eye(k)]),
+                        np.vstack([W.T, math.sqrt(rho) * Z0.T]), rcond=None)[0].T
+    grad = (X @ F - W) @ F.T + rho * (X - Z0)
+    ok = np.abs(grad).max() < 1e-9
+    ok &= np.array_equal(np.where(Z1 < 0, -1, 1), np.where(X < 0, -1, 1))
+    ok &= np.linalg.matrix_rank(np.abs(Z1), tol=1e-9) == 1
+    # side B is side A on the transposed problem
+    ZB = admm(W.T, F.T, "B", Z0.T, 1, 1.0)
+    ok &= np.allclose(ZB, Z1.T, rtol=1e-10, atol=1e-12)
+    return bool(ok)
+
+
+def pin_factorize_fixed_point(fact):
+    """Started at an exact factorisation W = X* Y* (both scaled sign), the
+    alternating ADMM stays there: rel_err ~ 0 and the same sign matrices."""
+    rng = np.random.default_rng(42)
+    N, M, k = 12, 10, 4
+    a, A, m = _scaled_sign(rng, N, k)
+    r, B, b = _scaled_sign(rng, k, M)
+    X, Y = a[:, None] * A * m[None, :], r[:, None] * B * b[None, :]
+    W = X @ Y
+    f = fact(W, k, None, 3, 5, 1.0, start=(X, Y))
+    ok = f["rel_err"] < 1e-10
+    ok &= np.array_equal(f["S1"], A) and np.array_equal(f["S2"], B)
+    dw = (f["alpha"][:, None] * f["S1"] * f["beta"][None, :]) @ (f["S2"] * f["gamma"][None, :])
+    ok &= np.allclose(dw, W, rtol=1e-10, atol=1e-12)
+    return bool(ok)
+
+
+def test_svid_pins():
+    assert pin_svid(oracle.svid)
+
+
+def test_admm_step_pins():
+    assert pin_admm_step(oracle.admm_scaled_sign)
+
+
+def test_factorize_fixed_point():
+    assert pin_factorize_fixed_point(oracle.factorize)
+
+
+def test_factorize_improves_on_its_start():
+    """The alternating steps lower the error from the sketch start and the
+    result is a valid layer: its dense update equals the reported error."""
+    rng = np.random.default_rng(43)
+    W = rng.standard_normal((40, 30))
+    om = rng.standard_normal((8, 40))
+    f1 = oracle.factorize(W, 8, om, 1, 1)
+    f4 = oracle.factorize(W, 8, om, 4, 10)
+    assert f4["rel_err"] < f1["rel_err"] < 1.0
+    dw = oracle.delta_w(f4["S1"], f4["S2"], f4["alpha"], f4["beta"], f4["gamma"])
+    assert abs(np.linalg.norm(W - dw) / np.linalg.norm(W) - f4["rel_err"]) < 1e-12
+
+
+def test_factorisation_pins_reject_mutants():
+    def svid_no_sqrt(Y):
+        u, S, v = oracle.svid(Y)
+        return u * u, S, v * v
+    assert not pin_svid(svid_no_sqrt)
+
+    def admm_wrong_penalty(W, F, side, Z, iters, rho0):
+        return oracle.admm_scaled_sign(W, F, side, Z, iters, 0.1 * rho0)
+    assert not pin_admm_step(admm_wrong_penalty)
+
+    def fact_swapped(W, k, omega, outer, iters, rho0=1.0, start=None):
+        f = oracle.factorize(W, k, omega, outer, iters, rho0, start)
+        f["beta"] = f["beta"][::-1].copy()
+        return f
+    assert not pin_factorize_fixed_point(fact_swapped)
