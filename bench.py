@@ -37,6 +37,7 @@ import csv
 import glob
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -50,6 +51,7 @@ sys.path.insert(0, ROOT)
 METRIC = "DBF sign-matmul tokens/s + effective GB/s (4096², R=2048, T=1/256), % roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # published; the kernels here issue unpacked fp32 FMAs
 N_, R_, M_ = 4096, 2048, 4096
 GEMM_SRC = os.path.join(ROOT, "double_binary_rank_amd", "csrc", "dbf_gemm.hip")
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "k_gemm_traffic_attn4096_R2048_T256.md")
@@ -471,6 +473,53 @@ def main():
         }
         log(f"backward T=256: {tB * 1e6:.1f} us/call, {flB / tB / 1e12:.1f} TFLOP/s, "
             f"max err {max(errB.values()):.2e}; fp64 oracle {t_o:.2f} s")
+
+    # ----------------------- factorisation of a dense 4096 x 4096 matrix --
+    if want("factorize"):
+        Nf = Mf = 4096
+        kf, outer, iters, n_pow = 2048, 2, 5, 8
+        rngf = np.random.default_rng(9)
+        Wf = torch.as_tensor(rngf.standard_normal((Nf, Mf)) * 0.02, dtype=torch.float32).to(dev)
+        omf = torch.as_tensor(rngf.standard_normal((kf, Nf)), dtype=torch.float32).to(dev)
+        wsf = torch.empty(dbf.dbf_factorize_workspace_bytes(Nf, Mf, kf), dtype=torch.uint8,
+                          device=dev)
+        run = lambda: dbf.dbf_factorize(Wf, kf, omf, outer=outer, admm_iters=iters,  # noqa: E731
+                                        power_iters=n_pow, ws=wsf)
+        run()
+        torch.cuda.synchronize()
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record()
+        fres = run()
+        e_.record()
+        torch.cuda.synchronize()
+        tf = s_.elapsed_time(e_) / 1e3
+        n_ns = 2 * math.ceil(math.log2(kf + 1)) + 10
+        ns = n_ns * 2 * 2 * kf ** 3
+        gem = 2 * kf * Nf * Mf + 2 * Nf * kf * kf  # the start, the first least squares
+        gem += outer * (2 * kf * kf * Mf + ns + 2 * Nf * Mf * kf + iters * 2 * Nf * kf * kf
+                        + 2 * kf * kf * Nf + ns + 2 * kf * Mf * Nf + iters * 2 * kf * kf * Mf)
+        gem += 2 * Nf * kf * Mf  # the error check
+        # the fp64 oracle on a bounded sample: a 512 x 512 matrix, k = 256
+        Ws = rngf.standard_normal((512, 512)) * 0.02
+        oms = rngf.standard_normal((256, 512))
+        t_o = time.perf_counter()
+        ref_s = oracle.factorize(Ws, 256, oms, 1, 2)
+        t_o = time.perf_counter() - t_o
+        got_s = dbf.dbf_factorize(torch.as_tensor(Ws, dtype=torch.float32).to(dev), 256,
+                                  torch.as_tensor(oms, dtype=torch.float32).to(dev), outer=1,
+                                  admm_iters=2, power_iters=30)
+        torch.cuda.synchronize()
+        out["factorize_4096x4096_k2048"] = {
+            "N": Nf, "M": Mf, "k": kf, "outer": outer, "admm_iters": iters, "power_iters": n_pow,
+            "seconds": tf, "rel_err": float(fres["rel_err"]),
+            "gemm_tflop_executed": gem / 1e12, "achieved_TFLOPs": gem / tf / 1e12,
+            "fp32_vector_peak_frac": gem / tf / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+            "sample_512_k256": {"rel_err_gpu": float(got_s["rel_err"]),
+                                "rel_err_oracle": ref_s["rel_err"], "oracle_seconds": t_o},
+        }
+        log(f"factorize 4096x4096 k=2048: {tf:.3f} s, rel err {float(fres['rel_err']):.4f}, "
+            f"{gem / tf / 1e12:.1f} TFLOP/s executed; 512 sample: gpu "
+            f"{float(got_s['rel_err']):.4f} vs oracle {ref_s['rel_err']:.4f} ({t_o:.1f} s)")
 
     # ------------------------------------------------ copy calibration --
     if args.copy_calibration:

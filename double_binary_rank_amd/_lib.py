@@ -44,6 +44,8 @@ EXPORTS = (
     "dbf_forward_multi_adapter",
     "dbf_backward_workspace_bytes",
     "dbf_backward",
+    "dbf_factorize_workspace_bytes",
+    "dbf_factorize",
 )
 
 
@@ -130,6 +132,17 @@ lib.dbf_backward.argtypes = [
     _vp, _sz, _vp,  # ws, ws_bytes, stream
 ]
 
+lib.dbf_factorize_workspace_bytes.restype = _i32
+lib.dbf_factorize_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
+lib.dbf_factorize.restype = _i32
+lib.dbf_factorize.argtypes = [
+    _vp, _i64, _i64, _i64, _i64,  # W, N, M, ldw, k
+    _vp, _vp, _vp,  # omega, X0, Y0
+    _i32, _i32, _i32, ctypes.c_float,  # outer, admm_iters, power_iters, rho0
+    _vp, _vp, _vp, _vp, _vp, _vp,  # S1, S2, alpha, beta, gamma, rel_err
+    _vp, _sz, _vp,  # ws, ws_bytes, stream
+]
+
 
 def status_string(status: int) -> str:
     return lib.dbf_status_string(status).decode()
@@ -160,4 +173,11 @@ def backward_workspace_bytes(N: int, R: int, M: int, ell: int, T: int) -> int:
     out = _sz(0)
     check(lib.dbf_backward_workspace_bytes(N, R, M, ell, T, ctypes.byref(out)),
           "dbf_backward_workspace_bytes")
+    return out.value
+
+
+def factorize_workspace_bytes(N: int, M: int, k: int) -> int:
+    out = _sz(0)
+    check(lib.dbf_factorize_workspace_bytes(N, M, k, ctypes.byref(out)),
+          "dbf_factorize_workspace_bytes")
     return out.value

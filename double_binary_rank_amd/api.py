@@ -26,6 +26,8 @@ __all__ = [
     "dbf_forward_multi_adapter",
     "dbf_backward_workspace_bytes",
     "dbf_backward",
+    "dbf_factorize_workspace_bytes",
+    "dbf_factorize",
     "PackedLayer",
     "pointer_table",
 ]
@@ -199,6 +201,40 @@ def dbf_backward(x: torch.Tensor, g: torch.Tensor, B1: torch.Tensor, B2: torch.T
     return out
 
 
+def dbf_factorize_workspace_bytes(N: int, M: int, k: int) -> int:
+    return _lib.factorize_workspace_bytes(N, M, k)
+
+
+def dbf_factorize(W: torch.Tensor, k: int, omega: torch.Tensor | None = None, *, outer: int = 3,
+                  admm_iters: int = 10, power_iters: int = 8, rho0: float = 1.0, start=None,
+                  ws: torch.Tensor | None = None, stream=None) -> dict:
+    """Double binary factorisation of the fp32 matrix W [N][M] at inner
+    dimension k: returns S1 int8 [N][k], S2 int8 [k][M], alpha [1][N], beta
+    [1][k], gamma [1][M] fp16 and rel_err (a 0-d fp32 device tensor).  omega
+    [k][N] fp32 is the caller's Gaussian sketch for the start, or ``start`` =
+    (X0, Y0) fp32 scaled sign matrices."""
+    N, M = W.shape
+    ldw = _row_major(W, "W")
+    dev = W.device
+    out = {"S1": torch.empty((N, k), dtype=torch.int8, device=dev),
+           "S2": torch.empty((k, M), dtype=torch.int8, device=dev),
+           "alpha": torch.empty((1, N), dtype=torch.float16, device=dev),
+           "beta": torch.empty((1, k), dtype=torch.float16, device=dev),
+           "gamma": torch.empty((1, M), dtype=torch.float16, device=dev),
+           "rel_err": torch.empty((), dtype=torch.float32, device=dev)}
+    X0 = Y0 = None
+    if start is not None:
+        X0, Y0 = (t.contiguous() for t in start)
+    if ws is None:
+        ws = torch.empty(dbf_factorize_workspace_bytes(N, M, k), dtype=torch.uint8, device=dev)
+    check(lib.dbf_factorize(
+        _ptr(W), N, M, ldw, k, _ptr(omega), _ptr(X0), _ptr(Y0), outer, admm_iters, power_iters,
+        float(rho0), _ptr(out["S1"]), _ptr(out["S2"]), _ptr(out["alpha"]), _ptr(out["beta"]),
+        _ptr(out["gamma"]), _ptr(out["rel_err"]), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "dbf_factorize")
+    return out
+
+
 def pointer_table(tensors, device) -> torch.Tensor:
     """Device int64 array of the tensors' device addresses."""
     return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
@@ -265,6 +301,12 @@ class PackedLayer:
     def forward(self, x: torch.Tensor, **kw) -> torch.Tensor:
         return dbf_forward(x, self.B1, self.B2, self.alpha, self.beta, self.gamma, self.N, self.R,
                            self.M, **kw)
+
+    @classmethod
+    def from_factorization(cls, f: dict) -> "PackedLayer":
+        """The layer of a ``dbf_factorize`` result (signs packed here)."""
+        return cls(dbf_pack_signs(f["S1"]), dbf_pack_signs(f["S2"]), f["alpha"], f["beta"],
+                   f["gamma"], f["S1"].shape[0], f["S1"].shape[1], f["S2"].shape[1])
 
     def transposed_signs(self):
         """Packed S1^T (R x N) and S2^T (M x R), built once per layer."""

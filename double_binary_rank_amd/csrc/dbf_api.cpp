@@ -277,4 +277,57 @@ dbf_status dbf_backward(const void* x, int64_t ldx, const void* g, int64_t ldg, 
   return hip_status(dbf::launch_backward(a, (hipStream_t)stream));
 }
 
+dbf_status dbf_factorize_workspace_bytes(int64_t N, int64_t M, int64_t k, size_t* bytes) {
+  if (N <= 0 || M <= 0 || k <= 0 || bytes == nullptr) return DBF_ERR_INVALID_ARG;
+  if (N > DBF_MAX_DIM || M > DBF_MAX_DIM || k > DBF_MAX_DIM) return DBF_ERR_INVALID_ARG;
+  *bytes = dbf::factor_layout(N, M, k).total;
+  return DBF_OK;
+}
+
+dbf_status dbf_factorize(const float* W, int64_t N, int64_t M, int64_t ldw, int64_t k,
+                         const float* omega, const float* X0, const float* Y0, int32_t outer,
+                         int32_t admm_iters, int32_t power_iters, float rho0, int8_t* S1,
+                         int8_t* S2, void* alpha, void* beta, void* gamma, float* rel_err,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (N <= 0 || M <= 0 || k <= 0) return DBF_ERR_INVALID_ARG;
+  if (N > DBF_MAX_DIM || M > DBF_MAX_DIM || k > DBF_MAX_DIM) return DBF_ERR_INVALID_ARG;
+  // the dense products index their tiles and rows with 32 bits
+  if (cdiv(N, 64) * cdiv(M, 64) > INT32_MAX || cdiv(N > M ? N : M, 64) * cdiv(k, 64) > INT32_MAX)
+    return DBF_ERR_INVALID_ARG;
+  if (W == nullptr || S1 == nullptr || S2 == nullptr || alpha == nullptr || beta == nullptr ||
+      gamma == nullptr)
+    return DBF_ERR_INVALID_ARG;
+  if (omega == nullptr && (X0 == nullptr || Y0 == nullptr)) return DBF_ERR_INVALID_ARG;
+  if ((X0 == nullptr) != (Y0 == nullptr)) return DBF_ERR_INVALID_ARG;
+  if (ldw < M || outer < 0 || admm_iters < 1 || power_iters < 1) return DBF_ERR_INVALID_ARG;
+  if (!(rho0 > 0.0f && rho0 < 3.0e38f)) return DBF_ERR_INVALID_ARG;
+  if ((((uintptr_t)W) | ((uintptr_t)omega) | ((uintptr_t)X0) | ((uintptr_t)Y0) |
+       ((uintptr_t)rel_err)) & 3u)
+    return DBF_ERR_ALIGNMENT;
+  if ((((uintptr_t)alpha) | ((uintptr_t)beta) | ((uintptr_t)gamma)) & 1u) return DBF_ERR_ALIGNMENT;
+  if (ws == nullptr || ws_bytes < dbf::factor_layout(N, M, k).total) return DBF_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DBF_ERR_ALIGNMENT;
+  dbf::FactorArgs a{};
+  a.W = W;
+  a.ldw = ldw;
+  a.N = N;
+  a.M = M;
+  a.k = k;
+  a.omega = omega;
+  a.X0 = X0;
+  a.Y0 = Y0;
+  a.outer = outer;
+  a.admm_iters = admm_iters;
+  a.power_iters = power_iters;
+  a.rho0 = rho0;
+  a.S1 = S1;
+  a.S2 = S2;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.gamma = gamma;
+  a.rel_err = rel_err;
+  a.ws = ws;
+  return hip_status(dbf::launch_factorize(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -190,4 +190,31 @@ inline BwdLayout bwd_layout(int64_t N, int64_t R, int64_t M, int32_t ell, int64_
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 
+// ------------------------------------------------------- factorisation ----
+struct FactorArgs {
+  const float* W;  // [N][ldw]
+  int64_t ldw;
+  int64_t N, M, k;
+  const float* omega;  // [k][N] sketch for the start, or null with X0/Y0
+  const float* X0;     // [N][k] and [k][M] scaled sign start, or null
+  const float* Y0;
+  int32_t outer, admm_iters, power_iters;
+  float rho0;
+  int8_t* S1;  // [N][k]
+  int8_t* S2;  // [k][M]
+  void* alpha;  // fp16 [N], [k], [M]
+  void* beta;
+  void* gamma;
+  float* rel_err;  // device scalar or null
+  void* ws;
+};
+
+struct FactorLayout {
+  size_t xa, za, ua, xb, zb, ub, base, rhs, g, inv, inv2, t, ua_vec, va_vec, ub_vec, vb_vec, part,
+      prod, sc, total;
+};
+
+FactorLayout factor_layout(int64_t N, int64_t M, int64_t k);
+hipError_t launch_factorize(const FactorArgs& a, hipStream_t s);
+
 }  // namespace dbf

@@ -239,6 +239,47 @@ dbf_status dbf_backward(const void* x, int64_t ldx, const void* g, int64_t ldg, 
                         float* dS2, const float* H1, const float* H2, float tau, float* dH1,
                         float* dH2, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Workspace bytes needed by dbf_factorize for an N x M matrix and inner
+ * dimension k.  Errors: INVALID_ARG for sizes <= 0 or above DBF_MAX_DIM, or
+ * bytes == NULL.
+ */
+dbf_status dbf_factorize_workspace_bytes(int64_t N, int64_t M, int64_t k, size_t* bytes);
+
+/*
+ * Double binary factorisation of a dense matrix (DBF summary, section 2,
+ * "Algoritmo de Optimizacion"): W ~ (diag(alpha) S1 diag(beta)) (S2
+ * diag(gamma)), S1 [N][k] and S2 [k][M] sign matrices, so that dbf_forward
+ * with these factors (ell = 1, after dbf_pack_signs) applies the
+ * approximation of W.  Alternating minimisation over the two factors; each
+ * half step runs admm_iters ADMM iterations (scaled form, penalty rho0 *
+ * trace(Gram) / k) that project onto scaled sign matrices with SVID (sign
+ * times the rank-1 approximation of the magnitude, here by power_iters power
+ * steps warm-started across iterations; the linear solves by Newton-Schulz
+ * inversion of the k x k regularised Gram matrix).  outer alternations (0:
+ * only the start is projected).
+ *   W      fp32 [N][ldw] (ldw >= M)
+ *   omega  fp32 [k][N] Gaussian sketch drawn by the caller: the start is
+ *          Y0 = SVID(omega W); or NULL with
+ *   X0, Y0 fp32 [N][k], [k][M] scaled sign matrices to start from (both or
+ *          neither)
+ *   S1, S2 int8 +-1 outputs [N][k], [k][M]; alpha [N], beta [k], gamma [M]
+ *          fp16 outputs; rel_err: device fp32 scalar ||W - W~||_F / ||W||_F,
+ *          or NULL.
+ * Reading of the method where the page is silent: the row scale of the
+ * second factor is folded into beta; the first factor starts from SVID of
+ * the regularised least-squares solution.  All arithmetic is fp32.
+ * Errors: INVALID_ARG (null output, neither omega nor a start, sizes, ldw <
+ * M, outer < 0, admm_iters or power_iters < 1, rho0 not positive and
+ * finite), ALIGNMENT (fp32 inputs 4-byte, fp16 outputs 2-byte, ws 16-byte),
+ * WORKSPACE, HIP.
+ */
+dbf_status dbf_factorize(const float* W, int64_t N, int64_t M, int64_t ldw, int64_t k,
+                         const float* omega, const float* X0, const float* Y0, int32_t outer,
+                         int32_t admm_iters, int32_t power_iters, float rho0, int8_t* S1,
+                         int8_t* S2, void* alpha, void* beta, void* gamma, float* rel_err,
+                         void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -213,3 +213,48 @@ def test_backward_workspace_bytes():
     for bad in ((0, 16, 64, 1, 4), (32, 16, 64, 0, 4), (32, 16, 64, 1, 0)):
         assert L.dbf_backward_workspace_bytes(*bad, ctypes.byref(out)) == _lib.DBF_ERR_INVALID_ARG
     assert L.dbf_backward_workspace_bytes(32, 16, 64, 1, 4, None) == _lib.DBF_ERR_INVALID_ARG
+
+
+def _fac(**kw):
+    a = dict(W=A, N=64, M=48, ldw=48, k=8, omega=A, X0=None, Y0=None, outer=1, admm_iters=2,
+             power_iters=4, rho0=1.0, S1=A, S2=A, alpha=A, beta=A, gamma=A, rel_err=None, ws=A,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.dbf_factorize(*a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(k=-1), _lib.DBF_ERR_INVALID_ARG),
+    (dict(M=(1 << 30) + 1), _lib.DBF_ERR_INVALID_ARG),
+    (dict(W=None), _lib.DBF_ERR_INVALID_ARG),
+    (dict(S2=None), _lib.DBF_ERR_INVALID_ARG),
+    (dict(gamma=None), _lib.DBF_ERR_INVALID_ARG),
+    (dict(omega=None), _lib.DBF_ERR_INVALID_ARG),             # no start at all
+    (dict(omega=None, X0=A), _lib.DBF_ERR_INVALID_ARG),       # half a start
+    (dict(X0=A), _lib.DBF_ERR_INVALID_ARG),
+    (dict(ldw=40), _lib.DBF_ERR_INVALID_ARG),
+    (dict(outer=-1), _lib.DBF_ERR_INVALID_ARG),
+    (dict(admm_iters=0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(power_iters=0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(rho0=0.0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(rho0=float("nan")), _lib.DBF_ERR_INVALID_ARG),
+    (dict(W=A + 2), _lib.DBF_ERR_ALIGNMENT),
+    (dict(omega=A + 1), _lib.DBF_ERR_ALIGNMENT),
+    (dict(beta=A + 1), _lib.DBF_ERR_ALIGNMENT),
+    (dict(ws=None), _lib.DBF_ERR_WORKSPACE),
+    (dict(ws_bytes=4096), _lib.DBF_ERR_WORKSPACE),
+    (dict(ws=MIS), _lib.DBF_ERR_ALIGNMENT),
+])
+def test_factorize_rejects(kw, want):
+    assert _fac(**kw) == want
+
+
+def test_factorize_workspace_bytes():
+    out = ctypes.c_size_t(0)
+    assert L.dbf_factorize_workspace_bytes(64, 48, 8, ctypes.byref(out)) == _lib.DBF_OK
+    small = out.value
+    assert L.dbf_factorize_workspace_bytes(640, 480, 80, ctypes.byref(out)) == _lib.DBF_OK
+    assert out.value > small > 0
+    assert L.dbf_factorize_workspace_bytes(0, 48, 8, ctypes.byref(out)) == _lib.DBF_ERR_INVALID_ARG
+    assert L.dbf_factorize_workspace_bytes(64, 48, 8, None) == _lib.DBF_ERR_INVALID_ARG

@@ -638,3 +638,102 @@ def test_backward_attention_layer():
     for k in ("dx", "dalpha", "dbeta", "dgamma", "dS1", "dS2"):
         err = oracle.max_norm_error(got[k], want[k])
         assert err <= TOL, (k, err)
+
+
+# ------------------------------------------------------- factorisation --
+def _scaled_sign(rng, n, k):
+    u, v = np.exp(rng.normal(0, 0.3, n)), np.exp(rng.normal(0, 0.3, k))
+    return u[:, None] * np.where(rng.random((n, k)) < 0.5, -1, 1) * v[None, :]
+
+
+def _dense_of(f):
+    """float64 dense update of a factorisation result (its fp16 scales)."""
+    a = f["alpha"].float().cpu().numpy().astype(np.float64)[0]
+    b = f["beta"].float().cpu().numpy().astype(np.float64)[0]
+    g = f["gamma"].float().cpu().numpy().astype(np.float64)[0]
+    S1 = f["S1"].cpu().numpy().astype(np.float64)
+    S2 = f["S2"].cpu().numpy().astype(np.float64)
+    return (a[:, None] * S1 * b[None, :]) @ (S2 * g[None, :])
+
+
+def test_factorize_exact_start_is_a_fixed_point():
+    """Started at an exact factorisation W = X* Y*, the GPU iteration keeps
+    the sign matrices and reconstructs W (fp32 arithmetic, fp16 scales)."""
+    rng = np.random.default_rng(300)
+    N, M, k = 96, 80, 16
+    X, Y = _scaled_sign(rng, N, k), _scaled_sign(rng, k, M)
+    W = X @ Y
+    dev = lambda a: torch.as_tensor(a, dtype=torch.float32).cuda()  # noqa: E731
+    f = dbf_mod().dbf_factorize(dev(W), k, start=(dev(X), dev(Y)), outer=2, admm_iters=4)
+    torch.cuda.synchronize()
+    assert np.array_equal(f["S1"].cpu().numpy(), np.where(X < 0, -1, 1))
+    assert np.array_equal(f["S2"].cpu().numpy(), np.where(Y < 0, -1, 1))
+    assert float(f["rel_err"]) < 1e-5
+    assert oracle.max_norm_error(_dense_of(f), W) < 2e-3  # fp16 scales
+
+
+@pytest.mark.parametrize("shape", [(64, 48, 12), (200, 136, 40)])
+def test_factorize_one_step_matches_oracle(shape):
+    """From the same sketch, one ADMM iteration per side: the GPU's factors
+    agree with the oracle's (fp32 vs fp64, power iteration vs SVD): at least
+    99.5% of the signs, the dense updates within 1e-2 of max, and the same
+    error to 1e-3."""
+    N, M, k = shape
+    rng = np.random.default_rng(301 + N)
+    W = rng.standard_normal((N, M))
+    om = rng.standard_normal((k, N))
+    want = oracle.factorize(W, k, om, 1, 1)
+    dev = lambda a: torch.as_tensor(a, dtype=torch.float32).cuda()  # noqa: E731
+    f = dbf_mod().dbf_factorize(dev(W), k, dev(om), outer=1, admm_iters=1, power_iters=30)
+    torch.cuda.synchronize()
+    agree1 = (f["S1"].cpu().numpy() == want["S1"]).mean()
+    agree2 = (f["S2"].cpu().numpy() == want["S2"]).mean()
+    assert agree1 >= 0.995 and agree2 >= 0.995, (agree1, agree2)
+    dw_want = (want["alpha"][:, None] * want["S1"] * want["beta"][None, :]) @ (
+        want["S2"] * want["gamma"][None, :])
+    assert oracle.max_norm_error(_dense_of(f), dw_want) < 1e-2
+    assert abs(float(f["rel_err"]) - want["rel_err"]) < 1e-3
+
+
+def test_factorize_converges_like_oracle():
+    """Several alternations: the GPU's error lands within 0.01 of the
+    oracle's, it falls from the one-step error, and the reported error is
+    that of the returned factors."""
+    N, M, k = 128, 96, 24
+    rng = np.random.default_rng(310)
+    W = rng.standard_normal((N, M))
+    om = rng.standard_normal((k, N))
+    want = oracle.factorize(W, k, om, 4, 8)
+    dev = lambda a: torch.as_tensor(a, dtype=torch.float32).cuda()  # noqa: E731
+    f = dbf_mod().dbf_factorize(dev(W), k, dev(om), outer=4, admm_iters=8, power_iters=16)
+    f1 = dbf_mod().dbf_factorize(dev(W), k, dev(om), outer=1, admm_iters=1, power_iters=16)
+    torch.cuda.synchronize()
+    err = float(f["rel_err"])
+    assert abs(err - want["rel_err"]) < 0.01, (err, want["rel_err"])
+    assert err < float(f1["rel_err"])
+    dense_err = np.linalg.norm(W - _dense_of(f)) / np.linalg.norm(W)
+    assert abs(dense_err - err) < 2e-3  # the fp16 rounding of the scales
+
+
+def test_factorised_layer_runs_forward():
+    """The factors, packed, are a layer: dbf_forward on them matches the
+    oracle forward of the same factors."""
+    N, M, k, T = 256, 192, 64, 9
+    rng = np.random.default_rng(320)
+    W = rng.standard_normal((N, M))
+    om = rng.standard_normal((k, N))
+    dev = lambda a: torch.as_tensor(a, dtype=torch.float32).cuda()  # noqa: E731
+    f = dbf_mod().dbf_factorize(dev(W), k, dev(om), outer=2, admm_iters=4)
+    pl = dbf_mod().PackedLayer.from_factorization(f)
+    x = oracle.fp16_rne(rng.standard_normal((T, M)))
+    y = pl.forward(H().to_dev_rows(x))
+    torch.cuda.synchronize()
+    ref_y = oracle.forward(x, f["S1"].cpu().numpy(), f["S2"].cpu().numpy(),
+                           f["alpha"].float().cpu().numpy(), f["beta"].float().cpu().numpy(),
+                           f["gamma"].float().cpu().numpy())
+    assert oracle.max_norm_error(y.float().cpu().numpy(), ref_y) <= TOL
+
+
+def dbf_mod():
+    import double_binary_rank_amd as dbf
+    return dbf
