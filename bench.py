@@ -474,6 +474,43 @@ def main():
         log(f"backward T=256: {tB * 1e6:.1f} us/call, {flB / tB / 1e12:.1f} TFLOP/s, "
             f"max err {max(errB.values()):.2e}; fp64 oracle {t_o:.2f} s")
 
+    # ------------- three same-input layers (q/k/v) in one call, T=1 / 256 --
+    if want("grouped_layers"):
+        J = 3
+        layers_of = lambda i: [dbf.PackedLayer(B1s[(i * J + j) % n_inst], B2s[(i * J + j) % n_inst],  # noqa: E731
+                                               pl.alpha, pl.beta, pl.gamma, N_, R_, M_)
+                               for j in range(J)]
+        res = {}
+        for Tg in (1, 256):
+            xg = x256[:Tg].contiguous()
+            yg = torch.empty((J, Tg, N_), dtype=torch.float16, device=dev)
+            wsg = torch.empty(dbf.dbf_grouped_workspace_bytes(N_, R_, M_, 1, Tg, J),
+                              dtype=torch.uint8, device=dev)
+            ys1 = [torch.empty((Tg, N_), dtype=torch.float16, device=dev) for _ in range(J)]
+            ws1 = torch.empty(dbf.dbf_workspace_bytes(N_, R_, M_, 1, Tg), dtype=torch.uint8,
+                              device=dev)
+            lay = [layers_of(i) for i in range(64)]
+
+            def grouped(i):
+                dbf.dbf_forward_grouped(xg, lay[i % 64], y=yg, ws=wsg)
+
+            def separate(i):
+                for j, p_ in enumerate(lay[i % 64]):
+                    p_.forward(xg, y=ys1[j], ws=ws1)
+
+            grouped(0)
+            separate(0)
+            torch.cuda.synchronize()
+            same = all(torch.equal(yg[j], ys1[j]) for j in range(J))
+            tg_ = time_graph(grouped, 64, max(args.steps // 16, 4), 2)
+            ts_ = time_graph(separate, 64, max(args.steps // 16, 4), 2)
+            res[f"T{Tg}"] = {"grouped_us": tg_ * 1e6, "separate_us": ts_ * 1e6,
+                             "speedup": ts_ / tg_, "bit_identical": same,
+                             "tokens_per_s": J * Tg / tg_}
+            log(f"grouped q/k/v T={Tg}: {tg_ * 1e6:.2f} us vs {ts_ * 1e6:.2f} us for three calls"
+                f" (graph replay), identical={same}")
+        out["grouped_qkv_3x_attn"] = res
+
     # ----------------------- factorisation of a dense 4096 x 4096 matrix --
     if want("factorize"):
         Nf = Mf = 4096

@@ -42,6 +42,8 @@ EXPORTS = (
     "dbf_workspace_bytes",
     "dbf_forward",
     "dbf_forward_multi_adapter",
+    "dbf_grouped_workspace_bytes",
+    "dbf_forward_grouped",
     "dbf_backward_workspace_bytes",
     "dbf_backward",
     "dbf_factorize_workspace_bytes",
@@ -117,6 +119,16 @@ lib.dbf_forward_multi_adapter.argtypes = [
     _vp, _sz, _vp,  # ws, ws_bytes, stream
 ]
 
+lib.dbf_grouped_workspace_bytes.restype = _i32
+lib.dbf_grouped_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
+lib.dbf_forward_grouped.restype = _i32
+lib.dbf_forward_grouped.argtypes = [
+    _vp, _i64, _i64, _i32,  # x, ldx, T, num_layers
+    _vp, _vp, _vp, _vp, _vp,  # B1s, B2s, alphas, betas, gammas (host pointer arrays)
+    _i64, _i64, _i64, _i32,  # N, R, M, ell
+    _vp, _i64, _i64, _i32, _u32,  # y, ldy, y_layer_stride, y_type, flags
+    _vp, _sz, _vp,  # ws, ws_bytes, stream
+]
 lib.dbf_backward_workspace_bytes.restype = _i32
 lib.dbf_backward_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, ctypes.POINTER(_sz)]
 lib.dbf_backward.restype = _i32
@@ -180,4 +192,11 @@ def factorize_workspace_bytes(N: int, M: int, k: int) -> int:
     out = _sz(0)
     check(lib.dbf_factorize_workspace_bytes(N, M, k, ctypes.byref(out)),
           "dbf_factorize_workspace_bytes")
+    return out.value
+
+
+def grouped_workspace_bytes(N: int, R: int, M: int, ell: int, T: int, num_layers: int) -> int:
+    out = _sz(0)
+    check(lib.dbf_grouped_workspace_bytes(N, R, M, ell, T, num_layers, ctypes.byref(out)),
+          "dbf_grouped_workspace_bytes")
     return out.value

@@ -24,6 +24,8 @@ __all__ = [
     "dbf_workspace_bytes",
     "dbf_forward",
     "dbf_forward_multi_adapter",
+    "dbf_grouped_workspace_bytes",
+    "dbf_forward_grouped",
     "dbf_backward_workspace_bytes",
     "dbf_backward",
     "dbf_factorize_workspace_bytes",
@@ -120,9 +122,15 @@ def _flags(accumulate: bool, path: str | None, phases=None) -> int:
     return f
 
 
+def _padded_cols(N, dtype):
+    # rows of 16-byte multiples, as the C ABI requires of ldy
+    per = 16 // torch.empty((), dtype=dtype).element_size()
+    return -(-N // per) * per
+
+
 def _out(y, T, N, y_dtype, device):
     if y is None:
-        y = torch.empty((T, N), dtype=y_dtype, device=device)
+        y = torch.empty((T, _padded_cols(N, y_dtype)), dtype=y_dtype, device=device)[:, :N]
     return y, _row_major(y, "y")
 
 
@@ -153,6 +161,39 @@ def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torc
     check(lib.dbf_forward(_ptr(x), ldx, _ptr(B1), _ptr(B2), _ptr(alpha), _ptr(beta), _ptr(gamma),
                           N, R, M, ell, T, _ptr(y), ldy, yt, _flags(accumulate, path, phases), _ptr(ws),
                           ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward")
+    return y
+
+
+def dbf_grouped_workspace_bytes(N: int, R: int, M: int, ell: int, T: int, num_layers: int) -> int:
+    return _lib.grouped_workspace_bytes(N, R, M, ell, T, num_layers)
+
+
+def dbf_forward_grouped(x: torch.Tensor, layers, *, y: torch.Tensor | None = None,
+                        y_dtype=torch.float16, accumulate: bool = False, path: str | None = None,
+                        ws: torch.Tensor | None = None, stream=None, phases=None) -> torch.Tensor:
+    """The same-input layers ``layers`` (PackedLayer, equal shapes, 1..8 of
+    them) on x [T][M]: returns y [J][T][N] (or writes the given y of that
+    shape; with ``accumulate`` adds onto it)."""
+    J = len(layers)
+    p0 = layers[0]
+    N, R, M, ell = p0.N, p0.R, p0.M, p0.ell
+    T = x.shape[0]
+    ldx = _row_major(x, "x")
+    if y is None:
+        y = torch.empty((J, T, _padded_cols(N, y_dtype)), dtype=y_dtype, device=x.device)[:, :, :N]
+    if y.dim() != 3 or y.shape[0] != J or y.stride(2) != 1:
+        raise ValueError("y must be [layers][T][N] with unit inner stride")
+    ldy, ys = y.stride(1), y.stride(0)
+    if ws is None:
+        ws = torch.empty(max(dbf_grouped_workspace_bytes(N, R, M, ell, T, J), 16),
+                         dtype=torch.uint8, device=x.device)
+    arr = lambda ts: (ctypes.c_void_p * J)(*[t.data_ptr() for t in ts])  # noqa: E731
+    check(lib.dbf_forward_grouped(
+        _ptr(x), ldx, T, J, arr([p.B1 for p in layers]), arr([p.B2 for p in layers]),
+        arr([p.alpha for p in layers]), arr([p.beta for p in layers]),
+        arr([p.gamma for p in layers]), N, R, M, ell, _ptr(y), ldy, ys, _DTYPE[y.dtype],
+        _flags(accumulate, path, phases), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "dbf_forward_grouped")
     return y
 
 

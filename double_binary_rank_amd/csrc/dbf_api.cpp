@@ -199,6 +199,68 @@ dbf_status dbf_forward_multi_adapter(const void* x, int64_t ldx, int64_t T, cons
   return hip_status(dbf::launch_forward(a, (hipStream_t)stream));
 }
 
+dbf_status dbf_grouped_workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T,
+                                       int32_t num_layers, size_t* bytes) {
+  if (N <= 0 || R <= 0 || M <= 0 || ell < 1 || T < 0 || bytes == nullptr) return DBF_ERR_INVALID_ARG;
+  if (num_layers < 1 || num_layers > dbf::kMaxGroup) return DBF_ERR_INVALID_ARG;
+  *bytes = (size_t)num_layers * dbf::align256(dbf::workspace_bytes(N, R, M, ell, T));
+  return DBF_OK;
+}
+
+dbf_status dbf_forward_grouped(const void* x, int64_t ldx, int64_t T, int32_t num_layers,
+                               const uint32_t* const* B1s, const uint32_t* const* B2s,
+                               const void* const* alphas, const void* const* betas,
+                               const void* const* gammas, int64_t N, int64_t R, int64_t M,
+                               int32_t ell, void* y, int64_t ldy, int64_t y_layer_stride,
+                               dbf_dtype y_type, uint32_t flags, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (num_layers < 1 || num_layers > dbf::kMaxGroup || B1s == nullptr || B2s == nullptr ||
+      alphas == nullptr || betas == nullptr || gammas == nullptr)
+    return DBF_ERR_INVALID_ARG;
+  const size_t layer_ws = dbf::align256(dbf::workspace_bytes(N > 0 ? N : 1, R > 0 ? R : 1,
+                                                             M > 0 ? M : 1, ell > 0 ? ell : 1,
+                                                             T > 0 ? T : 0));
+  // per-layer checks as for dbf_forward, on layer 0's slice of the workspace
+  dbf_status st = check_common(x, ldx, N, R, M, ell, T, y, ldy, y_type, flags, ws,
+                               ws_bytes / (size_t)num_layers);
+  if (st != DBF_OK || T == 0) return st;
+  if (ws_bytes < layer_ws * (size_t)num_layers) return DBF_ERR_WORKSPACE;
+  const int64_t esz = y_type == DBF_F32 ? 4 : 2;
+  if (num_layers > 1 && y_layer_stride < ldy * (T - 1) + N) return DBF_ERR_INVALID_ARG;
+  if ((y_layer_stride * esz) % 16 != 0) return DBF_ERR_ALIGNMENT;
+  dbf::ForwardArgs a{};
+  for (int j = 0; j < num_layers; ++j) {
+    if (B1s[j] == nullptr || B2s[j] == nullptr || alphas[j] == nullptr || betas[j] == nullptr ||
+        gammas[j] == nullptr)
+      return DBF_ERR_INVALID_ARG;
+    if (!aligned16(B1s[j]) || !aligned16(B2s[j])) return DBF_ERR_ALIGNMENT;
+    if ((((uintptr_t)alphas[j]) | ((uintptr_t)betas[j]) | ((uintptr_t)gammas[j])) & 1u)
+      return DBF_ERR_ALIGNMENT;
+    a.grp[j] = dbf::Factors{B1s[j], B2s[j], (const dbf::half_t*)alphas[j],
+                            (const dbf::half_t*)betas[j], (const dbf::half_t*)gammas[j]};
+  }
+  a.x = (const dbf::half_t*)x;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.y_f32 = (y_type == DBF_F32);
+  a.accumulate = (flags & DBF_ACCUMULATE) != 0;
+  a.N = N;
+  a.R = R;
+  a.M = M;
+  a.T = T;
+  a.ell = ell;
+  a.multi = false;
+  a.ws = ws;
+  a.ws_bytes = layer_ws;
+  a.path = pick_path(flags, T, T);
+  a.phases = phases_of(flags);
+  a.group = num_layers;
+  a.y_layer_bytes = y_layer_stride * esz;
+  a.layer_ws = layer_ws;
+  return hip_status(dbf::launch_forward_grouped(a, (hipStream_t)stream));
+}
+
 dbf_status dbf_backward_workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T,
                                         size_t* bytes) {
   if (N <= 0 || R <= 0 || M <= 0 || ell < 1 || T <= 0 || bytes == nullptr)

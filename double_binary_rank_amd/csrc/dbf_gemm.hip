@@ -68,6 +68,12 @@ struct GemmParams {
   int64_t ldy;
   int64_t y_term;  // stage 3: floats per term of the output
   Factors single;
+  // grouped same-input layers: work items of layer j follow those of j-1;
+  // layer j reads grp[j], and offsets z / opnd by j*layer_ws bytes, y by
+  // j*y_layer_bytes
+  int32_t group;
+  int64_t layer_ws, y_layer_bytes;
+  Factors grp[kMaxGroup];
   const ColBlock* cbl;
   const WsHeader* hdr;
   const uint32_t* const* B1s;
@@ -279,9 +285,10 @@ __global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
   }
 }
 
-template <int STAGE, int NC, bool SPLITK, bool MULTI, bool XIN, int NWV>
+template <int STAGE, int NC, bool SPLITK, bool MULTI, bool XIN, int NWV, bool GROUP>
 __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
   static_assert(!XIN || (STAGE == 1 && !MULTI), "x is read in place by single-adapter stage 1");
+  static_assert(!GROUP || (!MULTI && STAGE != 3), "grouped layers take the single-adapter stages");
   static_assert(NWV == 4 || (SPLITK && NC == 2 && NWV == 8), "8 waves only split a reduction");
   constexpr int D = 2;  // operand buffers per wave (deeper rings measured slower)
   constexpr int TPW = 4 * NC / NWV;  // SPLITK: output tiles each wave finishes
@@ -294,7 +301,8 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
   const uint32_t one = p.one16;
   // item counts fit 32 bits (the workspace bounds T * R; the host checks)
   const int n_cb = MULTI ? p.hdr->n_colblocks : p.n_cb_host;
-  const int n_items = n_cb * p.n_rg;
+  const int n_per = n_cb * p.n_rg;  // items of one layer
+  const int n_items = GROUP ? n_per * p.group : n_per;
   // consecutive items share a column block; with the remap the items of one
   // XCD (workgroups b, b+8, ...) are consecutive, so they share operand
   // tiles in that XCD's L2
@@ -302,7 +310,15 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
   const int first = p.xcd_remap ? (b & 7) * (p.grid >> 3) + (b >> 3) : b;
 
   for (int it = first; it < n_items; it += p.grid) {
-    const int cb = it / p.n_rg, rg = it - cb * p.n_rg;
+    int layer = 0, itl = it;
+    if constexpr (GROUP) {
+      layer = it / n_per;
+      itl = it - layer * n_per;
+    }
+    const int cb = itl / p.n_rg, rg = itl - cb * p.n_rg;
+    half_t* const zl = (half_t*)((char*)p.z + (GROUP ? layer * p.layer_ws : 0));
+    const half_t* const ol = (const half_t*)((const char*)p.opnd + (GROUP ? layer * p.layer_ws : 0));
+    void* const yl = (char*)p.y + (GROUP ? layer * p.y_layer_bytes : 0);
     int t0, t1, ad;
     Factors f;
     if (MULTI) {
@@ -320,7 +336,7 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
       t0 = cb * 16 * NC;
       t1 = t0 + 16 * NC < p.T ? t0 + 16 * NC : p.T;
       ad = 0;
-      f = p.single;
+      f = GROUP ? p.grp[layer] : p.single;
     }
     const int q = SPLITK ? rg : 4 * rg + wv;  // row quad of this wave
     const int row_lo = (SPLITK ? rg : 4 * rg) * kQuad * kRowTile;
@@ -375,7 +391,7 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int t = min(t0 + 16 * c + c16, t1 - 1);
-          orow[c] = p.opnd + i * p.opnd_term + (int64_t)(t >> 4) * p.opnd_nkb * 2048 +
+          orow[c] = ol + i * p.opnd_term + (int64_t)(t >> 4) * p.opnd_nkb * 2048 +
                     (16 * g + (t & 15)) * 8;
         }
       }
@@ -474,13 +490,13 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
             // rows r0..r0+3 share one 8-entry chunk of the z tile; rows past
             // R get scale 0, so the chunk is written whole
             if (t < t1)
-              *(v4h*)(p.z + i * p.z_term + tile_off(t, r0, p.z_nkb)) =
+              *(v4h*)(zl + i * p.z_term + tile_off(t, r0, p.z_nkb)) =
                   v4h{(half_t)(sum[0] * sc[0]), (half_t)(sum[1] * sc[1]),
                       (half_t)(sum[2] * sc[2]), (half_t)(sum[3] * sc[3])};
           } else if (STAGE == 3) {
             if (t < t1 && r0 < p.rows) {
               const float o[4] = {sum[0], sum[1], sum[2], sum[3]};
-              store4((float*)p.y + i * p.y_term, p.ldy, true, t, r0, p.rows, o);
+              store4((float*)yl + i * p.y_term, p.ldy, true, t, r0, p.rows, o);
             }
           } else {
 #pragma unroll
@@ -492,11 +508,11 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
               float o[4] = {ys[e][0], ys[e][1], ys[e][2], ys[e][3]};
               if (p.accumulate) {
                 float old[4];
-                load4(p.y, p.ldy, p.y_f32, t, r0, p.rows, old);
+                load4(yl, p.ldy, p.y_f32, t, r0, p.rows, old);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) o[v] += old[v];
               }
-              store4(p.y, p.ldy, p.y_f32, t, r0, p.rows, o);
+              store4(yl, p.ldy, p.y_f32, t, r0, p.rows, o);
             }
           }
         }
@@ -509,7 +525,7 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
             if (t < t1)
 #pragma unroll
               for (int h = 0; h < 4; ++h)
-                *(v4h*)(p.z + i * p.z_term + tile_off(t, p.nq * 64 + h * 16 + 4 * g, p.z_nkb)) =
+                *(v4h*)(zl + i * p.z_term + tile_off(t, p.nq * 64 + h * 16 + 4 * g, p.z_nkb)) =
                     v4h{};
           }
         }
@@ -708,24 +724,24 @@ inline bool eight_waves(const GemmParams& p) {
   return !p.multi && p.nkb >= 4 && !wide_blocks(p) && cdiv(p.T, 32) * p.nq <= kComputeUnits;
 }
 
-template <int STAGE, int NC, bool SPLITK, bool MULTI, bool XIN>
+template <int STAGE, int NC, bool SPLITK, bool MULTI, bool XIN, bool GROUP>
 hipError_t launch_k(const GemmParams& p, int64_t grid, bool wide, hipStream_t s) {
   if constexpr (SPLITK && !MULTI && NC == 2) {  // 64-token blocks would spill at 8 waves
     if (wide) {
-      hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK, MULTI, XIN, 8>), dim3((unsigned)grid), dim3(512),
-                         0, s, p);
+      hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK, MULTI, XIN, 8, GROUP>), dim3((unsigned)grid),
+                         dim3(512), 0, s, p);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK, MULTI, XIN, 4>), dim3((unsigned)grid), dim3(256), 0,
-                     s, p);
+  hipLaunchKernelGGL((k_gemm<STAGE, NC, SPLITK, MULTI, XIN, 4, GROUP>), dim3((unsigned)grid),
+                     dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <int STAGE, int NC, bool SPLITK>
 hipError_t launch_one(GemmParams p, hipStream_t s) {
   p.n_rg = SPLITK ? p.nq : (p.nq + 3) / 4;
-  const int64_t items = (int64_t)p.n_cb_host * p.n_rg;
+  const int64_t items = (int64_t)p.n_cb_host * p.n_rg * (p.group > 1 ? p.group : 1);
   if (items > INT32_MAX) return hipErrorInvalidValue;
   int64_t grid = items;
   if (p.multi && grid > 8192) grid = 8192;
@@ -733,12 +749,20 @@ hipError_t launch_one(GemmParams p, hipStream_t s) {
   // consecutive items cannot be mapped to one XCD
   p.xcd_remap = (!p.multi && grid == items && items % 8 == 0) ? 1 : 0;
   p.grid = (int32_t)grid;
+  // the wave count follows one layer's items, as for a single call
   const bool wide = eight_waves(p);
-  if (p.multi) return launch_k<STAGE, NC, SPLITK, true, false>(p, grid, false, s);
-  if constexpr (STAGE == 1 && NC == 2) {
-    if (p.x != nullptr) return launch_k<1, NC, SPLITK, false, true>(p, grid, wide, s);
+  if (p.multi) return launch_k<STAGE, NC, SPLITK, true, false, false>(p, grid, false, s);
+  if (p.group > 1) {
+    if constexpr (STAGE == 2) return launch_k<2, NC, SPLITK, false, false, true>(p, grid, wide, s);
+    if constexpr (STAGE == 1 && NC == 2) {
+      if (p.x != nullptr) return launch_k<1, NC, SPLITK, false, true, true>(p, grid, wide, s);
+    }
+    return hipErrorNotSupported;
   }
-  return launch_k<STAGE, NC, SPLITK, false, false>(p, grid, wide, s);
+  if constexpr (STAGE == 1 && NC == 2) {
+    if (p.x != nullptr) return launch_k<1, NC, SPLITK, false, true, false>(p, grid, wide, s);
+  }
+  return launch_k<STAGE, NC, SPLITK, false, false, false>(p, grid, wide, s);
 }
 
 template <int STAGE>
@@ -869,6 +893,25 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   if (xin) {
     p1.x = a.x;
     p1.ldx = a.ldx;
+  }
+  if (a.group > 1) {
+    // one launch per stage for every layer: stage 1 reads x in place for all
+    // of them and stage 2 is not the short-rank register kernel; otherwise the
+    // caller runs the layers one by one (nothing has been launched)
+    bool ok = xin && (int64_t)a.ell * p2.nkb > 2;
+    for (int j = 0; j < a.group; ++j) ok = ok && (((uintptr_t)a.grp[j].gamma) & 15u) == 0;
+    if (!ok) return hipErrorNotSupported;
+    for (GemmParams* q : {&p1, &p2}) {
+      q->group = a.group;
+      q->layer_ws = (int64_t)a.layer_ws;
+      q->y_layer_bytes = a.y_layer_bytes;
+      for (int j = 0; j < a.group; ++j) q->grp[j] = a.grp[j];
+    }
+    if (a.phases & 2) {
+      const hipError_t e = launch_stage<1>(p1, s);
+      if (e != hipSuccess) return e;
+    }
+    return (a.phases & 4) ? launch_stage<2>(p2, s) : hipSuccess;
   }
 
   if ((a.phases & 1) && !xin) {

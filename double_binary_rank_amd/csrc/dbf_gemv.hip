@@ -212,6 +212,11 @@ struct GemvParams {
   const uint32_t* const* B2s;
   const half_t* const* alphas;
   const half_t* const* betas;
+  // grouped same-input layers (PIN stages): layer j reads grp[j] and offsets
+  // z by j*layer_ws bytes, y by j*y_layer_bytes
+  int32_t group;
+  int64_t layer_ws, y_layer_bytes;
+  Factors grp[kMaxGroup];
 };
 
 // Epilogue of one row tile: `sum` is the fp32 MFMA tile of this lane (rows
@@ -230,9 +235,9 @@ __device__ inline float row_next(float v) {
 }
 
 template <int STAGE, bool SCALE_LDS = false>
-__device__ inline void gemv_epilogue(const GemvParams& p, const half_t* srow, v4f sum,
-                                     int64_t tile, int lane, int g, int part, bool colv, int ci,
-                                     int ct, int ntok, int64_t t0) {
+__device__ inline void gemv_epilogue(const GemvParams& p, float* zb, void* yb, const half_t* srow,
+                                     v4f sum, int64_t tile, int lane, int g, int part, bool colv,
+                                     int ci, int ct, int ntok, int64_t t0) {
   const int64_t r0 = tile * kRowTile + 4 * g;
   // the parts of a column are lanes j, j+1, j+2 of one row of 16 (j <= 13)
   float tot[4];
@@ -254,7 +259,7 @@ __device__ inline void gemv_epilogue(const GemvParams& p, const half_t* srow, v4
       float o[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) o[v] = tot[v] * sc[v];
-      store4(p.z + ci * p.zstride, p.ldz, true, t0 + ct, r0, p.rows, o);
+      store4(zb + ci * p.zstride, p.ldz, true, t0 + ct, r0, p.rows, o);
     }
   } else {
     float val[4];
@@ -277,11 +282,11 @@ __device__ inline void gemv_epilogue(const GemvParams& p, const half_t* srow, v4
     if (part == 0 && colv && ci == 0 && r0 < p.rows) {
       if (p.accumulate) {
         float old[4];
-        load4(p.y, p.ldy, p.y_f32, t0 + ct, r0, p.rows, old);
+        load4(yb, p.ldy, p.y_f32, t0 + ct, r0, p.rows, old);
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[v] += old[v];
       }
-      store4(p.y, p.ldy, p.y_f32, t0 + ct, r0, p.rows, o);
+      store4(yb, p.ldy, p.y_f32, t0 + ct, r0, p.rows, o);
     }
   }
 }
@@ -300,9 +305,10 @@ __device__ inline void gemv_epilogue(const GemvParams& p, const half_t* srow, v4
 constexpr int kPinColTokens = 2;                // PIN: ell * tokens per column block
 constexpr int kPinCols = kParts * kPinColTokens;  // PIN: live operand columns
 
-template <int STAGE, int RTG, int KC, bool MULTI, bool PIN = false, int NW = 4>
+template <int STAGE, int RTG, int KC, bool MULTI, bool PIN = false, int NW = 4, bool GROUP = false>
 __global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
   static_assert(!PIN || !MULTI, "operand parts are built in place for one adapter");
+  static_assert(!GROUP || PIN, "grouped layers take the parts-building stages");
   __shared__ v4f red[NW][RTG][64];
   // PIN: the wave's parts, [block][column][128 bytes], and their scale codes
   // (at most kPinCols live columns)
@@ -316,11 +322,19 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
   const int c = j / kParts, part = j - kParts * (j / kParts);
   // item counts fit 32 bits (the host checks)
   const int n_cb = MULTI ? p.hdr->n_colblocks : (int)p.n_cb_host;
-  const int n_items = n_cb * (int)p.n_rg;
+  const int n_per = n_cb * (int)p.n_rg;  // items of one layer
+  const int n_items = GROUP ? n_per * p.group : n_per;
   const int grid = (int)p.grid;
 
   for (int it = blockIdx.x; it < n_items; it += grid) {
-    const int cb = it / (int)p.n_rg, rg = it - cb * (int)p.n_rg;
+    int layer = 0, itl = it;
+    if constexpr (GROUP) {
+      layer = it / n_per;
+      itl = it - layer * n_per;
+    }
+    const int cb = itl / (int)p.n_rg, rg = itl - cb * (int)p.n_rg;
+    float* const zl = (float*)((char*)p.z + (GROUP ? layer * p.layer_ws : 0));
+    void* const yl = (char*)p.y + (GROUP ? layer * p.y_layer_bytes : 0);
     int64_t t0, t1;
     int32_t ad;
     Factors f;
@@ -339,7 +353,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
       t0 = (int64_t)cb * p.tcb;
       t1 = t0 + p.tcb < p.T ? t0 + p.tcb : p.T;
       ad = 0;
-      f = p.single;
+      f = GROUP ? p.grp[layer] : p.single;
     }
     const int64_t tile0 = (int64_t)rg * RTG;
     if (ad < 0) {
@@ -402,7 +416,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
                 if (k < p.K) v0 = (float)gi[k] * (float)xr[k];
                 if (k + 1 < p.K) v1 = (float)gi[k + 1] * (float)xr[k + 1];
               } else {
-                const float* zr = p.z + ci2 * p.zstride + t * p.ldz;
+                const float* zr = zl + ci2 * p.zstride + t * p.ldz;
                 if (k < p.K) v0 = zr[k];
                 if (k + 1 < p.K) v1 = zr[k + 1];
               }
@@ -469,7 +483,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
 #pragma unroll
       for (int w = 1; w < NW; ++w) sum += red[w][rt][lane];
       const half_t* srow = (STAGE == 1 ? f.beta : f.alpha) + (int64_t)ci * p.rows;
-      gemv_epilogue<STAGE>(p, srow, sum, tile, lane, g, part, colv, ci, ct, ntok, t0);
+      gemv_epilogue<STAGE>(p, zl, yl, srow, sum, tile, lane, g, part, colv, ci, ct, ntok, t0);
     }
     __syncthreads();
   }
@@ -724,7 +738,7 @@ __global__ __launch_bounds__(256) void k_gemv_stream(GemvParams p) {
     for (int e = 0; e < QPW * 4; ++e) {
       const int64_t tile = (qw0 + 4 * (e >> 2)) * kQuad + (e & 3);
       if (e < nqw * 4 && tile < p.nrt)
-        gemv_epilogue<STAGE, true>(p, srow, partial[(wv * QPW * 4 + e) * 64 + lane], tile, lane, g,
+        gemv_epilogue<STAGE, true>(p, p.z, p.y, srow, partial[(wv * QPW * 4 + e) * 64 + lane], tile, lane, g,
                                    part, colv, ci, ct, ntok, t0);
     }
   }
@@ -1153,15 +1167,20 @@ template <int STAGE>
 static hipError_t launch_gemv_pin(GemvParams p, int kc, hipStream_t s) {
   p.nq = cdiv(p.nrt, kQuad);
   p.n_rg = cdiv(p.nrt, kQuad);
-  const int64_t grid = p.n_cb_host * p.n_rg;
+  const int64_t grid = p.n_cb_host * p.n_rg * (p.group > 1 ? p.group : 1);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   p.grid = grid;
-  if (kc == 1)
-    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 1, false, true, 16>), dim3((unsigned)grid), dim3(1024),
-                       0, s, p);
-  else
-    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 2, false, true, 16>), dim3((unsigned)grid), dim3(1024),
-                       0, s, p);
+  const dim3 g((unsigned)grid), b(1024);
+  if (p.group > 1) {
+    if (kc == 1)
+      hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 1, false, true, 16, true>), g, b, 0, s, p);
+    else
+      hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 2, false, true, 16, true>), g, b, 0, s, p);
+  } else if (kc == 1) {
+    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 1, false, true, 16>), g, b, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 2, false, true, 16>), g, b, 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -1321,6 +1340,18 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
     return nkb <= 16 ? 1 : nkb <= 32 ? 2 : 0;
   };
   const int kc1 = pin_kc(g1.nkb), kc2 = pin_kc(g2.nkb);
+  if (a.group > 1) {
+    // one launch per stage for every layer when both stages build their own
+    // parts; otherwise the caller runs the layers one by one (nothing has
+    // been launched)
+    if (kc1 == 0 || kc2 == 0) return hipErrorNotSupported;
+    for (GemvParams* q : {&g1, &g2}) {
+      q->group = a.group;
+      q->layer_ws = (int64_t)a.layer_ws;
+      q->y_layer_bytes = a.y_layer_bytes;
+      for (int j = 0; j < a.group; ++j) q->grp[j] = a.grp[j];
+    }
+  }
 
   // stage 1: z = beta * (S2 . (gamma * x))
   if (kc1 > 0) {

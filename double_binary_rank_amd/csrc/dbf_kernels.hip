@@ -149,4 +149,25 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
   return launch_gemm(a, s);
 }
 
+// Same-input layers: the grouped kernels run every layer in one launch per
+// stage when the fast stages apply to all of them (the path launchers
+// return hipErrorNotSupported, before launching anything, when they do
+// not); otherwise the layers run one by one, each on its workspace slice.
+hipError_t launch_forward_grouped(const ForwardArgs& a0, hipStream_t s) {
+  ForwardArgs a = a0;
+  a.single = a0.grp[0];
+  hipError_t e = launch_forward(a, s);
+  if (e != hipErrorNotSupported) return e;
+  for (int j = 0; j < a0.group; ++j) {
+    ForwardArgs b = a0;
+    b.group = 0;
+    b.single = a0.grp[j];
+    b.y = (char*)a0.y + j * a0.y_layer_bytes;
+    b.ws = (char*)a0.ws + j * a0.layer_ws;
+    b.ws_bytes = a0.layer_ws;
+    if ((e = launch_forward(b, s)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace dbf

@@ -8,6 +8,9 @@ namespace dbf {
 // Which kernel family evaluates the two sign-accumulation stages.
 enum class Path : int { Gemv = 0, Mfma = 1 };
 
+// Largest number of same-input layers in one grouped call.
+constexpr int kMaxGroup = 8;
+
 struct ForwardArgs {
   // activations and output
   const half_t* x;
@@ -34,6 +37,12 @@ struct ForwardArgs {
   size_t ws_bytes;
   Path path;
   int phases;  // bit 0: prep (operands of stage 1), bit 1: stage 1 (z), bit 2: stage 2 (y)
+  // grouped same-input layers (group > 1): layer j has factors grp[j], writes
+  // y + j * y_layer_bytes and uses ws + j * layer_ws
+  int32_t group;
+  Factors grp[kMaxGroup];
+  int64_t y_layer_bytes;
+  size_t layer_ws;
 };
 
 // Largest batch the small-T (fp4 matrix-core) path accepts; its operand
@@ -96,6 +105,7 @@ hipError_t launch_unpack(const uint32_t* src, int64_t rows, int64_t cols, int8_t
 hipError_t launch_transpose(const uint32_t* src, int64_t rows, int64_t cols, uint32_t* dst,
                             hipStream_t s);
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t s);
 Path choose_path(int64_t T, int64_t tokens_per_segment_estimate);
 // tokens per column block on the small-T path (3 fp8 parts x ell terms
 // x tokens must fit the 16 columns of one MFMA); 0 if ell is too large.

@@ -192,6 +192,46 @@ dbf_status dbf_forward_multi_adapter(const void* x, int64_t ldx, int64_t T, cons
                                      size_t ws_bytes, void* stream);
 
 /*
+ * Workspace bytes needed by dbf_forward_grouped: num_layers (1..8) slices,
+ * each the dbf_workspace_bytes of one layer rounded up to 256 bytes.
+ * Errors: INVALID_ARG as for dbf_workspace_bytes, or num_layers outside
+ * 1..8.
+ */
+dbf_status dbf_grouped_workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T,
+                                       int32_t num_layers, size_t* bytes);
+
+/*
+ * Several layers on the same input (the q/k/v or up/gate projections of a
+ * decoder layer: LoRDBA summary, section 1, adapters evaluated unmerged next
+ * to the base layers; decode throughput is the DBF summary's second speed
+ * figure, section 4): for j < num_layers,
+ *   y_j = sum_i diag(alpha_ji) B1_j diag(beta_ji) B2_j diag(gamma_ji) x
+ * written to y + j * y_layer_stride elements (with DBF_ACCUMULATE added onto
+ * it: the fused add into the base layers' outputs).  Every layer has the
+ * same N, R, M and ell.  B1s .. gammas are HOST arrays of num_layers device
+ * pointers (1 <= num_layers <= 8), each checked as in dbf_forward.  When
+ * both stages of the chosen path can run every layer in one launch (the
+ * decode stages that build their own operand parts; the large-T stages with
+ * x read in place and a reduction of more than 2 blocks in stage 2) they
+ * do, otherwise the layers run one after another; either way each layer's
+ * result is bit for bit that of dbf_forward on it.
+ *   y_layer_stride  elements between layers' outputs: at least
+ *                   ldy * (T - 1) + N when num_layers > 1, and a multiple
+ *                   of 16 bytes
+ *   ws              dbf_grouped_workspace_bytes bytes
+ * Errors as for dbf_forward, plus INVALID_ARG for num_layers outside 1..8, a
+ * null table or layer pointer, or overlapping outputs, and ALIGNMENT for
+ * the stride.
+ */
+dbf_status dbf_forward_grouped(const void* x, int64_t ldx, int64_t T, int32_t num_layers,
+                               const uint32_t* const* B1s, const uint32_t* const* B2s,
+                               const void* const* alphas, const void* const* betas,
+                               const void* const* gammas, int64_t N, int64_t R, int64_t M,
+                               int32_t ell, void* y, int64_t ldy, int64_t y_layer_stride,
+                               dbf_dtype y_type, uint32_t flags, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
  * Workspace bytes needed by dbf_backward for these sizes.
  * Errors: INVALID_ARG if N, R, M <= 0 (or above DBF_MAX_DIM), ell < 1,
  * T <= 0 or bytes == NULL.

@@ -258,3 +258,36 @@ def test_factorize_workspace_bytes():
     assert out.value > small > 0
     assert L.dbf_factorize_workspace_bytes(0, 48, 8, ctypes.byref(out)) == _lib.DBF_ERR_INVALID_ARG
     assert L.dbf_factorize_workspace_bytes(64, 48, 8, None) == _lib.DBF_ERR_INVALID_ARG
+
+
+def _grp(**kw):
+    arr = (ctypes.c_void_p * 3)(A, A, A)
+    a = dict(x=A, ldx=64, T=4, J=3, B1s=arr, B2s=arr, alphas=arr, betas=arr, gammas=arr, N=32,
+             R=16, M=64, ell=1, y=A, ldy=32, ys=32 * 4, y_type=_lib.DBF_F16, flags=0, ws=A,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.dbf_forward_grouped(*a.values())
+
+
+def test_grouped_rejects():
+    arr0 = (ctypes.c_void_p * 3)(A, None, A)
+    mis = (ctypes.c_void_p * 3)(A, MIS, A)
+    odd = (ctypes.c_void_p * 3)(A, A + 1, A)
+    assert _grp(J=0) == _lib.DBF_ERR_INVALID_ARG
+    assert _grp(J=9) == _lib.DBF_ERR_INVALID_ARG
+    assert _grp(B1s=None) == _lib.DBF_ERR_INVALID_ARG
+    assert _grp(B2s=arr0) == _lib.DBF_ERR_INVALID_ARG
+    assert _grp(B1s=mis) == _lib.DBF_ERR_ALIGNMENT
+    assert _grp(gammas=odd) == _lib.DBF_ERR_ALIGNMENT
+    assert _grp(ys=32 * 3) == _lib.DBF_ERR_INVALID_ARG      # outputs would overlap
+    assert _grp(ys=32 * 4 + 4) == _lib.DBF_ERR_ALIGNMENT    # 8 bytes off 16
+    assert _grp(ldx=63) == _lib.DBF_ERR_INVALID_ARG
+    assert _grp(ws_bytes=1024) == _lib.DBF_ERR_WORKSPACE
+    assert _grp(T=0) == _lib.DBF_OK  # no-op
+    out = ctypes.c_size_t(0)
+    assert L.dbf_grouped_workspace_bytes(32, 16, 64, 1, 4, 3, ctypes.byref(out)) == _lib.DBF_OK
+    one = ctypes.c_size_t(0)
+    assert L.dbf_grouped_workspace_bytes(32, 16, 64, 1, 4, 1, ctypes.byref(one)) == _lib.DBF_OK
+    assert out.value == 3 * one.value
+    assert L.dbf_grouped_workspace_bytes(32, 16, 64, 1, 4, 9, ctypes.byref(out)) == \
+        _lib.DBF_ERR_INVALID_ARG

@@ -737,3 +737,56 @@ def test_factorised_layer_runs_forward():
 def dbf_mod():
     import double_binary_rank_amd as dbf
     return dbf
+
+
+# ---------------------------------------------------- grouped layers --
+GROUP_CASES = [
+    (300, 130, 264, 1, 1, 3),   # decode, stages build their parts: one launch each
+    (256, 512, 1024, 2, 1, 2),  # two terms, one token
+    (200, 136, 520, 1, 2, 3),   # two tokens
+    (136, 300, 520, 1, 70, 3),  # large T, x read in place, a partial last block
+    (64, 390, 904, 1, 33, 8),   # eight layers
+    (40, 300, 260, 1, 37, 2),   # M not a multiple of 8: layers one by one
+    (96, 64, 128, 2, 20, 2),    # short-rank stage 2: layers one by one
+    (72, 400, 8000, 1, 300, 2),  # a long reduction: prep launch, layers one by one
+]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES)
+def test_grouped_equals_single_calls(case):
+    """Several layers on one x in one call: each layer's output is bit for bit
+    that of dbf_forward on it, and within the bar of the oracle."""
+    N, R, M, ell, T, J = case
+    Ls = [synth.make_layer(N, R, M, ell, T, seed=400 + 10 * j + sum(case)) for j in range(J)]
+    x = H().to_dev_rows(Ls[0].x)
+    pls = [H().upload(L) for L in Ls]
+    y = dbf_mod().dbf_forward_grouped(x, pls)
+    singles = [p.forward(x) for p in pls]
+    torch.cuda.synchronize()
+    for j in range(J):
+        assert torch.equal(y[j], singles[j]), j
+        want = oracle.forward(Ls[0].x, Ls[j].S1, Ls[j].S2, Ls[j].alpha, Ls[j].beta, Ls[j].gamma)
+        assert oracle.max_norm_error(y[j].float().cpu().numpy(), want) <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_grouped_accumulate_integer(T):
+    """The fused add onto base outputs: integer data with unit scales, fp16
+    output, y_j = fp16(base_j + y_j) exactly, in a strided output buffer."""
+    N, R, M, J = 96, 300, 256, 3
+    Ls = [synth.make_layer(N, R, M, 1, T, seed=450 + j, alpha="ones", beta="ones", gamma="ones",
+                           x_kind="int3") for j in range(J)]
+    x = H().to_dev_rows(Ls[0].x)
+    pls = [H().upload(L) for L in Ls]
+    rng = np.random.default_rng(451)
+    base = rng.integers(-50, 50, size=(J, T, N)).astype(np.float16)
+    buf = torch.zeros((J, T + 3, 104), dtype=torch.float16, device="cuda")
+    y = buf[:, :T, :N]
+    y.copy_(torch.as_tensor(base).cuda())
+    dbf_mod().dbf_forward_grouped(x, pls, y=y, accumulate=True)
+    torch.cuda.synchronize()
+    for j in range(J):
+        want = oracle.fp16_rne(oracle.forward(Ls[0].x, Ls[j].S1, Ls[j].S2, Ls[j].alpha,
+                                              Ls[j].beta, Ls[j].gamma, y_old=base[j]))
+        assert np.array_equal(y[j].float().cpu().numpy().astype(np.float64), want), j
+    assert not bool(buf[:, T:, :].any()) and not bool(buf[:, :T, N:].any())
