@@ -39,6 +39,8 @@ invariances, and the pages' printed storage figures).
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 __all__ = [
@@ -54,6 +56,9 @@ __all__ = [
     "svid",
     "admm_scaled_sign",
     "factorize",
+    "rank_for_bits",
+    "channel_importance",
+    "prune_channels",
     "stage1",
     "fp16_rne",
     "max_norm_error",
@@ -382,6 +387,48 @@ def bits_per_weight(N: int, R: int, M: int, ell: int = 1) -> float:
     """Storage per entry of the N x M matrix the factors stand for
     ([DBF] "Control Granular de Compresion": the middle width k sets it)."""
     return (sign_bits(N, R, M) + 8 * scale_bytes(N, R, M, ell)) / (N * M)
+
+
+def rank_for_bits(N: int, M: int, bpw: float, ell: int = 1) -> int:
+    """[DBF] "Control Granular de Compresion": the middle width k sets the bits
+    per weight, so a (fractional) budget picks k: the largest k >= 0 with
+    bits_per_weight(N, k, M, ell) <= bpw, i.e. the floor of
+    (bpw N M - 16 ell (N + M)) / (N + M + 16 ell)."""
+    num = bpw * N * M - 16 * ell * (N + M)
+    return max(0, int(math.floor(num / (N + M + 16 * ell))))
+
+
+def channel_importance(alpha, beta, gamma) -> np.ndarray:
+    """[DBF] section 3, "Poda Iterativa No Uniforme": the middle dimension is
+    treated as channels and pruned by importance.  Reading (data-free, ell =
+    1): channel r contributes the rank-1 term beta_r (alpha . S1[:, r])
+    (S2[r, :] . gamma) to the update; its Frobenius norm, whatever the signs,
+    is |beta_r| ||alpha|| ||gamma||, the importance used here."""
+    a, b, g = _terms(alpha, beta, gamma)
+    if a.shape[0] != 1:
+        raise ValueError("channel importance is defined for ell = 1")
+    return np.abs(b[0]) * np.linalg.norm(a[0]) * np.linalg.norm(g[0])
+
+
+def prune_channels(shapes, importances, budget_bits):
+    """[DBF] "Poda Iterativa No Uniforme" over a stack of layers: repeatedly
+    drop the globally least important remaining channel (ties: lower layer,
+    then lower channel index first) until the stack's storage (sign bits plus
+    fp16 scales, ell = 1) fits budget_bits.  Dropping a channel of an N x M
+    layer saves N + M sign bits and one 16-bit beta entry.  shapes is a list
+    of (N, R, M); importances a list of length-R arrays.  Returns the kept
+    channel indices per layer (sorted)."""
+    keep = [np.ones(R, bool) for (_, R, _) in shapes]
+    total = sum(sign_bits(N, R, M) + 8 * scale_bytes(N, R, M, 1) for (N, R, M) in shapes)
+    order = sorted(((float(imp[r]), li, r) for li, imp in enumerate(importances)
+                    for r in range(len(imp))))
+    for _, li, r in order:
+        if total <= budget_bits:
+            break
+        N, _, M = shapes[li]
+        keep[li][r] = False
+        total -= N + M + 16
+    return [np.nonzero(k)[0] for k in keep]
 
 
 def compression_vs_fp16_lora(N: int, R: int, M: int, ell: int = 1) -> float:

@@ -741,3 +741,61 @@ def test_factorisation_pins_reject_mutants():
         f["beta"] = f["beta"][::-1].copy()
         return f
     assert not pin_factorize_fixed_point(fact_swapped)
+
+
+# ------------------------------------------- non-uniform ranks, pruning ----
+
+def test_rank_for_bits_brackets_the_budget():
+    """The chosen k is the largest whose storage (the pinned bits_per_weight
+    closed form) fits: k fits, k + 1 does not; and the pages' "1.5 bits per
+    weight" lands between the 1- and 2-bit configurations' ranks."""
+    for (N, M) in ((4096, 4096), (14336, 4096), (4096, 14336), (256, 256)):
+        for bpw in (1.0, 1.5, 2.0, 3.3):
+            k = oracle.rank_for_bits(N, M, bpw)
+            assert oracle.bits_per_weight(N, k, M) <= bpw + 1e-12
+            assert oracle.bits_per_weight(N, k + 1, M) > bpw
+    k1 = oracle.rank_for_bits(4096, 4096, 1.0)
+    k15 = oracle.rank_for_bits(4096, 4096, 1.5)
+    k2 = oracle.rank_for_bits(4096, 4096, 2.0)
+    assert k1 < k15 < k2
+    assert oracle.rank_for_bits(64, 64, 0.1) == 0
+
+
+def test_channel_importance_is_the_terms_norm():
+    """|beta_r| ||alpha|| ||gamma|| equals the Frobenius norm of the dense
+    update of channel r alone (delta_w with one middle channel)."""
+    rng = np.random.default_rng(50)
+    N, R, M = 9, 5, 7
+    S1 = np.where(rng.random((N, R)) < 0.5, -1, 1)
+    S2 = np.where(rng.random((R, M)) < 0.5, -1, 1)
+    a, b, c = rng.standard_normal(N), rng.standard_normal(R), rng.standard_normal(M)
+    imp = oracle.channel_importance(a, b, c)
+    for r in range(R):
+        dw = oracle.delta_w(S1[:, r:r + 1], S2[r:r + 1], a, b[r:r + 1], c)
+        assert abs(np.linalg.norm(dw) - imp[r]) < 1e-12
+
+
+def test_prune_channels_brute_force():
+    """On a tiny stack, the kept set fits the budget, dropping one more kept
+    channel is never needed, and every dropped channel is at most as
+    important as every kept one (the global greedy order)."""
+    rng = np.random.default_rng(51)
+    shapes = [(6, 4, 5), (3, 6, 8), (7, 3, 2)]
+    imps = [rng.random(R) for (_, R, _) in shapes]
+    full = sum(oracle.sign_bits(*s) + 8 * oracle.scale_bytes(*s, 1) for s in shapes)
+    for budget in (full, full - 1, full - 40, full // 2, 0):
+        keep = oracle.prune_channels(shapes, imps, budget)
+        used = sum(oracle.sign_bits(N, len(k), M) + 8 * oracle.scale_bytes(N, len(k), M, 1)
+                   for (N, _, M), k in zip(shapes, keep))
+        dropped = [imps[li][r] for li, (s, k) in enumerate(zip(shapes, keep))
+                   for r in range(s[1]) if r not in set(k)]
+        kept = [imps[li][r] for li, k in enumerate(keep) for r in k]
+        if kept and dropped:
+            assert max(dropped) <= min(kept)
+        assert used <= budget or not kept
+        if dropped:  # the last drop was needed: before it the stack did not fit
+            li, r = max(((li, r) for li, (s, k) in enumerate(zip(shapes, keep))
+                         for r in range(s[1]) if r not in set(k)),
+                        key=lambda t: (imps[t[0]][t[1]], t[0], t[1]))
+            N, _, M = shapes[li]
+            assert used + N + M + 16 > budget
