@@ -511,6 +511,101 @@ def main():
                 f" (graph replay), identical={same}")
         out["grouped_qkv_3x_attn"] = res
 
+    # ----- decoder-layer stack: non-uniform widths at 1.5 bits per weight --
+    if want("stack"):
+        n_dec, bpw = 2, 1.5
+        proj = [("q", 4096, 4096, -0.5), ("k", 4096, 4096, -0.5), ("v", 4096, 4096, 0.0),
+                ("o", 4096, 4096, 0.0), ("gate", 14336, 4096, -0.3), ("up", 14336, 4096, -0.3),
+                ("down", 4096, 14336, 0.3)]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(11)
+
+        def lognormal(n, mu):
+            z = torch.randn(n, generator=gen, device=dev, dtype=torch.float32)
+            return torch.exp(mu + 0.5 * z).to(torch.float16)[None].contiguous()
+
+        def make(N, M, R, off):
+            # signs Bernoulli(1/2); alpha, gamma ~ exp(N(-1, 0.5^2)); beta scaled so that
+            # the projection's gain is near 1 (times a per-type offset)
+            S1 = (torch.randint(0, 2, (N, R), generator=gen, device=dev, dtype=torch.int8) * 2 - 1)
+            S2 = (torch.randint(0, 2, (R, M), generator=gen, device=dev, dtype=torch.int8) * 2 - 1)
+            mu_b = off - math.log(math.exp(-2.25) * math.sqrt(R * M))
+            return dbf.PackedLayer(dbf.dbf_pack_signs(S1), dbf.dbf_pack_signs(S2),
+                                   lognormal(N, -1.0), lognormal(R, mu_b), lognormal(M, -1.0),
+                                   N, R, M)
+
+        full = [make(N, M, dbf.rank_for_bits(N, M, 2.0), off) for _ in range(n_dec)
+                for (_, N, M, off) in proj]
+        shapes = [(p_.N, p_.R, p_.M) for p_ in full]
+        budget = bpw * sum(N * M for (N, _, M) in shapes)
+        keep = dbf.plan_channels(shapes, [p_.channel_importance() for p_ in full], budget)
+        nonuni = [p_.select_channels(k) for p_, k in zip(full, keep)]
+        uni = [make(N, M, dbf.rank_for_bits(N, M, bpw), off) for _ in range(n_dec)
+               for (_, N, M, off) in proj]
+        del full
+        bits = lambda ls: sum(dbf.layer_bits(q.N, q.R, q.M) for q in ls)  # noqa: E731
+        weights = sum(N * M for (N, _, M) in shapes)
+        wsS = torch.empty(max(dbf.dbf_grouped_workspace_bytes(14336, 6400, 14336, 1, 256, 3), 16),
+                          dtype=torch.uint8, device=dev)
+
+        def chain(ls, h, bufs, grouped):
+            # per decoder layer: q, k, v on h; h += o(q); gate, up on h; h += down(up)
+            for d in range(n_dec):
+                b = 7 * d
+                if grouped:
+                    dbf.dbf_forward_grouped(h, ls[b:b + 3], y=bufs["qkv"], ws=wsS)
+                    q = bufs["qkv"][0]
+                else:
+                    q = ls[b].forward(h, y=bufs["q"], ws=wsS)
+                    ls[b + 1].forward(h, y=bufs["k"], ws=wsS)
+                    ls[b + 2].forward(h, y=bufs["v"], ws=wsS)
+                ls[b + 3].forward(q, y=h, accumulate=True, ws=wsS)
+                if grouped:
+                    dbf.dbf_forward_grouped(h, ls[b + 4:b + 6], y=bufs["gu"], ws=wsS)
+                    u = bufs["gu"][1]
+                else:
+                    ls[b + 4].forward(h, y=bufs["g"], ws=wsS)
+                    u = ls[b + 5].forward(h, y=bufs["u"], ws=wsS)
+                ls[b + 6].forward(u, y=h, accumulate=True, ws=wsS)
+
+        def timed(ls, Ts, grouped):
+            x0 = torch.randn((Ts, 4096), generator=gen, device=dev).to(torch.float16)
+            h = torch.empty_like(x0)
+            e16 = lambda *sh: torch.empty(sh, dtype=torch.float16, device=dev)  # noqa: E731
+            bufs = {"q": e16(Ts, 4096), "k": e16(Ts, 4096), "v": e16(Ts, 4096),
+                    "g": e16(Ts, 14336), "u": e16(Ts, 14336), "qkv": e16(3, Ts, 4096),
+                    "gu": e16(2, Ts, 14336)}
+
+            def step(_i):
+                h.copy_(x0)
+                chain(ls, h, bufs, grouped)
+
+            return time_graph(step, 8, max(args.steps // 20, 4), 2)
+
+        res = {"decoder_layers": n_dec, "projections": [p_[0] for p_ in proj], "target_bpw": bpw}
+        for name, ls, grouped in (("uniform", uni, False), ("uniform_grouped", uni, True),
+                                  ("nonuniform", nonuni, False)):
+            r = {"widths": [q.R for q in ls], "bpw": bits(ls) / weights}
+            for Ts in (1, 256):
+                t_ = timed(ls, Ts, grouped)
+                r[f"T{Ts}_us"] = t_ * 1e6
+                r[f"T{Ts}_tokens_per_s"] = Ts / t_
+            res[name] = r
+            log(f"stack {name}: {r['bpw']:.3f} bpw, decode {r['T1_us']:.1f} us/token, "
+                f"prefill T=256 {r['T256_us']:.1f} us")
+        # parity of the first pruned projection at T = 1
+        xq = torch.randn((1, 4096), generator=gen, device=dev).to(torch.float16)
+        p0 = nonuni[0]
+        yq = p0.forward(xq)
+        torch.cuda.synchronize()
+        S1h = dbf.dbf_unpack_signs(p0.B1, p0.N, p0.R).cpu().numpy()
+        S2h = dbf.dbf_unpack_signs(p0.B2, p0.R, p0.M).cpu().numpy()
+        res["parity_err_first_projection"] = oracle.max_norm_error(
+            yq.float().cpu().numpy(),
+            oracle.forward(xq.cpu().numpy(), S1h, S2h, p0.alpha.cpu().numpy(),
+                           p0.beta.cpu().numpy(), p0.gamma.cpu().numpy()))
+        out["decoder_stack_2x7_1p5bpw"] = res
+
     # ----------------------- factorisation of a dense 4096 x 4096 matrix --
     if want("factorize"):
         Nf = Mf = 4096

@@ -32,6 +32,9 @@ __all__ = [
     "dbf_factorize",
     "PackedLayer",
     "pointer_table",
+    "rank_for_bits",
+    "layer_bits",
+    "plan_channels",
 ]
 
 _DTYPE = {torch.int8: _lib.DBF_I8, torch.float16: _lib.DBF_F16, torch.float32: _lib.DBF_F32}
@@ -276,6 +279,47 @@ def dbf_factorize(W: torch.Tensor, k: int, omega: torch.Tensor | None = None, *,
     return out
 
 
+def layer_bits(N: int, R: int, M: int, ell: int = 1) -> int:
+    """Storage of one layer: N*R + R*M sign bits and 16-bit alpha, beta,
+    gamma per term (DBF summary, Control Granular de Compresion)."""
+    return N * R + R * M + 16 * ell * (N + R + M)
+
+
+def rank_for_bits(N: int, M: int, bpw: float, ell: int = 1) -> int:
+    """Largest middle width k whose storage is at most bpw bits per entry of
+    the N x M matrix (fractional budgets allowed)."""
+    k = int((bpw * N * M - 16 * ell * (N + M)) // (N + M + 16 * ell))
+    while k > 0 and layer_bits(N, k, M, ell) > bpw * N * M:
+        k -= 1
+    while layer_bits(N, k + 1, M, ell) <= bpw * N * M:
+        k += 1
+    return max(k, 0)
+
+
+def plan_channels(shapes, importances, budget_bits: float):
+    """Non-uniform middle widths for a stack (DBF summary, section 3,
+    iterative non-uniform pruning, read without data): drop the globally
+    least important channel (ties: earlier layer, then lower index) until the
+    stack's storage fits budget_bits.  shapes: (N, R, M) per layer (ell = 1);
+    importances: host arrays of length R, e.g. ``PackedLayer.channel_importance``.
+    Returns the sorted kept channel indices of each layer (host int64 arrays;
+    a layer may keep none)."""
+    import numpy as np
+
+    total = sum(layer_bits(N, R, M) for (N, R, M) in shapes)
+    cand = sorted((float(v), li, r) for li, imp in enumerate(importances)
+                  for r, v in enumerate(np.asarray(imp, dtype=np.float64)))
+    dropped = [set() for _ in shapes]
+    for _, li, r in cand:
+        if total <= budget_bits:
+            break
+        N, _, M = shapes[li]
+        dropped[li].add(r)
+        total -= N + M + 16
+    return [np.array([r for r in range(R) if r not in d], dtype=np.int64)
+            for (_, R, _), d in zip(shapes, dropped)]
+
+
 def pointer_table(tensors, device) -> torch.Tensor:
     """Device int64 array of the tensors' device addresses."""
     return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
@@ -348,6 +392,29 @@ class PackedLayer:
         """The layer of a ``dbf_factorize`` result (signs packed here)."""
         return cls(dbf_pack_signs(f["S1"]), dbf_pack_signs(f["S2"]), f["alpha"], f["beta"],
                    f["gamma"], f["S1"].shape[0], f["S1"].shape[1], f["S2"].shape[1])
+
+    def channel_importance(self):
+        """Per middle channel r (ell = 1): |beta_r| ||alpha|| ||gamma||, the
+        Frobenius norm of the channel's rank-1 term of the update; a host
+        float64 array."""
+        if self.ell != 1:
+            raise ValueError("channel importance is defined for ell = 1")
+        a = self.alpha.double().norm()
+        g = self.gamma.double().norm()
+        return (self.beta[0].double().abs() * a * g).cpu().numpy()
+
+    def select_channels(self, keep) -> "PackedLayer":
+        """The layer restricted to the middle channels ``keep`` (sorted
+        indices): columns of S1, rows of S2 and entries of beta.  Offline
+        re-packing (unpack, gather, pack on the device)."""
+        idx = torch.as_tensor(keep, dtype=torch.int64, device=self.B1.device)
+        if idx.numel() == 0:
+            raise ValueError("a layer needs at least one channel")
+        S1 = dbf_unpack_signs(self.B1, self.N, self.R)[:, idx].contiguous()
+        S2 = dbf_unpack_signs(self.B2, self.R, self.M)[idx].contiguous()
+        return PackedLayer(dbf_pack_signs(S1), dbf_pack_signs(S2), self.alpha,
+                           self.beta[:, idx].contiguous(), self.gamma, self.N, int(idx.numel()),
+                           self.M)
 
     def transposed_signs(self):
         """Packed S1^T (R x N) and S2^T (M x R), built once per layer."""

@@ -291,3 +291,23 @@ def test_grouped_rejects():
     assert out.value == 3 * one.value
     assert L.dbf_grouped_workspace_bytes(32, 16, 64, 1, 4, 9, ctypes.byref(out)) == \
         _lib.DBF_ERR_INVALID_ARG
+
+
+def test_rank_and_plan_match_the_definition():
+    import double_binary_rank_amd as dbf
+    """The library's host planning equals the oracle's definitions: the rank
+    for a bits budget, and the channels kept by non-uniform pruning."""
+    import numpy as np
+    import oracle
+    for (N, M) in ((4096, 4096), (14336, 4096), (300, 17)):
+        for bpw in (0.3, 1.0, 1.5, 2.0, 2.7):
+            assert dbf.rank_for_bits(N, M, bpw) == oracle.rank_for_bits(N, M, bpw)
+    rng = np.random.default_rng(60)
+    shapes = [(40, 12, 30), (17, 20, 9), (64, 7, 64), (5, 30, 11)]
+    imps = [rng.random(R) for (_, R, _) in shapes]
+    imps[1][3] = imps[0][5]  # a tie across layers
+    full = sum(dbf.layer_bits(*s) for s in shapes)
+    for frac in (1.0, 0.9, 0.6, 0.3, 0.0):
+        got = dbf.plan_channels(shapes, imps, frac * full)
+        want = oracle.prune_channels(shapes, imps, frac * full)
+        assert all(np.array_equal(g, w) for g, w in zip(got, want))

@@ -790,3 +790,72 @@ def test_grouped_accumulate_integer(T):
                                               Ls[j].beta, Ls[j].gamma, y_old=base[j]))
         assert np.array_equal(y[j].float().cpu().numpy().astype(np.float64), want), j
     assert not bool(buf[:, T:, :].any()) and not bool(buf[:, :T, N:].any())
+
+
+# -------------------------------- non-uniform ranks, decoder-layer stack --
+def test_select_channels_equals_oracle():
+    """A layer restricted to some middle channels equals the oracle on the
+    same columns of S1, rows of S2 and entries of beta."""
+    L = synth.make_layer(200, 130, 264, 1, 9, seed=500)
+    pl = H().upload(L)
+    keep = np.sort(np.random.default_rng(501).choice(130, 70, replace=False))
+    sub = pl.select_channels(keep)
+    y = sub.forward(H().to_dev_rows(L.x))
+    torch.cuda.synchronize()
+    want = oracle.forward(L.x, L.S1[:, keep], L.S2[keep], L.alpha, L.beta[:, keep], L.gamma)
+    assert sub.R == 70
+    assert oracle.max_norm_error(y.float().cpu().numpy(), want) <= TOL
+
+
+DEC_SMALL = [(64, 64), (64, 64), (64, 64), (64, 64), (160, 64), (160, 64), (64, 160)]
+
+
+@pytest.mark.parametrize("T", [1, 40])
+def test_pruned_decoder_stack_chain(T):
+    """Two synthetic decoder layers (q, k, v, o, gate, up, down; o and down
+    added onto the residual with DBF_ACCUMULATE), built at 2 bits per weight
+    and pruned non-uniformly to 1.5: the GPU chain equals an oracle chain that
+    rounds to fp16 where the GPU does, within the bar, and the plan fits the
+    budget with unequal widths."""
+    import double_binary_rank_amd as dbf
+    layers, host = [], []
+    for li in range(2):
+        for j, (N, M) in enumerate(DEC_SMALL):
+            R = dbf.rank_for_bits(N, M, 2.0)
+            # alpha = 1: each projection has a gain near 1, so the DBF
+            # branches move h as much as the residual does
+            L = synth.make_layer(N, R, M, 1, 0, seed=510 + 10 * li + j, alpha="ones",
+                                 x_kind="none")
+            host.append(L)
+            layers.append(H().upload(L))
+    shapes = [(p.N, p.R, p.M) for p in layers]
+    budget = 1.5 * sum(N * M for (N, _, M) in shapes)
+    keep = dbf.plan_channels(shapes, [p.channel_importance() for p in layers], budget)
+    assert sum(dbf.layer_bits(N, len(k), M) for (N, _, M), k in zip(shapes, keep)) <= budget
+    assert len({len(k) for k in keep}) > 1  # non-uniform
+    pruned = [p.select_channels(k) for p, k in zip(layers, keep)]
+    x = oracle.fp16_rne(np.random.default_rng(520).standard_normal((T, 64)))
+    h = H().to_dev_rows(x)
+    hr = x.copy()
+
+    def ref(j, inp):
+        L, k = host[j], keep[j]
+        return oracle.forward(inp, L.S1[:, k], L.S2[k], L.alpha, L.beta[:, k], L.gamma)
+
+    for li in range(2):
+        b = 7 * li
+        q = pruned[b].forward(h)
+        pruned[b + 1].forward(h)
+        pruned[b + 2].forward(h)
+        qr = oracle.fp16_rne(ref(b, hr))
+        h = h.clone()
+        pruned[b + 3].forward(q, y=h, accumulate=True)
+        hr = oracle.fp16_rne(hr + ref(b + 3, qr))
+        pruned[b + 4].forward(h)
+        u = pruned[b + 5].forward(h)
+        ur = oracle.fp16_rne(ref(b + 5, hr))
+        pruned[b + 6].forward(u, y=h, accumulate=True)
+        hr = oracle.fp16_rne(hr + ref(b + 6, ur))
+    torch.cuda.synchronize()
+    assert oracle.max_norm_error(h.float().cpu().numpy(), hr) <= TOL
+    assert oracle.max_norm_error(x, hr) > 0.5  # the layers changed h
