@@ -305,15 +305,29 @@ __device__ inline void gemv_epilogue(const GemvParams& p, float* zb, void* yb, c
 constexpr int kPinColTokens = 2;                // PIN: ell * tokens per column block
 constexpr int kPinCols = kParts * kPinColTokens;  // PIN: live operand columns
 
-template <int STAGE, int RTG, int KC, bool MULTI, bool PIN = false, int NW = 4, bool GROUP = false>
-__global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
+// LDS of one stage: the cross-wave partial tiles, then (PIN) each wave's
+// parts, [block][column][128 bytes], and their scale codes (at most kPinCols
+// live columns).
+template <int RTG, int KC, bool PIN, int NW>
+struct GemvLds {
+  static constexpr int red_bytes = NW * RTG * 64 * 16;
+  static constexpr int pinb_bytes = PIN ? NW * KC * kPinCols * 128 : 16;
+  static constexpr int pins_bytes = PIN ? NW * KC * kPinCols : 16;
+  static constexpr int bytes = red_bytes + pinb_bytes + pins_bytes;
+};
+
+// The work items it = first, first + stride, ... of one stage.
+template <int STAGE, int RTG, int KC, bool MULTI, bool PIN, int NW, bool GROUP>
+__device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvParams& p,
+                                                                     char* lds, int first,
+                                                                     int stride) {
   static_assert(!PIN || !MULTI, "operand parts are built in place for one adapter");
   static_assert(!GROUP || PIN, "grouped layers take the parts-building stages");
-  __shared__ v4f red[NW][RTG][64];
-  // PIN: the wave's parts, [block][column][128 bytes], and their scale codes
-  // (at most kPinCols live columns)
-  __shared__ uint8_t pin_b[PIN ? NW : 1][PIN ? KC * kPinCols * 128 : 1];
-  __shared__ uint8_t pin_s[PIN ? NW : 1][PIN ? KC * kPinCols : 1];
+  typedef GemvLds<RTG, KC, PIN, NW> Lds;
+  auto red = reinterpret_cast<v4f (*)[RTG][64]>(lds);
+  auto pin_b = reinterpret_cast<uint8_t (*)[Lds::pinb_bytes / NW]>(lds + Lds::red_bytes);
+  auto pin_s =
+      reinterpret_cast<uint8_t (*)[Lds::pins_bytes / NW]>(lds + Lds::red_bytes + Lds::pinb_bytes);
   static_assert(RTG % kQuad == 0, "row tiles come in quads");
   constexpr int RQ = RTG / kQuad;
   const int lane = threadIdx.x & 63;
@@ -324,9 +338,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
   const int n_cb = MULTI ? p.hdr->n_colblocks : (int)p.n_cb_host;
   const int n_per = n_cb * (int)p.n_rg;  // items of one layer
   const int n_items = GROUP ? n_per * p.group : n_per;
-  const int grid = (int)p.grid;
 
-  for (int it = blockIdx.x; it < n_items; it += grid) {
+  for (int it = first; it < n_items; it += stride) {
     int layer = 0, itl = it;
     if constexpr (GROUP) {
       layer = it / n_per;
@@ -487,6 +500,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
     }
     __syncthreads();
   }
+}
+
+template <int STAGE, int RTG, int KC, bool MULTI, bool PIN = false, int NW = 4, bool GROUP = false>
+__global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[GemvLds<RTG, KC, PIN, NW>::bytes];
+  gemv_fp4_items<STAGE, RTG, KC, MULTI, PIN, NW, GROUP>(p, lds, blockIdx.x, (int)p.grid);
 }
 
 // Stage the live B operand pieces of blocks [k0, k0 + nkc) of a column block

@@ -525,11 +525,13 @@ def test_segmentation_blocks(path, ell, chunk):
 
 # ------------------------------------------------------- split phases --
 @pytest.mark.parametrize("path", PATHS)
-@pytest.mark.parametrize("shape", [(300, 130, 260, 1, 37), (64, 16, 8, 3, 70), (96, 200, 8000, 1, 2)])
+@pytest.mark.parametrize("shape", [(300, 130, 260, 1, 37), (64, 16, 8, 3, 70), (96, 200, 8000, 1, 2),
+                                   (300, 130, 260, 2, 1), (4096, 2048, 4096, 1, 1)])
 def test_stage_split_equals_whole(shape, path):
     """The three phases run one at a time on one workspace give the whole
     call's result bit for bit, and the phases before stage 2 leave y
-    untouched."""
+    untouched (at decode sizes the whole call is one cooperative launch of
+    both stages, the phases two launches)."""
     N, R, M, ell, T = shape
     L = synth.make_layer(N, R, M, ell, T, seed=81)
     pl = H().upload(L)
