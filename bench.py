@@ -114,6 +114,34 @@ def time_graph(fn, n_calls, reps, warmup):
     return s.elapsed_time(e) / 1e3 / (reps * n_calls)
 
 
+def call_percentiles(fn, n_calls, warmup):
+    """p10 / median / p90 of per-call GPU time (µs): an event is recorded on
+    the stream between consecutive calls (outside the timed region)."""
+    for i in range(warmup):
+        fn(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n_calls):
+        fn(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n_calls)])
+    return {"p10": float(np.percentile(d, 10)), "median": float(np.median(d)),
+            "p90": float(np.percentile(d, 90)), "calls": n_calls}
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def replicate(t: torch.Tensor, k: int):
     return [t.clone() for _ in range(k)]
 
@@ -179,6 +207,29 @@ def summarize_pmc(fetch_dir, write_dir):
             "fetch_factor": f_fac, "write_factor": w_fac, "stages": stages}
 
 
+def summarize_trace(trace_dir, top=12):
+    """Markdown table of kernel durations from a rocprofv3 --kernel-trace
+    run: calls, mean, p10, median, p90, min, max and share of the summed
+    time per kernel name, from the per-dispatch timestamps."""
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    per = {}
+    for r in rows:
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault(r["Kernel_Name"], []).append(d)
+    total = sum(sum(v) for v in per.values()) or 1.0
+    lines = ["| kernel | calls | mean us | p10 us | median us | p90 us | min us | max us | share |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1]))[:top]:
+        a = np.array(v)
+        short = name if len(name) <= 70 else name[:67] + "..."
+        lines.append(f"| `{short}` | {len(a)} | {a.mean():.2f} | {np.percentile(a, 10):.2f} | "
+                     f"{np.median(a):.2f} | {np.percentile(a, 90):.2f} | {a.min():.2f} | "
+                     f"{a.max():.2f} | {100 * a.sum() / total:.1f}% |")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,9 +240,14 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run a {COPY_MIB} MiB device copy (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print a kernel duration table from a rocprofv3 --kernel-trace run")
     args = ap.parse_args()
     if args.summarize_pmc:
         print("traffic_json: " + json.dumps(summarize_pmc(*args.summarize_pmc)))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -244,6 +300,9 @@ def main():
         value = T / t_call
         achieved_tflops = flops / t_call / 1e12
         log(f"prefill T=256: {t_call * 1e6:.2f} us/call, {achieved_tflops:.1f} TFLOP/s")
+        out["prefill_T256_call_us"] = call_percentiles(call256, 200, 10)
+        log("prefill per-call us: " + ", ".join(
+            f"{k} {v:.2f}" for k, v in out["prefill_T256_call_us"].items() if k != "calls"))
 
         # each launch alone: stage 1 (z = beta * B2 (gamma x), reading x in
         # place; the prep phase launches nothing on this layer) and stage 2
@@ -292,6 +351,7 @@ def main():
         b1 = alg_bytes(N_, R_, M_, 1, 1)
         out["decode_T1"] = {
             "T": 1, "us_per_call": t1 * 1e6, "tokens_per_s": 1 / t1,
+            "call_us": call_percentiles(call1, 200, 10),
             "effective_GBs": b1 / t1 / 1e9, "hbm_frac": b1 / t1 / 1e9 / HBM_PEAK_GBS,
             "alg_bytes_per_call": b1, "parity_err": err1,
         }
@@ -663,8 +723,20 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: {COPY_MIB} MiB device copy x5")
 
+    # ------------------------------------- achievable HBM: a device copy --
+    if want("copy"):
+        n = COPY_MIB << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        sec = time_calls(lambda i: dst.copy_(src), 20, 3) / 20
+        out["device_copy"] = {"MiB": COPY_MIB, "GBs_read_plus_write": 2 * n / sec / 1e9,
+                              "hbm_frac": 2 * n / sec / 1e9 / HBM_PEAK_GBS}
+        log(f"device copy {COPY_MIB} MiB: {2 * n / sec / 1e9:.0f} GB/s read + write")
+        del src, dst
+
     # ------------------------------------------------------ CPU oracle --
     cpu = None
+    cpu_ctx = None
     if not args.no_cpu_baseline:
         try:
             from threadpoolctl import threadpool_info
@@ -680,6 +752,35 @@ def main():
                "sample": f"fp64 oracle on the same 4096x4096 R=2048 layer, T=256, "
                          f"{n_rep} calls in {dt:.1f} s"}
         log(f"cpu oracle: {cpu['value']:.0f} tokens/s on {cores} threads")
+        cpu_ctx = {"host_cpu": host_cpu_model(), "host_threads": os.cpu_count()}
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                n1, t1s = 0, time.perf_counter()
+                while time.perf_counter() - t1s < 5.0:
+                    oracle.forward(L.x, L.S1, L.S2, L.alpha, L.beta, L.gamma)
+                    n1 += 1
+                d1 = time.perf_counter() - t1s
+            cpu_ctx["oracle_1_thread_tokens_per_s"] = n1 * T / d1
+            log(f"cpu oracle, 1 thread: {n1 * T / d1:.0f} tokens/s")
+        except ImportError:  # pragma: no cover
+            pass
+        # the factored form against the dense update built from the factors
+        # (small configurations only: the dense update is N x M)
+        dense = {}
+        for cfg, tc, name in ((1, 4, "tiny_T4"), (2, 1, "lordba_T1")):
+            Lc = synth.make_config_layer(cfg, tc)
+            ta = time.perf_counter()
+            yf = oracle.forward(Lc.x, Lc.S1, Lc.S2, Lc.alpha, Lc.beta, Lc.gamma)
+            tf_ = time.perf_counter() - ta
+            ta = time.perf_counter()
+            dw = oracle.delta_w(Lc.S1, Lc.S2, Lc.alpha, Lc.beta, Lc.gamma)
+            yd = np.asarray(Lc.x, np.float64) @ dw.T
+            td_ = time.perf_counter() - ta
+            dense[name] = {"factored_s": tf_, "dense_dW_s": td_,
+                           "max_norm_diff": oracle.max_norm_error(yd, yf)}
+            log(f"cpu {name}: factored {tf_ * 1e3:.2f} ms, dense dW {td_ * 1e3:.1f} ms")
+        cpu_ctx["dense_vs_factored"] = dense
 
     line = {
         "metric": METRIC,
@@ -701,6 +802,7 @@ def main():
         "achieved_TFLOPs_per_call": achieved_tflops,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cpu_context": cpu_ctx,
         "cases": out,
     }
     print(json.dumps(line), flush=True)
