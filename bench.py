@@ -348,14 +348,19 @@ def main():
 
         n1 = max(args.steps, 256)
         t1 = time_calls(call1, n1, args.warmup) / n1
+        # the same calls captured in a HIP graph: the GPU's time per call,
+        # free of the host's launch rate
+        t1g = time_graph(call1, 64, max(args.steps // 16, 4), 2)
         b1 = alg_bytes(N_, R_, M_, 1, 1)
         out["decode_T1"] = {
             "T": 1, "us_per_call": t1 * 1e6, "tokens_per_s": 1 / t1,
+            "us_per_call_graph": t1g * 1e6, "effective_GBs_graph": b1 / t1g / 1e9,
             "call_us": call_percentiles(call1, 200, 10),
             "effective_GBs": b1 / t1 / 1e9, "hbm_frac": b1 / t1 / 1e9 / HBM_PEAK_GBS,
             "alg_bytes_per_call": b1, "parity_err": err1,
         }
-        log(f"decode T=1: {t1 * 1e6:.2f} us/call, {b1 / t1 / 1e9:.1f} GB/s")
+        log(f"decode T=1: {t1 * 1e6:.2f} us/call, {b1 / t1 / 1e9:.1f} GB/s; graph replay "
+            f"{t1g * 1e6:.2f} us/call, {b1 / t1g / 1e9:.1f} GB/s")
 
     # ------------------------- grouped decode: 256 layers, 1 token each --
     if want("grouped"):

@@ -6,6 +6,8 @@
 namespace dbf {
 
 typedef half_t v4h __attribute__((ext_vector_type(4)));
+typedef half_t v2h __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 // (a & m) | c in one VALU op (ALU only; no memory access).  gfx950 VOP3
 // encodings take no literal constants, so m and c come from registers (m a

@@ -234,17 +234,24 @@ __device__ inline float row_next(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x100 + n, 0xF, 0xF, true));
 }
 
-template <int STAGE, bool SCALE_LDS = false>
+// SCALE: where the row scales come from: 0, srow in device memory; 1, srow
+// staged in LDS; 2, the caller's sc_given (the lane's four rows, loaded
+// early).
+template <int STAGE, int SCALE = 0>
 __device__ inline void gemv_epilogue(const GemvParams& p, float* zb, void* yb, const half_t* srow,
                                      v4f sum, int64_t tile, int lane, int g, int part, bool colv,
-                                     int ci, int ct, int ntok, int64_t t0) {
+                                     int ci, int ct, int ntok, int64_t t0,
+                                     const half_t* sc_given = nullptr) {
   const int64_t r0 = tile * kRowTile + 4 * g;
   // the parts of a column are lanes j, j+1, j+2 of one row of 16 (j <= 13)
   float tot[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) tot[v] = (sum[v] + row_next<1>(sum[v])) + row_next<2>(sum[v]);
   float sc[4];
-  if (SCALE_LDS) {
+  if (SCALE == 2) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sc[v] = (float)sc_given[v];
+  } else if (SCALE == 1) {
     // staged rows are zero past p.rows: one 8-byte LDS read, no guards
     typedef const __attribute__((address_space(3))) v4h* lds_v4hp;
     const v4h s4 = *(lds_v4hp)(srow + r0);
@@ -323,6 +330,7 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
                                                                      int stride) {
   static_assert(!PIN || !MULTI, "operand parts are built in place for one adapter");
   static_assert(!GROUP || PIN, "grouped layers take the parts-building stages");
+  static_assert(!PIN || RTG <= NW, "each wave finishes at most one row tile");
   typedef GemvLds<RTG, KC, PIN, NW> Lds;
   auto red = reinterpret_cast<v4f (*)[RTG][64]>(lds);
   auto pin_b = reinterpret_cast<uint8_t (*)[Lds::pinb_bytes / NW]>(lds + Lds::red_bytes);
@@ -388,7 +396,24 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
     const bool colv = j < ncols;
     const int ci = colv ? c / ntok : 0, ct = colv ? c - ntok * (c / ntok) : 0;
     const uint32_t* __restrict__ S = STAGE == 1 ? f.B2 : f.B1;
-
+    // PIN: wave w < RTG finishes row tile tile0 + w; its row scales are
+    // requested now, so the epilogue does not wait for them.  Four 16-bit
+    // loads from clamped rows into separate registers, rows past the end
+    // zeroed at the use: a select or a packing next to the loads would wait
+    // for them here.
+    uint32_t scu[4] = {0u, 0u, 0u, 0u};
+    int64_t sc_r0 = 0;
+    if constexpr (PIN) {
+      const int64_t ptile = tile0 + wv < p.nrt ? tile0 + wv : p.nrt - 1;
+      const DBF_GLOBAL char* srow = (const DBF_GLOBAL char*)(STAGE == 1 ? f.beta : f.alpha);
+      sc_r0 = ptile * kRowTile + 4 * g;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        // term ci's row r; rows * ell < 2^31 entries
+        const int r = (int)(sc_r0 + v < p.rows ? sc_r0 + v : p.rows - 1) + ci * (int)p.rows;
+        scu[v] = *(const DBF_GLOBAL uint16_t*)(srow + 2u * (uint32_t)r);
+      }
+    }
     const int64_t nrt_here = (p.nrt - tile0) < RTG ? (p.nrt - tile0) : RTG;
     const int nq_here = (int)((nrt_here + kQuad - 1) / kQuad);
     bool first_chunk = true;
@@ -417,29 +442,72 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
         // lane l holds entries 2l, 2l+1 of the block; they meet adjacent
         // operand bytes
         const int boff = fp8_operand_byte(operand_k_of_col(2 * lane));
-        for (int kk = 0; kk < nk; ++kk) {
-          const int64_t k = (kw0 + kk) * kColBlock + 2 * lane;
-          for (int ci2 = 0; ci2 < p.ell; ++ci2)
-            for (int ct2 = 0; ct2 < ntok; ++ct2) {
-              const int64_t t = t0 + ct2;
-              float v0 = 0.0f, v1 = 0.0f;
+        // every entry of the wave's blocks is requested before the first
+        // part is built (column cc = term * ntok + token, ell * ntok <=
+        // kPinColTokens)
+        // Entries k, k+1 (k even) of a row come as one 4-byte word (x, gamma)
+        // or 8-byte pair (z), every load from an address inside the row
+        // (clamped) and the entries past K zeroed after: no branch between
+        // the requests, so all of them are in flight together.  Stage 1
+        // runs here only with K even and gamma 4-byte aligned (the host
+        // checks), so its pairs are aligned words.
+        constexpr int NCC = kPinColTokens;
+        const int ncc = p.ell * ntok;
+        v2f ev[KC][NCC];
+        {
+          // row starts are wave-uniform; the lane's part is a 32-bit byte
+          // offset (a parts-building stage has K <= 32 * 128)
+          const int kc = STAGE == 1 ? (int)p.K - 2 : (int)p.ldz - 2;
+          typedef const DBF_GLOBAL char* gcp;
+          uint32_t ea[KC][NCC], eb[KC][NCC];
+          v2f ez[KC][NCC];
+#pragma unroll
+          for (int kk = 0; kk < KC; ++kk) {
+            const int k = (int)(kw0 + kk) * kColBlock + 2 * lane;
+            const uint32_t off = (uint32_t)(k < kc ? k : kc) * (STAGE == 1 ? 2u : 4u);
+#pragma unroll
+            for (int cc = 0; cc < NCC; ++cc) {
+              const int q = cc / ntok, ci2 = q < p.ell ? q : p.ell - 1;
+              const int64_t t = t0 + (cc - q * ntok);
               if (STAGE == 1) {
-                const half_t* gi = f.gamma + ci2 * p.K;
-                const half_t* xr = p.x + t * p.ldx;
-                if (k < p.K) v0 = (float)gi[k] * (float)xr[k];
-                if (k + 1 < p.K) v1 = (float)gi[k + 1] * (float)xr[k + 1];
+                ea[kk][cc] = *(const DBF_GLOBAL uint32_t*)((gcp)(f.gamma + ci2 * p.K) + off);
+                eb[kk][cc] = *(const DBF_GLOBAL uint32_t*)((gcp)(p.x + t * p.ldx) + off);
               } else {
-                const float* zr = zl + ci2 * p.zstride + t * p.ldz;
-                if (k < p.K) v0 = zr[k];
-                if (k + 1 < p.K) v1 = zr[k + 1];
+                ez[kk][cc] = *(const DBF_GLOBAL v2f*)((gcp)(zl + ci2 * p.zstride + t * p.ldz) + off);
               }
-              const int col0 = kParts * (ci2 * ntok + ct2);
-              block_parts(v0, v1, [&](int pp, uint16_t code, int sc) {
-                *(uint16_t*)(pb + (kk * kPinCols + col0 + pp) * 128 + boff) = code;
-                if (lane == 0) ps[kk * kPinCols + col0 + pp] = (uint8_t)(sc + 127);
-              });
+            }
+          }
+#pragma unroll
+          for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+            for (int cc = 0; cc < NCC; ++cc) {
+              const int64_t k = (kw0 + kk) * kColBlock + 2 * lane;
+              const bool on = kk < nk && cc < ncc;
+              float v0, v1;
+              if (STAGE == 1) {
+                const v2h ga = __builtin_bit_cast(v2h, ea[kk][cc]);
+                const v2h xb = __builtin_bit_cast(v2h, eb[kk][cc]);
+                v0 = (float)ga[0] * (float)xb[0];
+                v1 = (float)ga[1] * (float)xb[1];
+              } else {
+                v0 = ez[kk][cc][0];
+                v1 = ez[kk][cc][1];
+              }
+              ev[kk][cc] = v2f{on && k < p.K ? v0 : 0.0f, on && k + 1 < p.K ? v1 : 0.0f};
             }
         }
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+          for (int cc = 0; cc < NCC; ++cc) {
+            if (kk >= nk || cc >= ncc) continue;
+            const float v0 = ev[kk][cc][0], v1 = ev[kk][cc][1];
+            const int col0 = kParts * cc;
+            block_parts(v0, v1, [&](int pp, uint16_t code, int sc) {
+              *(uint16_t*)(pb + (kk * kPinCols + col0 + pp) * 128 + boff) = code;
+              if (lane == 0) ps[kk * kPinCols + col0 + pp] = (uint8_t)(sc + 127);
+            });
+          }
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) {
           const bool live = colv && kk < nk;
@@ -496,7 +564,12 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
 #pragma unroll
       for (int w = 1; w < NW; ++w) sum += red[w][rt][lane];
       const half_t* srow = (STAGE == 1 ? f.beta : f.alpha) + (int64_t)ci * p.rows;
-      gemv_epilogue<STAGE>(p, zl, yl, srow, sum, tile, lane, g, part, colv, ci, ct, ntok, t0);
+      half_t scg[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        scg[v] = sc_r0 + v < p.rows ? __builtin_bit_cast(half_t, (uint16_t)scu[v]) : (half_t)0.0f;
+      gemv_epilogue<STAGE, PIN ? 2 : 0>(p, zl, yl, srow, sum, tile, lane, g, part, colv, ci, ct,
+                                        ntok, t0, scg);
     }
     __syncthreads();
   }
@@ -1358,7 +1431,12 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
     if (a.multi || (int64_t)a.ell * ntok > kPinColTokens) return 0;
     return nkb <= 16 ? 1 : nkb <= 32 ? 2 : 0;
   };
-  const int kc1 = pin_kc(g1.nkb), kc2 = pin_kc(g2.nkb);
+  // stage 1 reads gamma and x as aligned pairs of entries: M even and every
+  // gamma 4-byte aligned (x rows are 16-byte aligned by the boundary's rules)
+  bool pairs1 = a.M % 2 == 0;
+  for (int j = 0; j < (a.group > 1 ? a.group : 1); ++j)
+    pairs1 = pairs1 && (((uintptr_t)(a.group > 1 ? a.grp[j].gamma : a.single.gamma)) & 3u) == 0;
+  const int kc1 = pairs1 ? pin_kc(g1.nkb) : 0, kc2 = pin_kc(g2.nkb);
   if (a.group > 1) {
     // one launch per stage for every layer when both stages build their own
     // parts; otherwise the caller runs the layers one by one (nothing has
