@@ -1114,32 +1114,41 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
     // their parts need not wait for the signs.
     const int ntask1 = ell * ntok * nkb1;
     const int M = (int)p1.K;
-    auto load_v = [&](int task0, float (&v0)[4], float (&v1)[4]) {
+    // Each entry is a 16-bit load from an address clamped into its row, kept
+    // zero-extended in a register of its own until parts_v: no branch,
+    // packing or arithmetic next to the requests, so the sign ring below is
+    // requested while they are in flight.
+    typedef const DBF_GLOBAL uint16_t* gu16p;
+    auto load_v = [&](int task0, uint32_t (&e)[4][4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int task = task0 + q * NW, tq = task < ntask1 ? task : ntask1 - 1;
+        const int kb = tq % nkb1, cc = tq / nkb1;  // cc = term * ntok + token
+        const int i = cc / ntok, tt = cc - i * ntok;
+        const int k = kb * kColBlock + 2 * lane;
+        const int k0 = k < M ? k : M - 1, k1 = k + 1 < M ? k + 1 : M - 1;
+        const half_t* xr = fx.x + (t0 + tt) * fx.ldx;
+        const half_t* gi = gamma + (int64_t)i * M;
+        e[q][0] = *(gu16p)(gi + k0);
+        e[q][1] = *(gu16p)(gi + k1);
+        e[q][2] = *(gu16p)(xr + k0);
+        e[q][3] = *(gu16p)(xr + k1);
+      }
+    };
+    auto parts_v = [&](int task0, const uint32_t (&e)[4][4]) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int task = task0 + q * NW;
-        v0[q] = v1[q] = 0.0f;
         if (task < ntask1) {
-          const int kb = task % nkb1, cc = task / nkb1;  // cc = term * ntok + token
-          const int i = cc / ntok, tt = cc - i * ntok;
-          const int k = kb * kColBlock + 2 * lane;
-          const half_t* xr = fx.x + (t0 + tt) * fx.ldx;
-          const half_t* gi = gamma + (int64_t)i * M;
-          if (k < M) v0[q] = (float)gi[k] * (float)xr[k];
-          if (k + 1 < M) v1[q] = (float)gi[k + 1] * (float)xr[k + 1];
+          const int k = (task % nkb1) * kColBlock + 2 * lane;
+          auto h = [&](int w) { return (float)__builtin_bit_cast(half_t, (uint16_t)e[q][w]); };
+          const float v0 = k < M ? h(0) * h(2) : 0.0f, v1 = k + 1 < M ? h(1) * h(3) : 0.0f;
+          parts_to_lds(v0, v1, bl, bs, task % nkb1, (task / nkb1) * kParts, ncols, lane);
         }
       }
     };
-    auto parts_v = [&](int task0, const float (&v0)[4], const float (&v1)[4]) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int task = task0 + q * NW;
-        if (task < ntask1)
-          parts_to_lds(v0[q], v1[q], bl, bs, task % nkb1, (task / nkb1) * kParts, ncols, lane);
-      }
-    };
-    float v0[4], v1[4];
-    load_v(wv, v0, v1);
+    uint32_t ev[4][4];
+    load_v(wv, ev);
     v4u ring[D];
     if (has1) {
 #pragma unroll
@@ -1149,10 +1158,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_fused(GemvParams p1, GemvParam
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // the previous column block's LDS readers are done
     if (threadIdx.x == 0) qcnt[0] = qcnt[1] = NW;
-    parts_v(wv, v0, v1);
+    parts_v(wv, ev);
     for (int task0 = wv + 4 * NW; task0 < ntask1; task0 += 4 * NW) {
-      load_v(task0, v0, v1);
-      parts_v(task0, v0, v1);
+      load_v(task0, ev);
+      parts_v(task0, ev);
     }
     pad_blocks(bl, bs, nkb1, nkp1, ncols);
     // output scales of both stages, kSc per thread requested together (a
