@@ -147,17 +147,25 @@ __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
     live = ad >= 0 && ad < p.num_adapters;
     if (live && !p.from_z) gam = p.gammas[ad];
   }
+  // entries from addresses clamped into the row, each in a register of its
+  // own, range-checked at the use: the requests go out together
   float v0 = 0.0f, v1 = 0.0f;
   if (live) {
+    const int64_t k0 = k < p.K ? k : p.K - 1, k1 = k + 1 < p.K ? k + 1 : p.K - 1;
     if (p.from_z) {
       const float* zr = p.z + i * p.zstride + t * p.ldz;
-      if (k < p.K) v0 = zr[k];
-      if (k + 1 < p.K) v1 = zr[k + 1];
+      const float z0 = zr[k0], z1 = zr[k1];
+      v0 = k < p.K ? z0 : 0.0f;
+      v1 = k + 1 < p.K ? z1 : 0.0f;
     } else {
+      typedef const DBF_GLOBAL uint16_t* gu16p;
       const half_t* gi = gam + i * p.K;
       const half_t* xr = p.x + t * p.ldx;
-      if (k < p.K) v0 = (float)gi[k] * (float)xr[k];
-      if (k + 1 < p.K) v1 = (float)gi[k + 1] * (float)xr[k + 1];
+      const uint32_t g0 = *(gu16p)(gi + k0), g1 = *(gu16p)(gi + k1);
+      const uint32_t x0 = *(gu16p)(xr + k0), x1 = *(gu16p)(xr + k1);
+      auto h = [](uint32_t u) { return (float)__builtin_bit_cast(half_t, (uint16_t)u); };
+      v0 = k < p.K ? h(g0) * h(x0) : 0.0f;
+      v1 = k + 1 < p.K ? h(g1) * h(x1) : 0.0f;
     }
   }
   uint8_t* out = (uint8_t*)p.opnd + blk * (kParts * 4 * 32);
