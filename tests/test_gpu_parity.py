@@ -4,6 +4,8 @@ Bars: bit-exact on integer-valued inputs with unit scales (fp32 output equals
 float32 of the exact value; fp16 output equals its nearest-even rounding);
 max|y - y_ref| / max|y_ref| <= 2e-3 on fp16 inputs.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -268,21 +270,36 @@ def test_stage1_x_in_place_and_operand_tiles(shape):
         assert err <= TOL, err
 
 
+def odd_scales(pl):
+    """The layer with alpha, beta and gamma moved to views that start one
+    half past a 16-byte boundary (2-byte aligned only)."""
+    def shift(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        buf[1:] = t.reshape(-1)
+        return buf[1:].view(t.shape)
+    return dataclasses.replace(pl, alpha=shift(pl.alpha), beta=shift(pl.beta), gamma=shift(pl.gamma))
+
+
 @pytest.mark.parametrize("shape", [(300, 130, 260, 1, 1), (4096, 2048, 4096, 1, 1),
-                                   (96, 200, 8000, 1, 2), (72, 40, 136, 2, 1), (1, 1, 1, 1, 1)])
+                                   (96, 200, 8000, 1, 2), (72, 40, 136, 2, 1), (1, 1, 1, 1, 1),
+                                   (64, 37, 96, 1, 1), (64, 38, 97, 1, 1), (80, 37, 98, 2, 1)])
 def test_decode_stages_build_parts(shape):
     """With one adapter and ell * tokens <= 2 the small-T stages build their
     fp8 operand parts themselves, from gamma*x and from z, with no prep
     launch (reductions of 1..32 blocks: 1 or 2 blocks per wave; the
-    63-block stage 1 of M = 8000 takes a prep launch).  Exact
-    on integer inputs with unit scales, within the bar on fp16, and equal to
-    the result of the adapter-table call, whose prep launches build the same
-    parts, on integers."""
+    63-block stage 1 of M = 8000 takes a prep launch, and so does stage 1
+    when M is odd or gamma is not 4-byte aligned).  Odd R puts the last
+    entry pair of stage 2 on the z row's padding.  Exact on integer inputs
+    with unit scales, also with 2-byte aligned scale vectors, within the bar
+    on fp16, and equal to the result of the adapter-table call, whose prep
+    launches build the same parts, on integers."""
     N, R, M, ell, T = shape
     Li = synth.make_layer(N, R, M, ell, T, seed=101, alpha="ones", beta="ones", gamma="ones",
                           x_kind="int3")
     want = ref(Li).astype(np.float32).astype(np.float64)
     got = H().run_layer(Li, path="gemv", y_dtype=torch.float32)
+    assert np.array_equal(got, want)
+    got = H().run_layer(Li, path="gemv", y_dtype=torch.float32, pl=odd_scales(H().upload(Li)))
     assert np.array_equal(got, want)
     D = H().DeviceAdapters([Li])
     ids = H().to_dev(np.zeros(T, np.int32))
@@ -291,6 +308,8 @@ def test_decode_stages_build_parts(shape):
     assert np.array_equal(y.cpu().numpy().astype(np.float64), want)
     L = synth.make_layer(N, R, M, ell, T, seed=102)
     err = oracle.max_norm_error(H().run_layer(L, path="gemv"), ref(L))
+    assert err <= TOL, err
+    err = oracle.max_norm_error(H().run_layer(L, path="gemv", pl=odd_scales(H().upload(L))), ref(L))
     assert err <= TOL, err
 
 
