@@ -460,17 +460,24 @@ def main():
 
             nc = max(args.steps, 100)
             tc = time_calls(callc, nc, args.warmup) / nc
+            # the same calls replayed from a HIP graph: the GPU's time per
+            # call, free of the host's launch rate
+            tg = time_graph(callc, 64, max(args.steps // 16, 4), 2)
             bc, fc = alg_bytes(Nc, Rc, Mc, 1, Tc), alg_flops(Nc, Rc, Mc, 1, Tc)
             name = f"{synth.CONFIGS[cfg].name}_T{Tc}"
             cfgs[name] = {
                 "N": Nc, "R": Rc, "M": Mc, "T": Tc, "us_per_call": tc * 1e6,
                 "tokens_per_s": Tc / tc, "effective_GBs": bc / tc / 1e9,
                 "hbm_frac": bc / tc / 1e9 / HBM_PEAK_GBS,
-                "mfma_frac": fc / tc / 1e12 / MFMA_F16_PEAK_TFLOPS, "cold_instances": k_inst,
+                "mfma_frac": fc / tc / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                "us_per_call_graph": tg * 1e6, "effective_GBs_graph": bc / tg / 1e9,
+                "hbm_frac_graph": bc / tg / 1e9 / HBM_PEAK_GBS,
+                "mfma_frac_graph": fc / tg / 1e12 / MFMA_F16_PEAK_TFLOPS, "cold_instances": k_inst,
                 "parity_err": errc, "parity_check": chk,
             }
             log(f"{name}: {tc * 1e6:.2f} us/call, {bc / tc / 1e9:.1f} GB/s, "
-                f"{fc / tc / 1e12:.1f} TFLOP/s, err {errc:.2e}")
+                f"{fc / tc / 1e12:.1f} TFLOP/s; graph replay {tg * 1e6:.2f} us/call, "
+                f"{bc / tg / 1e9:.1f} GB/s, {fc / tg / 1e12:.1f} TFLOP/s; err {errc:.2e}")
             del cB1, cB2
         out["configs"] = cfgs
 

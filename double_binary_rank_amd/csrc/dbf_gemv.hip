@@ -1311,6 +1311,18 @@ static hipError_t launch_gemv_stage_any(GemvParams p, int64_t n_cb_est, int64_t 
                        p);
     return hipGetLastError();
   }
+  if (!multi && p.nkb > 4 * 8) {
+    // few column blocks and a reduction longer than one round of 4 waves x
+    // 8 blocks: 16 waves split it, 4 blocks each per round, so an item
+    // makes half as many dependent rounds (one quad of row tiles per item)
+    p.n_rg = cdiv(p.nrt, kQuad);
+    const int64_t grid = n_cb_max * p.n_rg;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
+    p.grid = grid;
+    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 4, false, false, 16>), dim3((unsigned)grid), dim3(1024),
+                       0, s, p);
+    return hipGetLastError();
+  }
   const int kc = p.nkb > 16 ? 8 : 4;
   const int rtg_max = 64 / kc;
   int rtg = 4;
