@@ -6,8 +6,8 @@
 // matrices is SVID: sign times the rank-1 approximation of the magnitude.
 //
 // Everything is fp32 on the device, one stream:
-//   * products of dense matrices: k_sgemm (register-tiled FMA, 64 x 64 tiles
-//     through LDS; NN, NT and TN operand orders);
+//   * products of dense matrices: k_sgemm (fp32 matrix-core tiles of
+//     128 x 128 through LDS; NN, NT and TN operand orders);
 //   * the k x k solve (Gram + rho I)^-1 by Newton-Schulz iteration,
 //     X <- X (2I - A X) from X0 = I / ||A||_inf, a fixed count of
 //     2 ceil(log2(k + 1)) + 10 steps (the initial error is below 1 - 1/cond and
@@ -29,82 +29,100 @@ namespace {
 
 // ------------------------------------------------------------- SGEMM ----
 // C[m][n] = sum_k A(m,k) B(k,n); A(m,k) = A[m*lda + k] (TA: A[k*lda + m]),
-// B(k,n) = B[k*ldb + n] (TB: B[n*ldb + k]).  256 threads, 64 x 64 tile of C,
-// 16-deep slices of the reduction staged in LDS, 4 x 4 outputs per thread.
-constexpr int kGT = 64, kGK = 16;
+// B(k,n) = B[k*ldb + n] (TB: B[n*ldb + k]).  fp32 in, fp32 accumulate, on
+// the matrix core (v_mfma_f32_16x16x4_f32: twice the unpacked vector FMA
+// rate).  A workgroup of 4 waves owns a 128 x 128 tile of C, each wave a
+// 64 x 64 quarter as 4 x 4 MFMA tiles.  16-deep slices of A and B go
+// through LDS, rows padded by 16 floats so that the 4 rows x 16 columns a
+// wave reads per operand hit 64 distinct banks; the next slice is read from
+// memory into registers while the current one is multiplied.
+// MFMA lane layout (16 x 16 x 4): lane l holds A(l % 16, l / 16) and
+// B(l / 16, l % 16); output register r of lane l is C(4 (l / 16) + r, l % 16).
+constexpr int kMT = 128, kMK = 16, kMP = kMT + 16;
 
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void k_sgemm(const float* __restrict__ A, int64_t lda,
                                                const float* __restrict__ B, int64_t ldb,
                                                float* __restrict__ C, int64_t ldc, int32_t Mr,
                                                int32_t Nc, int32_t K) {
-  __shared__ float As[kGK][kGT + 4];
-  __shared__ float Bs[kGK][kGT + 4];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int n_tn = (Nc + kGT - 1) / kGT;
-  const int m0 = (int)(blockIdx.x / n_tn) * kGT, n0 = (int)(blockIdx.x % n_tn) * kGT;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += kGK) {
-    // each thread stages 4 entries of each tile
+  __shared__ float As[kMK][kMP];  // As[k][m]
+  __shared__ float Bs[kMK][kMP];  // Bs[k][n]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n_tn = (Nc + kMT - 1) / kMT;
+  const int m0 = (int)(blockIdx.x / n_tn) * kMT, n0 = (int)(blockIdx.x % n_tn) * kMT;
+  const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
+  // entry e of this thread in a slice (2048 entries per operand, 8 each):
+  // consecutive threads take consecutive addresses of the source
+  auto a_pos = [&](int e, int& m, int& k) {
+    const int id = tid + 256 * e;
+    if (TA) { k = id >> 7; m = id & 127; } else { m = id >> 4; k = id & 15; }
+  };
+  auto b_pos = [&](int e, int& k, int& n) {
+    const int id = tid + 256 * e;
+    if (TB) { n = id >> 4; k = id & 15; } else { k = id >> 7; n = id & 127; }
+  };
+  float ra[8], rb[8];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int id = tid + 256 * e;  // 0..1023
-      // A tile: (m, k) with m in [0, 64), k in [0, 16)
-      int mm, kk;
-      if (TA) {
-        kk = id >> 6;
-        mm = id & 63;
-      } else {
-        mm = id >> 4;
-        kk = id & 15;
-      }
-      const int gm = m0 + mm, gk = k0 + kk;
-      As[kk][mm] = (gm < Mr && gk < K) ? (TA ? A[(int64_t)gk * lda + gm] : A[(int64_t)gm * lda + gk])
-                                       : 0.0f;
-      // B tile: (k, n)
-      int kb, nn;
-      if (TB) {
-        nn = id >> 4;
-        kb = id & 15;
-      } else {
-        kb = id >> 6;
-        nn = id & 63;
-      }
-      const int gn = n0 + nn, gkb = k0 + kb;
-      Bs[kb][nn] = (gn < Nc && gkb < K) ? (TB ? B[(int64_t)gn * ldb + gkb] : B[(int64_t)gkb * ldb + gn])
-                                        : 0.0f;
+    for (int e = 0; e < 8; ++e) {
+      int m, k, kb, n;
+      a_pos(e, m, k);
+      b_pos(e, kb, n);
+      const int gm = m0 + m, gk = k0 + k, gn = n0 + n, gkb = k0 + kb;
+      ra[e] = (gm < Mr && gk < K) ? (TA ? A[(int64_t)gk * lda + gm] : A[(int64_t)gm * lda + gk]) : 0.0f;
+      rb[e] = (gn < Nc && gkb < K) ? (TB ? B[(int64_t)gn * ldb + gkb] : B[(int64_t)gkb * ldb + gn]) : 0.0f;
+    }
+  };
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += kMK) {
+    __syncthreads();  // the previous slice's readers are done
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int m, k, kb, n;
+      a_pos(e, m, k);
+      b_pos(e, kb, n);
+      As[k][m] = ra[e];
+      Bs[kb][n] = rb[e];
     }
     __syncthreads();
+    if (k0 + kMK < K) fetch(k0 + kMK);
 #pragma unroll
-    for (int kk = 0; kk < kGK; ++kk) {
+    for (int k4 = 0; k4 < kMK / 4; ++k4) {
+      const int kk = 4 * k4 + (lane >> 4), c = lane & 15;
       float a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][wm + 16 * i + c];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][wn + 16 * j + c];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gm = m0 + ty * 4 + i;
-    if (gm >= Mr) continue;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + tx * 4 + j;
-      if (gn < Nc) C[(int64_t)gm * ldc + gn] = acc[i][j];
+      const int gn = n0 + wn + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gm = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
+        if (gm < Mr && gn < Nc) C[(int64_t)gm * ldc + gn] = acc[i][j][r];
+      }
     }
-  }
 }
 
 template <bool TA, bool TB>
 hipError_t sgemm(const float* A, int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
                  int64_t Mr, int64_t Nc, int64_t K, hipStream_t s) {
-  const int64_t grid = cdiv(Mr, kGT) * cdiv(Nc, kGT);
+  const int64_t grid = cdiv(Mr, kMT) * cdiv(Nc, kMT);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_sgemm<TA, TB>), dim3((unsigned)grid), dim3(256), 0, s, A, lda, B, ldb, C,
                      ldc, (int32_t)Mr, (int32_t)Nc, (int32_t)K);
