@@ -148,17 +148,29 @@ __device__ inline float block_sum(float x) {
   return r;
 }
 
-// Absolute column sums of the k x k matrix G + rho I (rho from the trace,
-// read again by every thread: k is small), one column per thread.
-__global__ __launch_bounds__(256) void k_colabs(const float* G, int32_t k, float rho0, float* cs) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= k) return;
+// Absolute column sums of the k x k matrix G + rho I.  A workgroup of 16
+// waves owns 64 columns (lane = column); wave w sums rows w, w + 16, ...,
+// and the 16 partial sums are added in wave order.  rho comes from the
+// trace summed exactly as k_regularise sums it.
+__global__ __launch_bounds__(1024) void k_colabs(const float* G, int32_t k, float rho0, float* cs) {
   float tr = 0.0f;
-  for (int i = 0; i < k; ++i) tr += G[(int64_t)i * k + i];
-  const float rho = rho0 * tr / (float)k;
+  for (int i = threadIdx.x; i < k; i += 1024) tr += G[(int64_t)i * k + i];
+  const float rho = rho0 * block_sum(tr) / (float)k;
+  __shared__ float part[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane;
   float a = 0.0f;
-  for (int i = 0; i < k; ++i) a += fabsf(G[(int64_t)i * k + j] + (i == j ? rho : 0.0f));
-  cs[j] = a;
+  if (j < k) {
+#pragma unroll 8
+    for (int i = w; i < k; i += 16) a += fabsf(G[(int64_t)i * k + j] + (i == j ? rho : 0.0f));
+  }
+  part[w][lane] = a;
+  __syncthreads();
+  if (w == 0 && j < k) {
+    float t = 0.0f;
+    for (int v = 0; v < 16; ++v) t += part[v][lane];
+    cs[j] = t;
+  }
 }
 
 // rho = rho0 * trace(G) / k;  A = G + rho I (in place);  Newton-Schulz start
@@ -263,6 +275,7 @@ __global__ __launch_bounds__(1024) void k_norm_cols(const float* part, int32_t n
   float ss = 0.0f;
   for (int j = threadIdx.x; j < cols; j += 1024) {
     float a = 0.0f;
+#pragma unroll 8
     for (int c = 0; c < n_chunks; ++c) a += part[(int64_t)c * cols + j];
     v[j] = a;
     ss += a * a;
@@ -427,7 +440,7 @@ hipError_t launch_factorize(const FactorArgs& a, hipStream_t s) {
   };
   // (G + rho I)^-1 into inv (G is k x k, already formed; regularised in place)
   auto ns_inverse = [&]() -> hipError_t {
-    DBF_LAUNCH(k_colabs, blocks(k), 256, (const float*)G, (int32_t)k, a.rho0, part);
+    DBF_LAUNCH(k_colabs, cdiv(k, 64), 1024, (const float*)G, (int32_t)k, a.rho0, part);
     DBF_LAUNCH(k_regularise, 1, 1024, G, (int32_t)k, a.rho0, (const float*)part, sc);
     DBF_LAUNCH(k_ns_init, blocks(k * k), 256, inv, (int32_t)k, (const float*)sc);
     float* x = inv;
