@@ -32,13 +32,14 @@ namespace {
 // B(k,n) = B[k*ldb + n] (TB: B[n*ldb + k]).  fp32 in, fp32 accumulate, on
 // the matrix core (v_mfma_f32_16x16x4_f32: twice the unpacked vector FMA
 // rate).  A workgroup of 4 waves owns a 128 x 128 tile of C, each wave a
-// 64 x 64 quarter as 4 x 4 MFMA tiles.  16-deep slices of A and B go
+// 64 x 64 quarter as 4 x 4 MFMA tiles.  kMK-deep slices of A and B go
 // through LDS, rows padded by 16 floats so that the 4 rows x 16 columns a
 // wave reads per operand hit 64 distinct banks; the next slice is read from
 // memory into registers while the current one is multiplied.
 // MFMA lane layout (16 x 16 x 4): lane l holds A(l % 16, l / 16) and
 // B(l / 16, l % 16); output register r of lane l is C(4 (l / 16) + r, l % 16).
 constexpr int kMT = 128, kMK = 16, kMP = kMT + 16;
+constexpr int kME = kMT * kMK / 256;  // entries of each operand per thread and slice
 
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void k_sgemm(const float* __restrict__ A, int64_t lda,
@@ -51,20 +52,20 @@ __global__ __launch_bounds__(256) void k_sgemm(const float* __restrict__ A, int6
   const int n_tn = (Nc + kMT - 1) / kMT;
   const int m0 = (int)(blockIdx.x / n_tn) * kMT, n0 = (int)(blockIdx.x % n_tn) * kMT;
   const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
-  // entry e of this thread in a slice (2048 entries per operand, 8 each):
-  // consecutive threads take consecutive addresses of the source
+  // entry e of this thread in a slice: consecutive threads take
+  // consecutive addresses of the source
   auto a_pos = [&](int e, int& m, int& k) {
     const int id = tid + 256 * e;
-    if (TA) { k = id >> 7; m = id & 127; } else { m = id >> 4; k = id & 15; }
+    if (TA) { k = id / kMT; m = id % kMT; } else { m = id / kMK; k = id % kMK; }
   };
   auto b_pos = [&](int e, int& k, int& n) {
     const int id = tid + 256 * e;
-    if (TB) { n = id >> 4; k = id & 15; } else { k = id >> 7; n = id & 127; }
+    if (TB) { n = id / kMK; k = id % kMK; } else { k = id / kMT; n = id % kMT; }
   };
-  float ra[8], rb[8];
+  float ra[kME], rb[kME];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < kME; ++e) {
       int m, k, kb, n;
       a_pos(e, m, k);
       b_pos(e, kb, n);
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void k_sgemm(const float* __restrict__ A, int6
   for (int k0 = 0; k0 < K; k0 += kMK) {
     __syncthreads();  // the previous slice's readers are done
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < kME; ++e) {
       int m, k, kb, n;
       a_pos(e, m, k);
       b_pos(e, kb, n);
