@@ -226,6 +226,26 @@ __global__ __launch_bounds__(256) void k_dense_tn(DenseParams p) {
   const int g = lane >> 4, c16 = lane & 15;
   const int ga = blockIdx.x % p.n_ga, gb = blockIdx.x / p.n_ga;
   const int ta0 = (ga * 2 + (wv & 1)) * 4, tb0 = (gb * 2 + (wv >> 1)) * 4;
+  float* __restrict__ out = p.out;
+  float* __restrict__ dH = p.dH;
+  const float* __restrict__ Hm = p.H;
+  const int64_t ldo = p.rows_b;
+  // interior waves (all 16 tiles inside both matrices) request every H entry
+  // they will scale before the products, so that its latency overlaps them,
+  // and store through one row pointer per register, the 4 column tiles at
+  // 64-byte immediate offsets
+  const bool interior = (ta0 + 4) * 16 <= p.rows_a && (tb0 + 4) * 16 <= p.rows_b;
+  float hv[4][4][4];  // [h][v][c]
+  if (STE && interior) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t o = (int64_t)((ta0 + h) * 16 + 4 * g + v) * ldo + tb0 * 16 + c16;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) hv[h][v][c] = Hm[o + 16 * c];
+      }
+  }
   v4f acc[4][4];
 #pragma unroll
   for (int h = 0; h < 4; ++h)
@@ -252,28 +272,17 @@ __global__ __launch_bounds__(256) void k_dense_tn(DenseParams p) {
   }
   // lane (g, c16), register v of tile (h, c): row 4g + v of A-tile h, row c16
   // of B-tile c
-  float* __restrict__ out = p.out;
-  float* __restrict__ dH = p.dH;
-  const float* __restrict__ Hm = p.H;
-  const int64_t ldo = p.rows_b;
-  // interior waves (all 16 tiles inside both matrices) store through one row
-  // pointer per register, the 4 column tiles at 64-byte immediate offsets
-  const bool interior = (ta0 + 4) * 16 <= p.rows_a && (tb0 + 4) * 16 <= p.rows_b;
   if (interior) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t o = (int64_t)((ta0 + h) * 16 + 4 * g + v) * ldo + tb0 * 16 + c16;
-        float hv[4];
-        if (STE)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) hv[c] = Hm[o + 16 * c];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const float val = acc[h][c][v];
           if (OUT) out[o + 16 * c] = val;
-          if (STE) dH[o + 16 * c] = val * (sech2(hv[c] * p.inv_tau) * p.inv_tau);
+          if (STE) dH[o + 16 * c] = val * (sech2(hv[h][v][c] * p.inv_tau) * p.inv_tau);
         }
       }
     }
