@@ -76,6 +76,8 @@ struct GemmParams {
   Factors grp[kMaxGroup];
   const ColBlock* cbl;
   const WsHeader* hdr;
+  int32_t cb_cap;        // column-block entries the workspace holds
+  int32_t num_adapters;  // several adapters: entries of the pointer tables
   const uint32_t* const* B1s;
   const uint32_t* const* B2s;
   const half_t* const* alphas;
@@ -285,6 +287,46 @@ __global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
   }
 }
 
+// Several adapters: the first column block of a workgroup and, for up to
+// kLdsAdapters adapters, the factor pointer tables (B1, B2, alpha, beta) are
+// requested together with the column-block count at the start; the tables
+// go to LDS, so the first item waits for one memory round trip instead of
+// three (count, then block, then pointers).  Workgroup-wide.
+constexpr int kLdsAdapters = 256;
+template <int CAP>
+struct FactorTab {
+  const void* ptr[CAP][4];
+};
+__device__ inline ColBlock prefetch_multi(const GemmParams& p, int first,
+                                          FactorTab<kLdsAdapters>& tab) {
+  const int cb0 = first / p.n_rg;
+  const ColBlock c = p.cbl[cb0 < p.cb_cap ? cb0 : p.cb_cap - 1];
+  if (p.num_adapters <= kLdsAdapters) {
+    for (int e = threadIdx.x; e < p.num_adapters; e += blockDim.x) {
+      tab.ptr[e][0] = p.B1s[e];
+      tab.ptr[e][1] = p.B2s[e];
+      tab.ptr[e][2] = p.alphas[e];
+      tab.ptr[e][3] = p.betas[e];
+    }
+  }
+  __syncthreads();
+  return c;
+}
+__device__ inline void factors_of(const GemmParams& p, const FactorTab<kLdsAdapters>& tab, int ad,
+                                  Factors& f) {
+  if (p.num_adapters <= kLdsAdapters) {
+    f.B1 = (const uint32_t*)tab.ptr[ad][0];
+    f.B2 = (const uint32_t*)tab.ptr[ad][1];
+    f.alpha = (const half_t*)tab.ptr[ad][2];
+    f.beta = (const half_t*)tab.ptr[ad][3];
+  } else {
+    f.B1 = p.B1s[ad];
+    f.B2 = p.B2s[ad];
+    f.alpha = p.alphas[ad];
+    f.beta = p.betas[ad];
+  }
+}
+
 template <int STAGE, int NC, bool SPLITK, bool MULTI, bool XIN, int NWV, bool GROUP>
 __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
   static_assert(!XIN || (STAGE == 1 && !MULTI), "x is read in place by single-adapter stage 1");
@@ -308,6 +350,9 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
   // tiles in that XCD's L2
   const int b = blockIdx.x;
   const int first = p.xcd_remap ? (b & 7) * (p.grid >> 3) + (b >> 3) : b;
+  __shared__ FactorTab<MULTI ? kLdsAdapters : 1> ftab;
+  ColBlock cb_first{};
+  if constexpr (MULTI) cb_first = prefetch_multi(p, first, ftab);
 
   for (int it = first; it < n_items; it += p.grid) {
     int layer = 0, itl = it;
@@ -321,17 +366,13 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
     void* const yl = (char*)p.y + (GROUP ? layer * p.y_layer_bytes : 0);
     int t0, t1, ad;
     Factors f;
-    if (MULTI) {
-      const ColBlock cbk = p.cbl[cb];
+    if constexpr (MULTI) {
+      const ColBlock cbk = it == first ? cb_first : p.cbl[cb];
       t0 = cbk.t0;
       t1 = cbk.t1;
       ad = cbk.adapter;
-      if (ad >= 0) {
-        f.B1 = p.B1s[ad];
-        f.B2 = p.B2s[ad];
-        f.alpha = p.alphas[ad];
-        f.beta = p.betas[ad];
-      }
+      if constexpr (MULTI)
+        if (ad >= 0) factors_of(p, ftab, ad, f);
     } else {
       t0 = cb * 16 * NC;
       t1 = t0 + 16 * NC < p.T ? t0 + 16 * NC : p.T;
@@ -571,19 +612,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int n_items = n_cb * p.n_rg;  // fits 32 bits (the host checks)
   const int nkb = p.nkb, ell = p.ell, rows = p.rows;
 
+  __shared__ FactorTab<kLdsAdapters> ftab;
+  ColBlock cb_first{};
+  if (p.multi) cb_first = prefetch_multi(p, blockIdx.x, ftab);
   for (int it = blockIdx.x; it < n_items; it += p.grid) {
     const int cb = it / p.n_rg, rg = it - cb * p.n_rg;
     int t0, t1, ad;
     Factors f;
     if (p.multi) {
-      const ColBlock cbk = p.cbl[cb];
+      const ColBlock cbk = it == (int)blockIdx.x ? cb_first : p.cbl[cb];
       t0 = cbk.t0;
       t1 = cbk.t1;
       ad = cbk.adapter;
-      if (ad >= 0) {
-        f.B1 = p.B1s[ad];
-        f.alpha = p.alphas[ad];
-      }
+      if (ad >= 0) factors_of(p, ftab, ad, f);
     } else {
       t0 = cb * 16 * NC;
       t1 = t0 + 16 * NC < p.T ? t0 + 16 * NC : p.T;
@@ -857,6 +898,8 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
   p.single = a.single;
   p.cbl = (const ColBlock*)(ws + L.cbl);
   p.hdr = (const WsHeader*)ws;
+  p.cb_cap = (int32_t)max_colblocks(a.T);
+  p.num_adapters = a.multi ? a.num_adapters : 0;
   p.B1s = a.B1s;
   p.B2s = a.B2s;
   p.alphas = a.alphas;
