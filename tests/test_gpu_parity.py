@@ -400,6 +400,24 @@ def test_multi_adapter_integer_unsorted_invalid(path):
                           _multi_ref(B, ids, y_old=base).astype(np.float32).astype(np.float64))
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_multi_adapter_many_adapters(path):
+    """More adapters than the stage kernels keep pointer tables for in LDS
+    (256): the factor pointers are then read from the device tables.  Exact
+    on integer inputs, including ids out of range."""
+    B = synth.make_multi_adapter(num_adapters=300, N=72, R=40, M=136, ell=2, T=700, seed=23,
+                                 alpha="ones", beta="ones", gamma="ones", x_kind="int3",
+                                 zipf_s=0.3)
+    ids = B.ids.copy()
+    ids[[3, 400]] = [-1, 300]
+    assert len(np.unique(ids[(ids >= 0) & (ids < 300)])) > 256
+    D = H().DeviceAdapters(B.adapters)
+    y = D.forward(H().to_dev(B.x), H().to_dev(ids), path=path, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64),
+                          _multi_ref(B, ids).astype(np.float32).astype(np.float64))
+
+
 def test_multi_adapter_permutation_invariance():
     B = synth.make_multi_adapter(num_adapters=8, N=256, R=64, M=256, ell=2, T=300, seed=33)
     D = H().DeviceAdapters(B.adapters)
