@@ -1271,7 +1271,8 @@ constexpr int kStreamD = 8;    // sign loads in flight per lane
 constexpr int64_t kStreamLdsB = 32 * 1024;  // LDS budget for staged B operands
 
 // A stage that builds its own operand parts: 16 waves per workgroup, so a
-// wave's chunk is kc <= 2 blocks, one quad of row tiles per item.
+// wave's chunk is kc = 1, 2 or 4 blocks (4: one adapter, not grouped), one
+// quad of row tiles per item.
 template <int STAGE>
 static hipError_t launch_gemv_pin(GemvParams p, int kc, hipStream_t s) {
   p.nq = cdiv(p.nrt, kQuad);
@@ -1287,6 +1288,8 @@ static hipError_t launch_gemv_pin(GemvParams p, int kc, hipStream_t s) {
       hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 2, false, true, 16, true>), g, b, 0, s, p);
   } else if (kc == 1) {
     hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 1, false, true, 16>), g, b, 0, s, p);
+  } else if (kc == 4) {
+    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 4, false, true, 16>), g, b, 0, s, p);
   } else {
     hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 2, false, true, 16>), g, b, 0, s, p);
   }
@@ -1450,15 +1453,15 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
   }
 
   // With one adapter and at most two columns per operand part (ell *
-  // tokens <= 2, the decode case), a stage whose reduction is at most 32
-  // blocks builds its operand parts itself (0: a prep launch does).  Every
-  // workgroup builds the parts of the whole reduction, so this pays only
-  // while that is short: at 50 blocks (4 per wave) it measured slower than
-  // the prep launch.
+  // tokens <= 2, the decode case), a stage whose reduction is at most 64
+  // blocks (32 when grouped) builds its operand parts itself (0: a prep
+  // launch does).  Every workgroup builds the parts of the whole reduction,
+  // so this pays only while that is short: at 50 blocks (4 per wave) it
+  // saves the prep launch by a small margin.
   auto pin_kc = [&](int64_t nkb) -> int {
     const int64_t ntok = a.T < tcb ? a.T : tcb;
     if (a.multi || (int64_t)a.ell * ntok > kPinColTokens) return 0;
-    return nkb <= 16 ? 1 : nkb <= 32 ? 2 : 0;
+    return nkb <= 16 ? 1 : nkb <= 32 ? 2 : (nkb <= 64 && a.group <= 1) ? 4 : 0;
   };
   // stage 1 reads gamma and x as aligned pairs of entries: M even and every
   // gamma 4-byte aligned (x rows are 16-byte aligned by the boundary's rules)
