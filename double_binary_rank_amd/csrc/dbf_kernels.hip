@@ -131,9 +131,19 @@ size_t workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T) 
   return ws_layout(N, R, M, ell, T).total;
 }
 
-Path choose_path(int64_t T, int64_t per_seg) {
-  (void)T;
-  return per_seg <= 16 ? Path::Gemv : Path::Mfma;
+// The small-T path streams the signs once per column block of at most 5
+// tokens; the large-T path costs a fixed few launches' latency, lowest when
+// stage 1 reads x in place (a reduction of at most 8 blocks per wave, M <=
+// 8192).  Whole calls replayed from graphs put the crossover at:
+//   rank 64 (4096 x 4096): small-T faster through T = 12;
+//   rank 2048 (4096 x 4096): large-T faster from T = 3;
+//   rank 6368, 14336 x 4096: even at T = 2..5, large-T much faster from 6;
+//   rank 6368, 4096 x 14336: small-T faster through T = 8, large-T at 12.
+Path choose_path(int64_t per_seg, int64_t R, int64_t M) {
+  if (R < 256) return per_seg <= 16 ? Path::Gemv : Path::Mfma;
+  if (per_seg <= 2) return Path::Gemv;
+  if (M <= 8192) return Path::Mfma;
+  return per_seg < 12 ? Path::Gemv : Path::Mfma;
 }
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
