@@ -48,10 +48,10 @@ dbf_status check_common(const void* x, int64_t ldx, int64_t N, int64_t R, int64_
   return DBF_OK;
 }
 
-dbf::Path pick_path(uint32_t flags, int64_t per_segment, int64_t R, int64_t M) {
+dbf::Path pick_path(uint32_t flags, int64_t per_segment, int64_t R, int64_t M, bool multi) {
   if (flags & DBF_PATH_GEMV) return dbf::Path::Gemv;
   if (flags & DBF_PATH_MFMA) return dbf::Path::Mfma;
-  return dbf::choose_path(per_segment, R, M);
+  return dbf::choose_path(per_segment, R, M, multi);
 }
 
 }  // namespace
@@ -148,7 +148,7 @@ dbf_status dbf_forward(const void* x, int64_t ldx, const uint32_t* B1, const uin
   a.multi = false;
   a.ws = ws;
   a.ws_bytes = ws_bytes;
-  a.path = pick_path(flags, T, R, M);
+  a.path = pick_path(flags, T, R, M, false);
   a.phases = phases_of(flags);
   return hip_status(dbf::launch_forward(a, (hipStream_t)stream));
 }
@@ -194,7 +194,7 @@ dbf_status dbf_forward_multi_adapter(const void* x, int64_t ldx, int64_t T, cons
   a.ws = ws;
   a.ws_bytes = ws_bytes;
   const int64_t per = T / (num_adapters < T ? num_adapters : T);
-  a.path = pick_path(flags, per, R, M);
+  a.path = pick_path(flags, per, R, M, true);
   a.phases = phases_of(flags);
   return hip_status(dbf::launch_forward(a, (hipStream_t)stream));
 }
@@ -253,7 +253,7 @@ dbf_status dbf_forward_grouped(const void* x, int64_t ldx, int64_t T, int32_t nu
   a.multi = false;
   a.ws = ws;
   a.ws_bytes = layer_ws;
-  a.path = pick_path(flags, T, R, M);
+  a.path = pick_path(flags, T, R, M, false);
   a.phases = phases_of(flags);
   a.group = num_layers;
   a.y_layer_bytes = y_layer_stride * esz;

@@ -139,8 +139,10 @@ size_t workspace_bytes(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T) 
 //   rank 2048 (4096 x 4096): large-T faster from T = 3;
 //   rank 6368, 14336 x 4096: even at T = 2..5, large-T much faster from 6;
 //   rank 6368, 4096 x 14336: small-T faster through T = 8, large-T at 12.
-Path choose_path(int64_t per_seg, int64_t R, int64_t M) {
-  if (R < 256) return per_seg <= 16 ? Path::Gemv : Path::Mfma;
+//   The multi-adapter call (whose large-T stage 1 never reads x in place)
+//   keeps 16 tokens per segment as the switch, as measured on its batch.
+Path choose_path(int64_t per_seg, int64_t R, int64_t M, bool multi) {
+  if (multi || R < 256) return per_seg <= 16 ? Path::Gemv : Path::Mfma;
   if (per_seg <= 2) return Path::Gemv;
   if (M <= 8192) return Path::Mfma;
   return per_seg < 12 ? Path::Gemv : Path::Mfma;

@@ -106,7 +106,7 @@ hipError_t launch_transpose(const uint32_t* src, int64_t rows, int64_t cols, uin
                             hipStream_t s);
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t s);
-Path choose_path(int64_t tokens_per_segment_estimate, int64_t R, int64_t M);
+Path choose_path(int64_t tokens_per_segment_estimate, int64_t R, int64_t M, bool multi);
 // tokens per column block on the small-T path (3 fp8 parts x ell terms
 // x tokens must fit the 16 columns of one MFMA); 0 if ell is too large.
 inline int gemv_tokens_per_block(int32_t ell) { return ell <= 5 ? 16 / (kParts * ell) : 0; }

@@ -55,10 +55,11 @@ typedef int32_t dbf_dtype;
 #define DBF_ACCUMULATE 1u /* y += product (unmerged adapter branch added onto
                              a base output, LoRDBA summary section 1); the
                              default overwrites y                            */
-/* Without a path flag the library chooses by tokens per segment (T, or T
-   over the adapters in use), the rank R and the reduction M: the small-T
-   kernels up to 2 tokens per segment (up to 16 when R < 256, and up to 11
-   when M > 8192), the large-T kernels above. */
+/* Without a path flag the library chooses by tokens per call, the rank R
+   and the reduction M: the small-T kernels up to 2 tokens (up to 16 when
+   R < 256, and up to 11 when M > 8192), the large-T kernels above.  The
+   multi-adapter call takes the small-T kernels up to 16 tokens per adapter
+   in use (T over min(T, num_adapters)). */
 #define DBF_PATH_GEMV 2u  /* force the small-T (decode) kernels  (tuning/tests) */
 #define DBF_PATH_MFMA 4u  /* force the large-T (prefill) kernels (tuning/tests) */
 /* Run only some phases of one product (profiling, or overlapping other work
