@@ -301,6 +301,12 @@ def main():
         achieved_tflops = flops / t_call / 1e12
         log(f"prefill T=256: {t_call * 1e6:.2f} us/call, {achieved_tflops:.1f} TFLOP/s")
         out["prefill_T256_call_us"] = call_percentiles(call256, 200, 10)
+        # the whole call replayed from a HIP graph (no host launch gaps)
+        t_g = time_graph(call256, 64, max(args.steps // 16, 4), 2)
+        out["prefill_T256_graph"] = {"us_per_call": t_g * 1e6, "tokens_per_s": T / t_g,
+                                     "TFLOPs": flops / t_g / 1e12}
+        log(f"prefill T=256 replayed from a graph: {t_g * 1e6:.2f} us/call, "
+            f"{T / t_g / 1e6:.2f} M tokens/s")
         log("prefill per-call us: " + ", ".join(
             f"{k} {v:.2f}" for k, v in out["prefill_T256_call_us"].items() if k != "calls"))
 
