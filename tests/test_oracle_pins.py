@@ -701,8 +701,109 @@ def pin_factorize_fixed_point(fact):
     return bool(ok)
 
 
+def _project_by_eig(Y):
+    """The scaled-sign projection from its definition, by another route than
+    an SVD: sign(Y) (0 -> +1) times the best rank-1 approximation of |Y|,
+    whose right factor is the top eigenvector v of |Y|^T |Y| (eigh), giving
+    (|Y| v) v^T."""
+    A = np.abs(Y)
+    _, vecs = np.linalg.eigh(A.T @ A)
+    v = vecs[:, -1]
+    return np.where(Y < 0, -1.0, 1.0) * np.outer(A @ v, v)
+
+
+def _ls_side_a(W, F, target, rho):
+    """argmin_X ||X F - W||^2 + rho ||X - target||^2, by least squares on the
+    stacked system [F^T; sqrt(rho) I] X^T = [W^T; sqrt(rho) target^T]."""
+    k = F.shape[0]
+    return np.linalg.lstsq(np.vstack([F.T, math.sqrt(rho) * np.eye(k)]),
+                           np.vstack([W.T, math.sqrt(rho) * target.T]), rcond=None)[0].T
+
+
+def _admm_by_definition(W, F, Z, iters, rho0):
+    """Side A of the ADMM half step in scaled form, each update taken from its
+    defining minimisation: X_j minimises ||X F - W||^2 + rho ||X - Z_{j-1} +
+    U_{j-1}||^2, Z_j is the projection of X_j + U_{j-1}, and the dual U_j =
+    U_{j-1} + X_j - Z_j (U_0 = 0).  Returns every (X_j, Z_j, U_j)."""
+    k = F.shape[0]
+    rho = rho0 * np.trace(F @ F.T) / k
+    U = np.zeros_like(Z)
+    out = []
+    for _ in range(iters):
+        X = _ls_side_a(W, F, Z - U, rho)
+        grad = (X @ F - W) @ F.T + rho * (X - Z + U)  # stationarity of the X update
+        assert np.abs(grad).max() < 1e-8 * max(1.0, np.abs(W).max() * np.abs(F).max() ** 2)
+        Z = _project_by_eig(X + U)
+        U = U + X - Z
+        out.append((X, Z, U))
+    return out
+
+
+def pin_admm_iterations(admm):
+    """Several iterations: after j >= 2 iterations the half step must return
+    Z_j of the scaled-form recurrence above, which uses the dual from the
+    iterations before (a plain alternating projection, or a dual with the
+    wrong sign, gives another Z_2).  Side B is side A on the transposed
+    problem."""
+    rng = np.random.default_rng(44)
+    N, M, k = 9, 8, 3
+    W = rng.standard_normal((N, M))
+    u, S, v = _scaled_sign(rng, k, M)
+    F = u[:, None] * S * v[None, :]
+    u0, S0, v0 = _scaled_sign(rng, N, k)
+    Z0 = u0[:, None] * S0 * v0[None, :]
+    ref = _admm_by_definition(W, F, Z0, 4, 1.0)
+    ok = True
+    # the dual is not negligible at these sizes: otherwise the pin is blind
+    ok &= np.abs(ref[0][2]).max() > 1e-3 * np.abs(ref[0][1]).max()
+    for j in (2, 3, 4):
+        Zj = admm(W, F, "A", Z0, j, 1.0)
+        ok &= np.allclose(Zj, ref[j - 1][1], rtol=1e-9, atol=1e-11)
+        ZB = admm(W.T, F.T, "B", Z0.T, j, 1.0)
+        ok &= np.allclose(ZB, ref[j - 1][1].T, rtol=1e-9, atol=1e-11)
+    return bool(ok)
+
+
+def pin_factorize_alternation(fact):
+    """One outer step from an exact first factor X* and a perturbed second
+    factor: side A runs its ADMM against the perturbed Y, then side B runs
+    its ADMM against the updated X, starting from the perturbed Y.  Both are
+    recomputed from the recurrence above (side B through the transposed
+    problem), and the returned layer must be their product."""
+    rng = np.random.default_rng(45)
+    N, M, k = 11, 9, 4
+    a, A, m = _scaled_sign(rng, N, k)
+    r, B, b = _scaled_sign(rng, k, M)
+    Xs, Ys = a[:, None] * A * m[None, :], r[:, None] * B * b[None, :]
+    W = Xs @ Ys
+    Bp = B.copy()
+    flip = rng.random(B.shape) < 0.3
+    Bp[flip] *= -1
+    Yp = r[:, None] * Bp * (b * np.exp(rng.normal(0, 0.2, M)))[None, :]
+    iters = 3
+    Xn = _admm_by_definition(W, Yp, Xs, iters, 1.0)[-1][1]
+    Yn = _admm_by_definition(W.T, Xn.T, Yp.T, iters, 1.0)[-1][1].T
+    f = fact(W, k, None, 1, iters, 1.0, start=(Xs, Yp))
+    dw = (f["alpha"][:, None] * f["S1"] * f["beta"][None, :]) @ (f["S2"] * f["gamma"][None, :])
+    ok = np.allclose(dw, Xn @ Yn, rtol=1e-9, atol=1e-11)
+    ok &= np.array_equal(f["S1"], np.where(Xn < 0, -1, 1))
+    ok &= np.array_equal(f["S2"], np.where(Yn < 0, -1, 1))
+    ok &= abs(f["rel_err"] - np.linalg.norm(W - Xn @ Yn) / np.linalg.norm(W)) < 1e-10
+    # the pin is not blind: side B moved away from where it started
+    ok &= np.abs(Yn - Yp).max() > 1e-3 * np.abs(Yp).max()
+    return bool(ok)
+
+
 def test_svid_pins():
     assert pin_svid(oracle.svid)
+
+
+def test_admm_iteration_pins():
+    assert pin_admm_iterations(oracle.admm_scaled_sign)
+
+
+def test_factorize_alternation_pin():
+    assert pin_factorize_alternation(oracle.factorize)
 
 
 def test_admm_step_pins():
@@ -741,6 +842,55 @@ def test_factorisation_pins_reject_mutants():
         f["beta"] = f["beta"][::-1].copy()
         return f
     assert not pin_factorize_fixed_point(fact_swapped)
+
+    def admm_no_dual(W, F, side, Z, iters, rho0):
+        # plain alternating projection: the dual variable is never carried
+        for _ in range(iters):
+            Z = oracle.admm_scaled_sign(W, F, side, Z, 1, rho0)
+        return Z
+    assert not pin_admm_iterations(admm_no_dual)
+
+    def admm_dual_sign_flipped(W, F, side, Z, iters, rho0):
+        W, F, Z = np.asarray(W, float), np.asarray(F, float), np.asarray(Z, float)
+        k = F.shape[0] if side == "A" else F.shape[1]
+        G = F @ F.T if side == "A" else F.T @ F
+        rho = rho0 * np.trace(G) / k
+        base = W @ F.T if side == "A" else F.T @ W
+        U = np.zeros_like(Z)
+        for _ in range(iters):
+            rhs = base + rho * (Z - U)
+            X = (np.linalg.solve(G + rho * np.eye(k), rhs.T).T if side == "A"
+                 else np.linalg.solve(G + rho * np.eye(k), rhs))
+            pu, pS, pv = oracle.svid(X + U)
+            Z = pu[:, None] * pS * pv[None, :]
+            U = U - X + Z
+        return Z
+    assert not pin_admm_iterations(admm_dual_sign_flipped)
+
+    def fact_skip_side_b(W, k, omega, outer, iters, rho0=1.0, start=None):
+        # never updates the second factor
+        X, Y = np.asarray(start[0], float), np.asarray(start[1], float)
+        for _ in range(outer):
+            X = oracle.admm_scaled_sign(W, Y, "A", X, iters, rho0)
+        a, A, m = oracle.svid(X)
+        r, B, b = oracle.svid(Y)
+        dw = (a[:, None] * A * (m * r)[None, :]) @ (B * b[None, :])
+        return {"alpha": a, "S1": A, "beta": m * r, "S2": B, "gamma": b,
+                "rel_err": float(np.linalg.norm(W - dw) / np.linalg.norm(W))}
+    assert not pin_factorize_alternation(fact_skip_side_b)
+    assert pin_factorize_fixed_point(fact_skip_side_b)  # the old pin alone missed it
+
+    def fact_sides_swapped(W, k, omega, outer, iters, rho0=1.0, start=None):
+        X, Y = np.asarray(start[0], float), np.asarray(start[1], float)
+        for _ in range(outer):
+            Y = oracle.admm_scaled_sign(W, X, "B", Y, iters, rho0)
+            X = oracle.admm_scaled_sign(W, Y, "A", X, iters, rho0)
+        a, A, m = oracle.svid(X)
+        r, B, b = oracle.svid(Y)
+        dw = (a[:, None] * A * (m * r)[None, :]) @ (B * b[None, :])
+        return {"alpha": a, "S1": A, "beta": m * r, "S2": B, "gamma": b,
+                "rel_err": float(np.linalg.norm(W - dw) / np.linalg.norm(W))}
+    assert not pin_factorize_alternation(fact_sides_swapped)
 
 
 # ------------------------------------------- non-uniform ranks, pruning ----
