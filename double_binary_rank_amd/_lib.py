@@ -9,7 +9,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdbf.so")
+# DBF_LIB_PATH names another build of the same library (a host-sanitized
+# checking build); by default the in-tree libdbf.so
+LIB_PATH = os.environ.get("DBF_LIB_PATH") or os.path.join(HERE, "libdbf.so")
 
 DBF_OK = 0
 DBF_ERR_INVALID_ARG = -1

@@ -144,6 +144,41 @@ def _ws(ws, N, R, M, ell, T, device):
     return ws
 
 
+def _need(t, name, dtype, contiguous=False):
+    """The C ABI reads raw memory: reject a tensor whose dtype, device or
+    layout it would misread."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _check_scales(alpha, beta, gamma):
+    for name, t in (("alpha", alpha), ("beta", beta), ("gamma", gamma)):
+        _need(t, name, torch.float16, contiguous=True)
+
+
+def _check_out(y):
+    if y is not None and y.dtype not in (torch.float16, torch.float32):
+        raise TypeError(f"y must be float16 or float32, got {y.dtype}")
+
+
+def _keep_alive(stream, *tensors):
+    """Buffers made here for work on another stream than the current one:
+    tell the caching allocator that stream uses them, so their memory is not
+    reused before that work has run."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torch.Tensor,
                 beta: torch.Tensor, gamma: torch.Tensor, N: int, R: int, M: int, *,
                 y: torch.Tensor | None = None, y_dtype=torch.float16, accumulate: bool = False,
@@ -155,16 +190,24 @@ def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torc
     beta [ell][R], gamma [ell][M] fp16 contiguous.  ``phases`` (a name or a
     list of "prep", "stage1", "stage2") runs only those phases
     (DBF_RUN_PREP / DBF_RUN_STAGE1 / DBF_RUN_STAGE2); None runs all."""
+    _need(x, "x", torch.float16)
+    _need(B1, "B1", None)
+    _need(B2, "B2", None)
+    _check_scales(alpha, beta, gamma)
+    _check_out(y)
     T = x.shape[0]
     ell = alpha.shape[0] if alpha.dim() == 2 else 1
     ldx = _row_major(x, "x")
+    made_y, made_ws = y is None, ws is None
     y, ldy = _out(y, T, N, y_dtype, x.device)
     ws = _ws(ws, N, R, M, ell, T, x.device)
     yt = _DTYPE[y.dtype]
     check(lib.dbf_forward(_ptr(x), ldx, _ptr(B1), _ptr(B2), _ptr(alpha), _ptr(beta), _ptr(gamma),
                           N, R, M, ell, T, _ptr(y), ldy, yt, _flags(accumulate, path, phases), _ptr(ws),
                           ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward")
+    _keep_alive(stream, y if made_y else None, ws if made_ws else None)
     return y
+
 
 
 def dbf_grouped_workspace_bytes(N: int, R: int, M: int, ell: int, T: int, num_layers: int) -> int:
@@ -180,8 +223,13 @@ def dbf_forward_grouped(x: torch.Tensor, layers, *, y: torch.Tensor | None = Non
     J = len(layers)
     p0 = layers[0]
     N, R, M, ell = p0.N, p0.R, p0.M, p0.ell
+    _need(x, "x", torch.float16)
+    for p in layers:
+        _check_scales(p.alpha, p.beta, p.gamma)
+    _check_out(y)
     T = x.shape[0]
     ldx = _row_major(x, "x")
+    made_y, made_ws = y is None, ws is None
     if y is None:
         y = torch.empty((J, T, _padded_cols(N, y_dtype)), dtype=y_dtype, device=x.device)[:, :, :N]
     if y.dim() != 3 or y.shape[0] != J or y.stride(2) != 1:
@@ -197,6 +245,7 @@ def dbf_forward_grouped(x: torch.Tensor, layers, *, y: torch.Tensor | None = Non
         arr([p.gamma for p in layers]), N, R, M, ell, _ptr(y), ldy, ys, _DTYPE[y.dtype],
         _flags(accumulate, path, phases), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)), "dbf_forward_grouped")
+    _keep_alive(stream, y if made_y else None, ws if made_ws else None)
     return y
 
 
@@ -216,10 +265,14 @@ def dbf_backward(x: torch.Tensor, g: torch.Tensor, B1: torch.Tensor, B2: torch.T
     dS2 [R][M]; with fp32 latents H1 [N][R] / H2 [R][M] and a temperature tau,
     the straight-through gradients dH1 / dH2.  B1t and B2t are the packed
     transposes (``dbf_transpose_signs``)."""
+    _need(x, "x", torch.float16)
+    _need(g, "g", torch.float16)
+    _check_scales(alpha, beta, gamma)
     T = x.shape[0]
     ell = alpha.shape[0] if alpha.dim() == 2 else 1
     dev = x.device
     ldx, ldg = _row_major(x, "x"), _row_major(g, "g")
+    made_ws = ws is None
     dx = torch.empty((T, M), dtype=dx_dtype, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dx": dx, "dalpha": torch.empty((ell, N), **f32), "dbeta": torch.empty((ell, R), **f32),
@@ -242,6 +295,7 @@ def dbf_backward(x: torch.Tensor, g: torch.Tensor, B1: torch.Tensor, B2: torch.T
         _ptr(out.get("dS2")), _ptr(H1), _ptr(H2), 0.0 if tau is None else float(tau),
         _ptr(out.get("dH1")), _ptr(out.get("dH2")), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)), "dbf_backward")
+    _keep_alive(stream, *out.values(), ws if made_ws else None)
     return out
 
 
@@ -257,9 +311,13 @@ def dbf_factorize(W: torch.Tensor, k: int, omega: torch.Tensor | None = None, *,
     [1][k], gamma [1][M] fp16 and rel_err (a 0-d fp32 device tensor).  omega
     [k][N] fp32 is the caller's Gaussian sketch for the start, or ``start`` =
     (X0, Y0) fp32 scaled sign matrices."""
+    _need(W, "W", torch.float32)
+    if omega is not None:
+        _need(omega, "omega", torch.float32, contiguous=True)
     N, M = W.shape
     ldw = _row_major(W, "W")
     dev = W.device
+    made_ws = ws is None
     out = {"S1": torch.empty((N, k), dtype=torch.int8, device=dev),
            "S2": torch.empty((k, M), dtype=torch.int8, device=dev),
            "alpha": torch.empty((1, N), dtype=torch.float16, device=dev),
@@ -268,7 +326,7 @@ def dbf_factorize(W: torch.Tensor, k: int, omega: torch.Tensor | None = None, *,
            "rel_err": torch.empty((), dtype=torch.float32, device=dev)}
     X0 = Y0 = None
     if start is not None:
-        X0, Y0 = (t.contiguous() for t in start)
+        X0, Y0 = (_need(t, "start", torch.float32).contiguous() for t in start)
     if ws is None:
         ws = torch.empty(dbf_factorize_workspace_bytes(N, M, k), dtype=torch.uint8, device=dev)
     check(lib.dbf_factorize(
@@ -276,6 +334,7 @@ def dbf_factorize(W: torch.Tensor, k: int, omega: torch.Tensor | None = None, *,
         float(rho0), _ptr(out["S1"]), _ptr(out["S2"]), _ptr(out["alpha"]), _ptr(out["beta"]),
         _ptr(out["gamma"]), _ptr(out["rel_err"]), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)), "dbf_factorize")
+    _keep_alive(stream, *out.values(), ws if made_ws else None, X0, Y0)
     return out
 
 
@@ -334,8 +393,19 @@ def dbf_forward_multi_adapter(x: torch.Tensor, ids: torch.Tensor, B1s: torch.Ten
                               phases=None) -> torch.Tensor:
     """Token t uses adapter ids[t]; the five tables are device int64 arrays
     of per-adapter device pointers (see ``pointer_table``)."""
+    _need(x, "x", torch.float16)
+    _need(ids, "ids", torch.int32, contiguous=True)
+    for name, t in (("B1s", B1s), ("B2s", B2s), ("alphas", alphas), ("betas", betas),
+                    ("gammas", gammas)):
+        _need(t, name, torch.int64, contiguous=True)
+        if t.numel() < num_adapters:
+            raise ValueError(f"{name} holds fewer than num_adapters pointers")
+    if ids.numel() != x.shape[0]:
+        raise ValueError("ids must hold one id per token row of x")
+    _check_out(y)
     T = x.shape[0]
     ldx = _row_major(x, "x")
+    made_y, made_ws = y is None, ws is None
     y, ldy = _out(y, T, N, y_dtype, x.device)
     ws = _ws(ws, N, R, M, ell, T, x.device)
     yt = _DTYPE[y.dtype]
@@ -343,6 +413,7 @@ def dbf_forward_multi_adapter(x: torch.Tensor, ids: torch.Tensor, B1s: torch.Ten
         _ptr(x), ldx, T, _ptr(ids), num_adapters, _ptr(B1s), _ptr(B2s), _ptr(alphas), _ptr(betas),
         _ptr(gammas), N, R, M, ell, _ptr(y), ldy, yt, _flags(accumulate, path, phases), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward_multi_adapter")
+    _keep_alive(stream, y if made_y else None, ws if made_ws else None)
     return y
 
 

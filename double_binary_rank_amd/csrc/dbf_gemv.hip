@@ -168,12 +168,12 @@ __global__ __launch_bounds__(256) void k_prep(PrepParams p) {
       v1 = k + 1 < p.K ? h(g1) * h(x1) : 0.0f;
     }
   }
-  uint8_t* out = (uint8_t*)p.opnd + blk * (kParts * 4 * 32);
+  uint8_t* out = (uint8_t*)p.opnd + (int64_t)blk * (kParts * 4 * 32);
   // kl even: cols kl, kl+1 meet adjacent operand entries, i.e. adjacent bytes
   const int boff = fp8_operand_byte(operand_k_of_col(kl));
   block_parts(v0, v1, [&](int part, uint16_t code, int s) {
     *(uint16_t*)(out + part * 128 + boff) = code;
-    if (lane < 4) p.oscl[blk * (kParts * 4) + part * 4 + lane] = (uint8_t)(s + 127);
+    if (lane < 4) p.oscl[(int64_t)blk * (kParts * 4) + part * 4 + lane] = (uint8_t)(s + 127);
   });
 }
 
@@ -1431,7 +1431,13 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
     const int64_t rz = cdiv(a.R, kColBlock) * kColBlock;
     const int64_t lds = lds_b + 48 + lds_s + 2 * (int64_t)a.ell * rows_pad * (int64_t)sizeof(half_t) +
                         n_slots * (int64_t)sizeof(ColBlock) + (int64_t)a.ell * tcb * rz * 4;
-    if (lds <= kFusedLdsMax) {
+    // the kernel's static LDS (its id counters and segmentation arrays)
+    // shares the budget with the dynamic part
+    hipFuncAttributes fa{};
+    const bool fa_ok =
+        hipFuncGetAttributes(&fa, (const void*)k_gemv_fused<kFusedD, kFusedNW>) == hipSuccess;
+    const int64_t lds_static = fa_ok ? (int64_t)fa.sharedSizeBytes : 4096;
+    if (lds + lds_static <= kFusedLdsMax) {
       g1.nq = cdiv(g1.nrt, kQuad);
       g2.nq = cdiv(g2.nrt, kQuad);
       g1.lds_b = g2.lds_b = lds_b;

@@ -68,18 +68,22 @@ def run_layer(L, path=None, y_dtype=torch.float16, accumulate=False, y_init=None
 class DeviceAdapters:
     """Per-adapter packed factors plus the device pointer tables."""
 
-    def __init__(self, adapters):
+    def __init__(self, adapters, entries=None):
+        """``entries``: for each pointer-table entry, the index of the adapter
+        it points to (default: one entry per adapter)."""
         self.layers = [upload(a) for a in adapters]
         dev = "cuda"
-        self.B1s = dbf.pointer_table([p.B1 for p in self.layers], dev)
-        self.B2s = dbf.pointer_table([p.B2 for p in self.layers], dev)
-        self.alphas = dbf.pointer_table([p.alpha for p in self.layers], dev)
-        self.betas = dbf.pointer_table([p.beta for p in self.layers], dev)
-        self.gammas = dbf.pointer_table([p.gamma for p in self.layers], dev)
+        tab = self.layers if entries is None else [self.layers[e] for e in entries]
+        self.n_entries = len(tab)
+        self.B1s = dbf.pointer_table([p.B1 for p in tab], dev)
+        self.B2s = dbf.pointer_table([p.B2 for p in tab], dev)
+        self.alphas = dbf.pointer_table([p.alpha for p in tab], dev)
+        self.betas = dbf.pointer_table([p.beta for p in tab], dev)
+        self.gammas = dbf.pointer_table([p.gamma for p in tab], dev)
         p0 = self.layers[0]
         self.N, self.R, self.M, self.ell = p0.N, p0.R, p0.M, p0.ell
 
     def forward(self, x, ids, **kw):
         return dbf.dbf_forward_multi_adapter(
-            x, ids, self.B1s, self.B2s, self.alphas, self.betas, self.gammas, len(self.layers),
+            x, ids, self.B1s, self.B2s, self.alphas, self.betas, self.gammas, self.n_entries,
             self.N, self.R, self.M, self.ell, **kw)

@@ -504,6 +504,54 @@ def test_multi_adapter_fused_decode(ell, integer, T, max_run):
         assert oracle.max_norm_error(split, want) <= TOL
 
 
+@pytest.mark.parametrize("integer", [False, True])
+def test_grouped_decode_full_size(integer):
+    """The grouped decode at its real shape: 256 one-token adapters of the
+    attention projection (4096, 2048, 4096) in one multi-adapter call, which
+    takes the fused decode kernel with 32 and 16 reduction blocks per stage
+    (four and two rounds of its 8-deep sign ring, and the stage-1 ring
+    handing over to a long stage 2).  Eight distinct layers sit behind 32
+    table entries each; the ids are a permutation of 0..255.  Every token and
+    every output is compared with the oracle: bit for bit on integer inputs
+    with unit scales, within the bar on fp16 data with log-normal scales."""
+    kind = (dict(alpha="ones", beta="ones", gamma="ones", x_kind="int3") if integer else
+            dict(alpha="lognormal", beta="lognormal", gamma="lognormal"))
+    B = synth.make_multi_adapter(num_adapters=8, N=4096, R=2048, M=4096, ell=1, T=256,
+                                 seed=3900 + int(integer), **kind)
+    entries = [e % 8 for e in range(256)]
+    ids = np.random.default_rng(3910).permutation(256).astype(np.int32)
+    D = H().DeviceAdapters(B.adapters, entries=entries)
+    y = D.forward(H().to_dev(B.x), H().to_dev(ids), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = _multi_ref(B, ids % 8)
+    got = y.cpu().numpy().astype(np.float64)
+    if integer:
+        assert np.abs(want).max() < 2 ** 24
+        assert np.array_equal(got, want.astype(np.float32).astype(np.float64))
+    else:
+        err = oracle.max_norm_error(got, want)
+        assert err <= TOL, err
+        # and row by row: no token is left to the maximum of the others
+        for t in range(0, 256, 17):
+            assert oracle.max_norm_error(got[t], want[t]) <= 4 * TOL
+
+
+@pytest.mark.parametrize("T,N,y_f32", [(256, 8192, True), (250, 8000, False), (320, 8192, True)])
+def test_wide_token_blocks_integer(T, N, y_f32):
+    """Stage 2 with many row quads and tokens (ceil(T/64) * ceil(N/64) >= 512
+    and a reduction of at least four 128-blocks): the large-T path's widest
+    token blocks, bit for bit on integer inputs, with a partial last token
+    block and a ragged last row quad in the second case."""
+    L = synth.make_layer(N, 512, 256, 1, T, seed=3950 + T, alpha="ones", beta="ones",
+                         gamma="ones", x_kind="int3")
+    want = oracle.forward(L.x, L.S1, L.S2, L.alpha, L.beta, L.gamma)
+    got = H().run_layer(L, path="mfma", y_dtype=torch.float32 if y_f32 else torch.float16)
+    if y_f32:
+        assert np.array_equal(got, want.astype(np.float32).astype(np.float64))
+    else:
+        assert np.array_equal(got, oracle.fp16_rne(want).astype(np.float64))
+
+
 def test_multi_adapter_fused_accumulate_fp16():
     """Fused decode with ACCUMULATE into an fp16 output: rows of out-of-range
     ids keep their old values, the others add the product."""
