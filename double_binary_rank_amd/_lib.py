@@ -18,6 +18,8 @@ DBF_ERR_INVALID_ARG = -1
 DBF_ERR_ALIGNMENT = -2
 DBF_ERR_WORKSPACE = -3
 DBF_ERR_HIP = -4
+DBF_ERR_TOO_LARGE = -5
+NO_ALLOC_SCRATCH_BYTES = 32 << 20
 
 DBF_I8 = 1
 DBF_F16 = 2
@@ -43,6 +45,7 @@ EXPORTS = (
     "dbf_transpose_signs",
     "dbf_workspace_bytes",
     "dbf_forward",
+    "dbf_forward_no_alloc",
     "dbf_forward_multi_adapter",
     "dbf_grouped_workspace_bytes",
     "dbf_forward_grouped",
@@ -111,6 +114,13 @@ lib.dbf_forward.argtypes = [
     _i64, _i64, _i64, _i32, _i64,  # N, R, M, ell, T
     _vp, _i64, _i32, _u32,  # y, ldy, y_type, flags
     _vp, _sz, _vp,  # ws, ws_bytes, stream
+]
+lib.dbf_forward_no_alloc.restype = _i32
+lib.dbf_forward_no_alloc.argtypes = [
+    _vp, _i64, _vp, _vp, _vp, _vp, _vp,  # x, ldx, B1, B2, alpha, beta, gamma
+    _i64, _i64, _i64, _i32, _i64,  # N, R, M, ell, T
+    _vp, _i64, _i32, _u32,  # y, ldy, y_type, flags
+    _vp,  # stream
 ]
 lib.dbf_forward_multi_adapter.restype = _i32
 lib.dbf_forward_multi_adapter.argtypes = [

@@ -23,6 +23,7 @@ __all__ = [
     "dbf_transpose_signs",
     "dbf_workspace_bytes",
     "dbf_forward",
+    "dbf_forward_no_alloc",
     "dbf_forward_multi_adapter",
     "dbf_grouped_workspace_bytes",
     "dbf_forward_grouped",
@@ -208,6 +209,27 @@ def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torc
     _keep_alive(stream, y if made_y else None, ws if made_ws else None)
     return y
 
+
+def dbf_forward_no_alloc(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor,
+                         alpha: torch.Tensor, beta: torch.Tensor, gamma: torch.Tensor, N: int,
+                         R: int, M: int, y: torch.Tensor, *, accumulate: bool = False,
+                         path: str | None = None, stream=None) -> torch.Tensor:
+    """dbf_forward with the library's static per-GPU workspace: the caller
+    passes the output y [T][N] (fp16 or fp32) and nothing is allocated."""
+    _need(x, "x", torch.float16)
+    _need(B1, "B1", None)
+    _need(B2, "B2", None)
+    _check_scales(alpha, beta, gamma)
+    _need(y, "y", None)
+    _check_out(y)
+    T = x.shape[0]
+    ell = alpha.shape[0] if alpha.dim() == 2 else 1
+    ldx, ldy = _row_major(x, "x"), _row_major(y, "y")
+    check(lib.dbf_forward_no_alloc(_ptr(x), ldx, _ptr(B1), _ptr(B2), _ptr(alpha), _ptr(beta),
+                                   _ptr(gamma), N, R, M, ell, T, _ptr(y), ldy, _DTYPE[y.dtype],
+                                   _flags(accumulate, path), _stream(stream)),
+          "dbf_forward_no_alloc")
+    return y
 
 
 def dbf_grouped_workspace_bytes(N: int, R: int, M: int, ell: int, T: int, num_layers: int) -> int:

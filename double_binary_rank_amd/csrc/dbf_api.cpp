@@ -1,12 +1,21 @@
 // C ABI of the library: synchronous argument validation, then launches on
-// the caller's stream.  No allocation, no global mutable state.
+// the caller's stream.  No allocation; the only global state is the table
+// of per-GPU addresses of dbf_forward_no_alloc's static scratch array.
 #include "../../include/dbf.h"
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "dbf_launch.h"
 
 using dbf::cdiv;
+
+// Workspace of dbf_forward_no_alloc: one static array per GPU, part of the
+// loaded code object.  In host code its name is only a stand-in; the device
+// address of each GPU's copy is looked up once (hipGetSymbolAddress with that
+// GPU current) and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[DBF_NO_ALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -48,6 +57,35 @@ dbf_status check_common(const void* x, int64_t ldx, int64_t N, int64_t R, int64_
   return DBF_OK;
 }
 
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the GPU that runs `stream`.
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 dbf::Path pick_path(uint32_t flags, int64_t per_segment, int64_t R, int64_t M, bool multi) {
   if (flags & DBF_PATH_GEMV) return dbf::Path::Gemv;
   if (flags & DBF_PATH_MFMA) return dbf::Path::Mfma;
@@ -72,6 +110,9 @@ const char* dbf_status_string(dbf_status s) {
       return "DBF_ERR_WORKSPACE: workspace missing or smaller than dbf_workspace_bytes";
     case DBF_ERR_HIP:
       return "DBF_ERR_HIP: the HIP runtime refused a launch";
+    case DBF_ERR_TOO_LARGE:
+      return "DBF_ERR_TOO_LARGE: the call needs a larger workspace than the library's static "
+             "scratch array (DBF_NO_ALLOC_SCRATCH_BYTES); use dbf_forward with a workspace";
     default:
       return "unknown dbf_status";
   }
@@ -151,6 +192,23 @@ dbf_status dbf_forward(const void* x, int64_t ldx, const uint32_t* B1, const uin
   a.path = pick_path(flags, T, R, M, false);
   a.phases = phases_of(flags);
   return hip_status(dbf::launch_forward(a, (hipStream_t)stream));
+}
+
+dbf_status dbf_forward_no_alloc(const void* x, int64_t ldx, const uint32_t* B1,
+                                const uint32_t* B2, const void* alpha, const void* beta,
+                                const void* gamma, int64_t N, int64_t R, int64_t M, int32_t ell,
+                                int64_t T, void* y, int64_t ldy, dbf_dtype y_type,
+                                uint32_t flags, void* stream) {
+  if (N <= 0 || R <= 0 || M <= 0 || ell < 1 || T < 0 || N > DBF_MAX_DIM || R > DBF_MAX_DIM ||
+      M > DBF_MAX_DIM || T > DBF_MAX_DIM)
+    return DBF_ERR_INVALID_ARG;
+  if (T == 0) return DBF_OK;
+  if (dbf::workspace_bytes(N, R, M, ell, T) > DBF_NO_ALLOC_SCRATCH_BYTES) return DBF_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address((hipStream_t)stream, &ws);
+  if (e != hipSuccess) return DBF_ERR_HIP;
+  return dbf_forward(x, ldx, B1, B2, alpha, beta, gamma, N, R, M, ell, T, y, ldy, y_type, flags,
+                     ws, DBF_NO_ALLOC_SCRATCH_BYTES, stream);
 }
 
 dbf_status dbf_forward_multi_adapter(const void* x, int64_t ldx, int64_t T, const int32_t* ids,

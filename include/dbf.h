@@ -21,7 +21,9 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    never allocates or frees memory and keeps no per-call state.
+ *    never allocates or frees memory and keeps no per-call state (the one
+ *    exception, dbf_forward_no_alloc, uses a static device array that is
+ *    part of the loaded library).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    null stream).  Buffers must stay valid until the stream reaches the work.
  *    Calls are re-entrant; concurrent calls must not share a workspace.
@@ -45,6 +47,8 @@ typedef int32_t dbf_status;
 #define DBF_ERR_ALIGNMENT (-2)   /* pointer or stride misaligned            */
 #define DBF_ERR_WORKSPACE (-3)   /* workspace missing or too small          */
 #define DBF_ERR_HIP (-4)         /* the HIP runtime refused a launch        */
+#define DBF_ERR_TOO_LARGE (-5)   /* dbf_forward_no_alloc: the call needs more
+                                    than DBF_NO_ALLOC_SCRATCH_BYTES        */
 
 typedef int32_t dbf_dtype;
 #define DBF_I8 1
@@ -172,6 +176,30 @@ dbf_status dbf_forward(const void* x, int64_t ldx, const uint32_t* B1, const uin
                        int64_t R, int64_t M, int32_t ell, int64_t T, void* y, int64_t ldy,
                        dbf_dtype y_type, uint32_t flags, void* ws, size_t ws_bytes,
                        void* stream);
+
+/*
+ * dbf_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same product, arguments and results as dbf_forward, without ws/ws_bytes.
+ * The workspace is a static device array of DBF_NO_ALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, held from the library's first use on
+ * that GPU until the process ends; its device address is looked up once per
+ * GPU (on the first call there) and no call allocates or frees anything.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams, or different threads without ordering)
+ * race on it and give undefined results; calls ordered on one stream are
+ * safe.  The array keeps the last call's contents; no part of it has to
+ * start at zero.
+ * Errors as for dbf_forward, plus TOO_LARGE when dbf_workspace_bytes for
+ * these sizes exceeds DBF_NO_ALLOC_SCRATCH_BYTES (nothing is launched), and
+ * HIP if the array's address cannot be obtained.
+ */
+#define DBF_NO_ALLOC_SCRATCH_BYTES (((size_t)32) << 20)
+dbf_status dbf_forward_no_alloc(const void* x, int64_t ldx, const uint32_t* B1,
+                                const uint32_t* B2, const void* alpha, const void* beta,
+                                const void* gamma, int64_t N, int64_t R, int64_t M, int32_t ell,
+                                int64_t T, void* y, int64_t ldy, dbf_dtype y_type,
+                                uint32_t flags, void* stream);
 
 /*
  * Batched adapter serving (LoRDBA summary, section 1: many unmerged adapters

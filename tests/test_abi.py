@@ -311,3 +311,40 @@ def test_rank_and_plan_match_the_definition():
         got = dbf.plan_channels(shapes, imps, frac * full)
         want = oracle.prune_channels(shapes, imps, frac * full)
         assert all(np.array_equal(g, w) for g, w in zip(got, want))
+
+
+def _fwd_na(**kw):
+    a = dict(x=A, ldx=64, B1=A, B2=A, alpha=A, beta=A, gamma=A, N=32, R=16, M=64, ell=1, T=4,
+             y=A, ldy=32, y_type=_lib.DBF_F16, flags=0, stream=None)
+    a.update(kw)
+    return L.dbf_forward_no_alloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(ell=0), _lib.DBF_ERR_INVALID_ARG),
+    (dict(T=-1), _lib.DBF_ERR_INVALID_ARG),
+    (dict(M=(1 << 30) + 1), _lib.DBF_ERR_INVALID_ARG),
+    # workspaces beyond the static array are refused before anything else
+    (dict(N=14336, R=6368, M=4096, T=4096, ldx=4096, ldy=14336), _lib.DBF_ERR_TOO_LARGE),
+    (dict(N=4096, R=64, M=4096, ell=2, T=2048, ldx=4096, ldy=4096), _lib.DBF_ERR_TOO_LARGE),
+])
+def test_forward_no_alloc_rejects(kw, want):
+    assert _fwd_na(**kw) == want
+
+
+def test_forward_no_alloc_T0_is_noop():
+    assert _fwd_na(T=0, x=None, y=None) == _lib.DBF_OK
+
+
+def test_no_alloc_limit_matches_header():
+    import re
+    with open(os.path.join(ROOT, "include", "dbf.h")) as f:
+        h = f.read()
+    m = re.search(r"#define DBF_NO_ALLOC_SCRATCH_BYTES \(\(\(size_t\)(\d+)\) << (\d+)\)", h)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NO_ALLOC_SCRATCH_BYTES
+    # the decode and T = 256 shapes of the workloads fit
+    for shape in ((4096, 2048, 4096, 1, 256), (14336, 6368, 4096, 1, 256),
+                  (4096, 6368, 14336, 1, 256), (4096, 64, 4096, 1, 8)):
+        assert L.dbf_workspace_bytes(*shape, ctypes.byref(ctypes.c_size_t())) == 0
+        assert _lib.workspace_bytes(*shape) <= _lib.NO_ALLOC_SCRATCH_BYTES
