@@ -373,7 +373,10 @@ def main():
         G = n_inst
         tab = lambda ts: dbf.pointer_table(ts, dev)  # noqa: E731
         tB1, tB2 = tab(B1s), tab(B2s)
-        ta, tb, tg = tab([pl.alpha] * G), tab([pl.beta] * G), tab([pl.gamma] * G)
+        # every layer instance has its own copy of the scales too, so the
+        # call streams all the bytes it is credited with
+        aS, bS, gS = replicate(pl.alpha, G), replicate(pl.beta, G), replicate(pl.gamma, G)
+        ta, tb, tg = tab(aS), tab(bS), tab(gS)
         xg = x256[:1].repeat(G, 1).contiguous()
         ids = torch.arange(G, dtype=torch.int32, device=dev)
         yg = torch.empty((G, N_), dtype=torch.float16, device=dev)
@@ -385,14 +388,20 @@ def main():
 
         callg(0)
         torch.cuda.synchronize()
-        errg = oracle.max_norm_error(yg[:1].float().cpu().numpy(), yref[:1])
+        yg_h = yg.float().cpu().numpy()
+        errg = oracle.max_norm_error(yg_h[:1], yref[:1])
+        # the G instances are copies of one layer on copies of one token, so
+        # every row must be the same, bit for bit
+        rows_equal = bool((yg_h == yg_h[:1]).all())
+        errg_all = oracle.max_norm_error(yg_h, np.repeat(yref[:1], G, axis=0))
         ng = max(args.steps // 10, 10)
         tg_ = time_calls(callg, ng, 3) / ng
         bg = G * alg_bytes(N_, R_, M_, 1, 1, ids=True)
         out["grouped_decode_256_layers"] = {
             "layers": G, "T_per_layer": 1, "us_per_call": tg_ * 1e6, "tokens_per_s": G / tg_,
             "effective_GBs": bg / tg_ / 1e9, "hbm_frac": bg / tg_ / 1e9 / HBM_PEAK_GBS,
-            "alg_bytes_per_call": bg, "parity_err_token0": errg,
+            "alg_bytes_per_call": bg, "parity_err_token0": errg, "parity_err_all_rows": errg_all,
+            "rows_bit_identical": rows_equal,
         }
         log(f"grouped decode: {tg_ * 1e6:.1f} us/call, {bg / tg_ / 1e9:.1f} GB/s")
 
