@@ -53,8 +53,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3  # published dense fp32 (matrix core; also the packed vector rate)
 N_, R_, M_ = 4096, 2048, 4096
-GEMM_SRC = os.path.join(ROOT, "double_binary_rank_amd", "csrc", "dbf_gemm.hip")
-TRAFFIC_MD = os.path.join(ROOT, "profiles", "k_gemm_traffic_attn4096_R2048_T256.md")
+GEMM_SRC = os.path.join(ROOT, "double_binary_rank_amd", "csrc", "dbf_tile.hip")
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "k_tile_traffic_attn4096_R2048_T256.md")
 COPY_MIB = 256
 
 
@@ -183,7 +183,7 @@ def summarize_pmc(fetch_dir, write_dir):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = ("stage1" if "k_gemm<1" in name else "stage2" if "k_gemm<2" in name
+            key = ("stage1" if "k_tile<1" in name else "stage2" if "k_tile<2" in name
                    else "prep" if "k_prep_v" in name
                    else "copy" if "copy" in name.lower() or "elementwise" in name else None)
             if key:
@@ -330,8 +330,7 @@ def main():
         ach = f_st[dom] / t_ph[dom] / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": committed_traffic(dom[-1]),
-                "kernel": {"stage1": "k_gemm<1, 2, true, false, true, 8>",
-                           "stage2": "k_gemm<2, 2, true, false, false, 4>"}[dom]
+                "kernel": {"stage1": "k_tile<1, ...>", "stage2": "k_tile<2, ...>"}[dom]
                           + f" ({dom} of the T=256 call)",
                 "launch_us": t_ph[dom] * 1e6, "alg_flops_per_launch": f_st[dom],
                 "phase_launch_us": {k: v * 1e6 for k, v in t_ph.items()}}

@@ -874,6 +874,13 @@ hipError_t launch_sign_product(const uint32_t* S, int64_t rows, int64_t K, int32
 }
 
 hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
+  // one adapter: the shared-token-tile stages (dbf_tile.hip); grouped
+  // layers then run one by one through the same stages, so each layer's
+  // result is that of dbf_forward on it
+  if (!a.multi && tile_path_fits(a)) {
+    if (a.group > 1) return hipErrorNotSupported;
+    return launch_tile_forward(a, s);
+  }
   const WsLayout L = ws_layout(a.N, a.R, a.M, a.ell, a.T);
   char* ws = (char*)a.ws;
   GemmParams p{};

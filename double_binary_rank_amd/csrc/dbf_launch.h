@@ -115,6 +115,10 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s);
 // column blocks hold at most kGemmChunk tokens of one adapter
 constexpr int kGemmChunk = 32;
 hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s);
+// large-T path of one adapter (not grouped): token tiles shared through LDS;
+// z as fp16 rows [ell][T][ldz_of(R)] in the workspace's z region
+hipError_t launch_tile_forward(const ForwardArgs& a, hipStream_t s);
+bool tile_path_fits(const ForwardArgs& a);
 // Token-major fp16 operand tiles (the large-T layout above) of
 // scale_i[k] * src[t][k] for each of ell terms (src fp16 [T][ld], shared).
 hipError_t launch_tiles_f16(const half_t* src, int64_t ld, int64_t T, int64_t K, int32_t ell,
