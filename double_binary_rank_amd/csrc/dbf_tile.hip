@@ -13,12 +13,12 @@
 // runs KS*W waves: wave (wq, kp) computes quad wq of the workgroup over the
 // 128-blocks kb = KS*j + kp of the reduction.  Per iteration j the
 // workgroup stages the token operand of its KS blocks (16*NC token rows x
-// 256 bytes each) from global memory into LDS once, and every wave of the
-// same K-part reads it as its MFMA B operand, so each staged byte feeds W
-// row quads.  The signs go straight to registers: one 16-byte load per lane
-// brings the four row tiles' words of one (quad, block) unit.  Stage 1
-// multiplies x by gamma_i while staging (one fp16 rounding of the exact
-// product, as the separate prep kernel of the multi-adapter path does).
+// 256 bytes each), every wave's sign words and (stage 1) gamma from global
+// memory straight into LDS with global_load_lds, and every wave of the
+// same K-part reads the token tile as its MFMA B operand, so each staged
+// byte feeds W row quads.  Stage 1 multiplies the staged x by gamma_i
+// before the MFMA (one fp16 rounding of the exact product, as the separate
+// prep kernel of the multi-adapter path does).
 //
 // Sign expansion: for step s of a block, ((w << (3-s)) & 0x88888888) |
 // 0x22222222 holds the lane's 8 signs of that step as e2m1 +-1.0 (the
@@ -26,11 +26,11 @@
 // v_cvt_scalef32_pk_f16_fp4 turn its bytes into the four f16 pairs of the A
 // operand: 6 VALU ops per 16x32 operand, each feeding NC MFMAs.
 //
-// The operand tiles in LDS are double-buffered (one barrier per
-// iteration): the next iteration's chunks are loaded into registers while
-// the current one is multiplied, and written to the other buffer after it.
-// The K-parts' partial tiles are summed in a fixed order through LDS at the
-// end, so results do not depend on timing.
+// The LDS holds NBUF pipeline buffers with NBUF-1 iterations' requests in
+// flight and one barrier per iteration; each wave spreads its requests for
+// a later iteration over the steps of the current one.  The K-parts'
+// partial tiles are summed in a fixed order through LDS at the end, so
+// results do not depend on timing.
 #include <climits>
 
 #include "dbf_device.h"
@@ -126,6 +126,22 @@ __device__ inline void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt with vmcnt <= n and lgkmcnt = 0 (every LDS read returned).
+template <int n>
+__device__ inline void wait_vm_lds() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1 in order.
+template <int B, int E, class F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <int STAGE, int NC, int W, int KS, int NBUF>
 struct TileShape {
   static constexpr int NWV = W * KS;                 // waves
@@ -136,9 +152,11 @@ struct TileShape {
   static constexpr int SGN = NWV * 1024;             // every wave's sign words
   static constexpr int GAM = STAGE == 1 ? KS * 256 : 0;  // gamma of each K-part's block
   static constexpr int BUF = KS * TILE + SGN + GAM;  // one pipeline buffer
-  // requests per wave per iteration (the gamma block is one more for the
-  // waves of quad 0 of the workgroup; the others wait as if they had it)
+  // requests per wave per iteration: JB token blocks and the sign words,
+  // plus (stage 1) the gamma block for the waves of quad 0 of the
+  // workgroup
   static constexpr int GROUP = JB + 1 + (STAGE == 1 ? 1 : 0);
+  static constexpr int GROUP_NQ0 = JB + 1;
   static constexpr int TPW = 4 * NC / KS;            // output tiles each wave finishes
   static constexpr int RED = KS * W * 4 * NC * 64 * 16;  // every wave's partial tiles
   static constexpr int BYTES = NBUF * BUF > RED ? NBUF * BUF : RED;
@@ -216,40 +234,46 @@ __global__ __launch_bounds__(64 * W * KS) void k_tile(TileParams p) {
     const int srow_s = q * 64 + lane;
     const half_t sclh = p.scl[(int64_t)i * p.rows + (srow_s < p.rows ? srow_s : p.rows - 1)];
 
-    // Requests of iteration it into pipeline buffer bf: this wave's token
-    // blocks, its sign words and (stage 1, by the waves of quad 0) its
-    // K-part's 128 entries of gamma.  Iterations past the last repeat the
-    // last one's addresses.
-    auto issue = [&](int it, int bf) {
+    // Request j of iteration it into pipeline buffer bf: this wave's token
+    // blocks (j < JB), its sign words (j = JB) and (stage 1, by the waves
+    // of quad 0) its K-part's 128 entries of gamma (j = JB + 1).
+    // Iterations past the last repeat the last one's addresses.
+    auto issue_part = [&](int it, int bf, auto jc) {
+      constexpr int j = decltype(jc)::value;
       it = it < last ? it : last;
       const uint32_t lb = lds0 + bf * Sh::BUF;
-      if (it < nwhole) {
-#pragma unroll
-        for (int j = 0; j < Sh::JB; ++j)
-          dma16(bterm, roff[j] + (uint32_t)(it * KS + rkp[j]) * 256u,
-                lb + (wv + j * Sh::NWV) * 1024);
-      } else {
-#pragma unroll
-        for (int j = 0; j < Sh::JB; ++j) {
+      if constexpr (j < Sh::JB) {
+        const int blk = wv + j * Sh::NWV;
+        if (it < nwhole) {
+          dma16(bterm, roff[j] + (uint32_t)(it * KS + rkp[j]) * 256u, lb + blk * 1024);
+        } else {
           // chunk column of this lane and its first entry, clamped
-          const int blk = wv + j * Sh::NWV;
           const int row = (blk % (Sh::ROWS / 4)) * 4 + (lane >> 4);
           const int c = (lane & 15) ^ (row & 15);
           int k = (it * KS + rkp[j]) * kColBlock + 8 * c;
           k = k < kmax ? k : kmax;
           dma16(bterm, roff[j] - (uint32_t)(c * 16) + (uint32_t)k * 2u, lb + blk * 1024);
         }
-      }
-      int kb = it * KS + kp;
-      kb = kb < nkb ? kb : nkb - 1;
-      dma16(sq, (uint32_t)((kb << 10) + lane * 16), lb + KS * Sh::TILE + wv * 1024);
-      if constexpr (STAGE == 1) {
+      } else if constexpr (j == Sh::JB) {
+        int kb = it * KS + kp;
+        kb = kb < nkb ? kb : nkb - 1;
+        dma16(sq, (uint32_t)((kb << 10) + lane * 16), lb + KS * Sh::TILE + wv * 1024);
+      } else if constexpr (STAGE == 1) {
         if (wq == 0) {  // lane L: entries 2L, 2L+1 of K-part kp's block
           int k = (it * KS + kp) * kColBlock + 2 * lane;
           k = k < K - 2 ? k : K - 2;
           dma4(gami, (uint32_t)k * 2u, lb + KS * Sh::TILE + Sh::SGN + kp * 256);
         }
       }
+    };
+    // the requests j of iteration it with first <= j < last (in order)
+    auto issue_range = [&](int it, int bf, auto firstc, auto lastc) {
+      static_for<decltype(firstc)::value, decltype(lastc)::value>(
+          [&](auto jc) { issue_part(it, bf, jc); });
+    };
+    auto issue = [&](int it, int bf) {
+      issue_range(it, bf, std::integral_constant<int, 0>{},
+                  std::integral_constant<int, Sh::GROUP>{});
     };
 
     v4f acc[4][NC];
@@ -258,40 +282,60 @@ __global__ __launch_bounds__(64 * W * KS) void k_tile(TileParams p) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[h][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // the MFMAs of iteration it from pipeline buffer bf; PART: the block
-    // is the reduction's partial last one (entries past K are zeroed).
-    // Every LDS read of the iteration is issued first, so the expansion of
-    // the signs (ALU) and the MFMAs overlap their latency.
-    auto compute = [&](int it, int bf, auto part_c) {
-      constexpr bool PART = decltype(part_c)::value;
-      const int kb = it * KS + kp;
+    // One step's token operands (each token tile's v8h) and, in stage 1,
+    // its gamma entries, read from pipeline buffer bf.
+    struct StepOps {
+      v8h bv[NC];
+      v8h gv;
+    };
+    auto load_step = [&](int bf, int s, StepOps& o) {
       const char* bb = lds + bf * Sh::BUF;
       const char* bl = bb + kp * Sh::TILE;
-      const v4u w = *(const v4u*)(bb + KS * Sh::TILE + wv * 1024 + lane * 16);
-      v8h bv[4][NC];
-      v8h gv[STAGE == 1 ? 4 : 1];
+      if constexpr (STAGE == 1)
+        o.gv = *(const v8h*)(bb + KS * Sh::TILE + Sh::SGN + kp * 256 + (4 * s + g) * 16);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if constexpr (STAGE == 1)
-          gv[s] = *(const v8h*)(bb + KS * Sh::TILE + Sh::SGN + kp * 256 + (4 * s + g) * 16);
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          bv[s][c] = *(const v8h*)(bl + (16 * c + c16) * 256 + (((4 * s + g) ^ c16) << 4));
-      }
-      // keep the reads ahead of the arithmetic (the scheduler would sink
-      // each next to its use)
-      __builtin_amdgcn_sched_barrier(0);
-      const int kvalid = K - kb * kColBlock;
+      for (int c = 0; c < NC; ++c)
+        o.bv[c] = *(const v8h*)(bl + (16 * c + c16) * 256 + (((4 * s + g) ^ c16) << 4));
+    };
+    // Which of the requests of the next group a step issues: with three or
+    // more buffers a quarter per step (issued together right after the
+    // barrier, the workgroup's requests queue at the texture unit and hold
+    // up every wave's MFMAs); with two, all at the first step (the group is
+    // waited for at the next iteration).
+    auto req_lo = [](int s) { return NBUF > 2 ? s * Sh::GROUP / 4 : (s == 0 ? 0 : Sh::GROUP); };
+
+    // Iteration it: the MFMAs of its KS blocks from buffer it % NBUF.  Each
+    // step reads the next step's operands ahead of its own MFMAs and then
+    // issues its share of the requests of iteration it + NBUF - 1 into
+    // buffer (it - 1) % NBUF, which every wave finished reading in
+    // iteration it - 1.  PART: a block of it may be the reduction's partial
+    // last one or lie past it (its entries from K on contribute zero).
+    auto body = [&](int it, auto part_c) {
+      constexpr bool PART = decltype(part_c)::value;
+      // this wave's requests of it done (requests complete in issue order;
+      // the bound is exact per wave), then every wave's
+      if (wq == 0)
+        wait_vm_lds<(NBUF - 2) * Sh::GROUP>();
+      else
+        wait_vm_lds<(NBUF - 2) * Sh::GROUP_NQ0>();
+      __syncthreads();
+      const int bf = it % NBUF, rbf = (it + NBUF - 1) % NBUF;
+      const v4u w = *(const v4u*)(lds + bf * Sh::BUF + KS * Sh::TILE + wv * 1024 + lane * 16);
+      const int kvalid = K - (it * KS + kp) * kColBlock;
+      StepOps ops[2];
+      load_step(bf, 0, ops[0]);
       auto step = [&](auto scst) {
         constexpr int s = decltype(scst)::value;
+        if constexpr (s < 3) load_step(bf, s + 1, ops[(s + 1) & 1]);
+        const StepOps& o = ops[s & 1];
         v8h a[4];
 #pragma unroll
         for (int h = 0; h < 4; ++h) a[h] = expand_cvt<s>(w[h], p.nib_mask, p.nib_one);
         const bool live = !PART || 32 * s + 8 * g < kvalid;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          v8h b = bv[s][c];
-          if constexpr (STAGE == 1) b = b * gv[s];
+          v8h b = o.bv[c];
+          if constexpr (STAGE == 1) b = b * o.gv;
           if constexpr (PART) {
             if (!live) b = v8h{};
           }
@@ -299,6 +343,11 @@ __global__ __launch_bounds__(64 * W * KS) void k_tile(TileParams p) {
           for (int h = 0; h < 4; ++h)
             acc[h][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[h], b, acc[h][c], 0, 0, 0);
         }
+        static_for<req_lo(s), req_lo(s + 1)>(
+            [&](auto jc) { issue_part(it + NBUF - 1, rbf, jc); });
+        // keep each step's reads, MFMAs and requests together (the
+        // scheduler would sink every read next to its use)
+        __builtin_amdgcn_sched_barrier(0);
       };
       step(std::integral_constant<int, 0>{});
       step(std::integral_constant<int, 1>{});
@@ -306,33 +355,20 @@ __global__ __launch_bounds__(64 * W * KS) void k_tile(TileParams p) {
       step(std::integral_constant<int, 3>{});
     };
 
-    // Pipeline: NBUF-1 iterations' requests in flight.  Before iteration
-    // it, each wave waits for its own requests of it, and the barrier makes
-    // every wave's visible and ends the reads of the buffer iteration
-    // it-1 used, which then receives the requests of it + NBUF - 1.
+    // Pipeline over NBUF buffers with the requests of NBUF - 1 iterations
+    // in flight.
     if (i > 0) __syncthreads();  // the previous term's readers of lds are done
 #pragma unroll
     for (int d = 0; d < NBUF - 1; ++d) issue(d, d);
     // The loop holds no branch around the MFMAs (a branch there makes the
     // compiler copy the accumulators every iteration): iterations whose KS
     // blocks are all present and whole run first; the last one, when its
-    // blocks are partial or missing, runs masked (entries past K and blocks
-    // past the last contribute zero).  Waves of a quad past the last one
-    // compute on quad 0's signs and store nothing.
+    // blocks are partial or missing, runs masked.  Waves of a quad past the
+    // last one compute on quad 0's signs and store nothing.
     const int nmain = K % kColBlock == 0 ? nkb / KS : (nkb - 1) / KS;
     int it = 0;
-    for (; it < nmain; ++it) {
-      wait_vm<(NBUF - 2) * Sh::GROUP>();
-      __syncthreads();
-      issue(it + NBUF - 1, (it + NBUF - 1) % NBUF);
-      compute(it, it % NBUF, std::false_type{});
-    }
-    for (; it < niter; ++it) {
-      wait_vm<(NBUF - 2) * Sh::GROUP>();
-      __syncthreads();
-      issue(it + NBUF - 1, (it + NBUF - 1) % NBUF);
-      compute(it, it % NBUF, std::true_type{});
-    }
+    for (; it < nmain; ++it) body(it, std::false_type{});
+    if (it < niter) body(it, std::true_type{});
     wait_vm<0>();
     __syncthreads();
 
