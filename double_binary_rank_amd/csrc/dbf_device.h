@@ -19,6 +19,81 @@ __device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return r;
 }
 
+// A operand of v_mfma_f32_16x16x32_f16 for step s of a 128-block (k = 32s +
+// 8g + e, e = 0..7, lane group g) from a lane's packed word w: ((w << (3-s))
+// & 0x88888888) | 0x22222222 holds the 8 signs of the step as e2m1 +-1.0
+// (slot 8s+e sits at bit 4e+s), and four v_cvt_scalef32_pk_f16_fp4 turn its
+// bytes into f16 pairs.  msk = 0x88888888 and one = 0x22222222 are passed in
+// registers.
+template <int s>
+__device__ inline v8h expand_cvt(uint32_t w, uint32_t msk, uint32_t one) {
+  const uint32_t n = and_or(w << (3 - s), msk, one);
+  const v2h r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n, 1.0f, 0);
+  const v2h r1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n, 1.0f, 1);
+  const v2h r2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n, 1.0f, 2);
+  const v2h r3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n, 1.0f, 3);
+  return v8h{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// Issues one 16-byte-per-lane direct-to-LDS load: lane L's 16 bytes at
+// base + voff go to LDS byte address lds + 16*L.  Written as inline asm so
+// that the compiler does not order every later LDS read after it (it cannot
+// tell which LDS bytes the load writes); the kernel waits for these loads
+// itself with s_waitcnt on vmcnt before the barrier that publishes them.
+// M0 (the LDS address operand) is saved and restored around the load.
+__device__ inline void dma16(const void* base_, uint32_t voff, uint32_t lds_) {
+  // base and lds are wave-uniform: pin them to scalar registers
+  const uint64_t bu = (uint64_t)(uintptr_t)base_;
+  // (readfirstlane returns a signed int: widen each half as unsigned)
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bu >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bu);
+  const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_);
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory");
+}
+
+// As dma16 with 4 bytes per lane (lane L's 4 bytes go to lds + 4*L).
+__device__ inline void dma4(const void* base_, uint32_t voff, uint32_t lds_) {
+  const uint64_t bu = (uint64_t)(uintptr_t)base_;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bu >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bu);
+  const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_);
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory");
+}
+
+// s_waitcnt with vmcnt <= n only (expcnt and lgkmcnt at their maximum).
+template <int n>
+__device__ inline void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt with vmcnt <= n and lgkmcnt = 0 (every LDS read returned).
+template <int n>
+__device__ inline void wait_vm_lds() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+}
+
 __device__ inline void store4(void* y, int64_t ldy, bool f32, int64_t t, int64_t r, int64_t rows,
                               const float v[4]) {
   if (f32) {

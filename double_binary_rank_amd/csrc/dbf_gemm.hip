@@ -874,6 +874,8 @@ hipError_t launch_sign_product(const uint32_t* S, int64_t rows, int64_t K, int32
 }
 
 hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s) {
+  // several adapters of short rank: token tiles served adapter by adapter
+  if (ma_short_fits(a)) return launch_ma_short(a, s);
   // one adapter: the shared-token-tile stages (dbf_tile.hip); grouped
   // layers then run one by one through the same stages, so each layer's
   // result is that of dbf_forward on it

@@ -231,4 +231,10 @@ struct FactorLayout {
 FactorLayout factor_layout(int64_t N, int64_t M, int64_t k);
 hipError_t launch_factorize(const FactorArgs& a, hipStream_t s);
 
+// large-T path of several adapters with R <= 64 and at most two terms: one
+// launch per stage over 16-token tiles, z fp16 [ell][T][ldz_of(R)] in the
+// workspace's z region, no prep phase
+bool ma_short_fits(const ForwardArgs& a);
+hipError_t launch_ma_short(const ForwardArgs& a, hipStream_t s);
+
 }  // namespace dbf

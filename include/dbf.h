@@ -76,7 +76,10 @@ typedef int32_t dbf_dtype;
      DBF_RUN_STAGE2  y from z (the only phase that writes y)
    On the large-T path each phase is at most one kernel launch; with one
    adapter, a short reduction over M (a multiple of 8) and gamma 16-byte
-   aligned, stage 1 reads x itself and DBF_RUN_PREP launches nothing. */
+   aligned, stage 1 reads x itself and DBF_RUN_PREP launches nothing.  With
+   several adapters of rank R <= 64 and at most two terms (M a multiple of
+   8, x and y rows 16-byte aligned), stage 1 reads x itself as well and
+   DBF_RUN_PREP writes only the token runs. */
 #define DBF_RUN_PREP 8u
 #define DBF_RUN_STAGE1 16u
 #define DBF_RUN_STAGE2 32u

@@ -418,6 +418,41 @@ def test_multi_adapter_many_adapters(path):
                           _multi_ref(B, ids).astype(np.float32).astype(np.float64))
 
 
+@pytest.mark.parametrize("shape", [(70, 20, 4104, 1, 40), (200, 64, 264, 2, 77),
+                                   (64, 33, 8, 2, 16)])
+def test_multi_short_rank_kernel(shape):
+    """The one-launch kernel of several short-rank adapters (R <= 64, at most
+    two terms) on the large-T path: N not a multiple of 4 or of 64, one or
+    two MFMA steps of rank, a reduction of two chunks ending in a partial
+    block, a partial last token tile, unsorted ids with out-of-range ones;
+    exact on integers (fp32 output, also accumulating onto a base) and
+    within the bar on fp16 data."""
+    N, R, M, ell, T = shape
+    B = synth.make_multi_adapter(num_adapters=6, N=N, R=R, M=M, ell=ell, T=T, seed=61,
+                                 alpha="ones", beta="ones", gamma="ones", x_kind="int3",
+                                 sort=False)
+    ids = B.ids.copy()
+    ids[[1, T - 1]] = [-1, 6]
+    D = H().DeviceAdapters(B.adapters)
+    x, idd = H().to_dev_rows(B.x), H().to_dev(ids)
+    y = D.forward(x, idd, path="mfma", y=H().empty_rows(T, N, torch.float32))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64),
+                          _multi_ref(B, ids).astype(np.float32).astype(np.float64))
+    base = np.random.default_rng(3).integers(-9, 9, size=(T, N)).astype(np.float32)
+    y2 = D.forward(x, idd, path="mfma", y=H().to_dev_rows(base), accumulate=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.cpu().numpy().astype(np.float64),
+                          _multi_ref(B, ids, y_old=base).astype(np.float32).astype(np.float64))
+    Bf = synth.make_multi_adapter(num_adapters=6, N=N, R=R, M=M, ell=ell, T=T, seed=62)
+    Df = H().DeviceAdapters(Bf.adapters)
+    yf = Df.forward(H().to_dev_rows(Bf.x), H().to_dev(Bf.ids), path="mfma",
+                    y=H().empty_rows(T, N, torch.float16))
+    torch.cuda.synchronize()
+    err = oracle.max_norm_error(yf.float().cpu().numpy(), _multi_ref(Bf, Bf.ids))
+    assert err <= TOL, err
+
+
 def test_multi_adapter_permutation_invariance():
     B = synth.make_multi_adapter(num_adapters=8, N=256, R=64, M=256, ell=2, T=300, seed=33)
     D = H().DeviceAdapters(B.adapters)
@@ -581,8 +616,9 @@ def _ref_blocks(ids, n_adapters, chunk):
     return out
 
 
-@pytest.mark.parametrize("path,ell,chunk", [("gemv", 1, 5), ("gemv", 2, 2), ("mfma", 2, 32)])
-def test_segmentation_blocks(path, ell, chunk):
+@pytest.mark.parametrize("path,ell,chunk,R", [("gemv", 1, 5, 32), ("gemv", 2, 2, 32),
+                                               ("mfma", 2, 32, 80), ("mfma", 2, 16, 32)])
+def test_segmentation_blocks(path, ell, chunk, R):
     """The column-block list the prep launch writes into the workspace (its
     header and list sit at the library's internal offsets 0 and 256) equals
     the list by definition: runs of 1..70 tokens over several 256-id passes,
@@ -594,10 +630,11 @@ def test_segmentation_blocks(path, ell, chunk):
     ids = np.concatenate(parts)[:1000]
     ids[300:340] = 4  # a run across the first pass boundary
     ids[511:513] = -1
-    B = synth.make_multi_adapter(num_adapters=A, N=64, R=32, M=128, ell=ell, T=len(ids), seed=92)
+    # (on the large-T path, ranks up to 64 cut runs every 16 tokens)
+    B = synth.make_multi_adapter(num_adapters=A, N=64, R=R, M=128, ell=ell, T=len(ids), seed=92)
     D = H().DeviceAdapters(B.adapters)
     T = len(ids)
-    ws = torch.full((dbf_ws(64, 32, 128, ell, T),), 0xAB, dtype=torch.uint8, device="cuda")
+    ws = torch.full((dbf_ws(64, R, 128, ell, T),), 0xAB, dtype=torch.uint8, device="cuda")
     D.forward(H().to_dev(B.x), H().to_dev(ids), path=path, ws=ws, phases="prep")
     torch.cuda.synchronize()
     want = _ref_blocks(ids, A, chunk)
