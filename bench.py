@@ -54,7 +54,13 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3  # published dense fp32 (matrix core; also the packed vector rate)
 N_, R_, M_ = 4096, 2048, 4096
 GEMM_SRC = os.path.join(ROOT, "double_binary_rank_amd", "csrc", "dbf_tile.hip")
+GEMV_SRC = os.path.join(ROOT, "double_binary_rank_amd", "csrc", "dbf_gemv.hip")
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "k_tile_traffic_attn4096_R2048_T256.md")
+# kernel-trace summaries the roofline objects take their launch durations from
+PREFILL_TRACE_MD = os.path.join(ROOT, "profiles", "k_tile_prefill_attn4096_R2048_T256.md")
+DECODE_TRACE_MD = os.path.join(ROOT, "profiles", "k_gemv_fused_grouped_decode_256x_attn4096_R2048.md")
+DECODE_TRAFFIC_MD = os.path.join(ROOT, "profiles",
+                                 "k_gemv_fused_traffic_grouped_decode_256x_attn4096_R2048.md")
 COPY_MIB = 256
 
 
@@ -151,6 +157,32 @@ def file_sha256(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def committed_json(path, tag, src):
+    """The `tag:` JSON line of a committed profile summary, or None when the
+    file is absent or was taken on kernel source other than `src`."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith(tag + ":"):
+                    d = json.loads(line.split(":", 1)[1])
+                    return d if d.get("source_sha256") == file_sha256(src) else None
+    except (OSError, ValueError):
+        return None
+    return None
+
+
+def committed_mean_us(path, kernel, src):
+    """Mean launch duration (us) of the kernel whose name starts with
+    `kernel` in a committed kernel-trace summary of the current source."""
+    d = committed_json(path, "trace_json", src)
+    if not d:
+        return None
+    for k, v in d.get("mean_us", {}).items():
+        if k.startswith(kernel):
+            return v
+    return None
+
+
 def committed_traffic(stage):
     """HBM bytes per launch of the stage kernel from the committed counter
     summary, or None when absent or taken on different kernel source."""
@@ -207,6 +239,46 @@ def summarize_pmc(fetch_dir, write_dir):
             "fetch_factor": f_fac, "write_factor": w_fac, "stages": stages}
 
 
+def trace_means(trace_dir):
+    """Mean duration (us) per kernel name in a rocprofv3 --kernel-trace run
+    (names shortened to the template, without the argument list)."""
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    per = {}
+    for r in rows:
+        name = r["Kernel_Name"].replace("dbf::(anonymous namespace)::", "").replace("void ", "")
+        name = name.replace("dbf::", "").split("(")[0].strip()
+        per.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {k: float(np.mean(v)) for k, v in per.items()}
+
+
+def summarize_pmc_kernel(fetch_dir, write_dir, kernel, src):
+    """FETCH_SIZE / WRITE_SIZE per launch of the kernel whose name contains
+    `kernel`, scaled like summarize_pmc by the calibration copy, tagged with
+    the kernel source's sha256."""
+    def per(d, counter):
+        k_v, c_v = [], []
+        for r in _pmc_rows(d):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            if kernel in name:
+                k_v.append(float(r["Counter_Value"]))
+            elif "copy" in name.lower() or "elementwise" in name:
+                c_v.append(float(r["Counter_Value"]))
+        return sum(k_v) / len(k_v), max(c_v)
+    fk, fc = per(fetch_dir, "FETCH_SIZE")
+    wk, wc = per(write_dir, "WRITE_SIZE")
+    copy_kib = COPY_MIB * 1024.0
+    ff, wf = copy_kib / fc, copy_kib / wc
+    return {"kernel": kernel, "source": os.path.relpath(src, ROOT), "source_sha256": file_sha256(src),
+            "copy_mib": COPY_MIB, "fetch_kib_raw": fk, "write_kib_raw": wk,
+            "copy_fetch_kib_raw": fc, "copy_write_kib_raw": wc, "fetch_factor": ff,
+            "write_factor": wf, "fetch_bytes": fk * 1024 * ff, "write_bytes": wk * 1024 * wf,
+            "bytes_per_launch": fk * 1024 * ff + wk * 1024 * wf}
+
+
 def summarize_trace(trace_dir, top=12):
     """Markdown table of kernel durations from a rocprofv3 --kernel-trace
     run: calls, mean, p10, median, p90, min, max and share of the summed
@@ -240,14 +312,29 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run a {COPY_MIB} MiB device copy (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-kernel", metavar="NAME",
+                    help="with --summarize-pmc: summarise this kernel (name substring) alone")
+    ap.add_argument("--pmc-source", metavar="SRC", help="with --pmc-kernel: its source file")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print a kernel duration table from a rocprofv3 --kernel-trace run")
+    ap.add_argument("--trace-source", metavar="SRC",
+                    help="with --summarize-trace: also print a trace_json line of mean "
+                         "durations tagged with this kernel source file's sha256")
     args = ap.parse_args()
     if args.summarize_pmc:
-        print("traffic_json: " + json.dumps(summarize_pmc(*args.summarize_pmc)))
+        if args.pmc_kernel:
+            print("traffic_json: " + json.dumps(summarize_pmc_kernel(
+                *args.summarize_pmc, args.pmc_kernel, args.pmc_source)))
+        else:
+            print("traffic_json: " + json.dumps(summarize_pmc(*args.summarize_pmc)))
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        if args.trace_source:
+            print("\ntrace_json: " + json.dumps({
+                "source": os.path.relpath(args.trace_source, ROOT),
+                "source_sha256": file_sha256(args.trace_source),
+                "mean_us": trace_means(args.summarize_trace)}))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -294,6 +381,7 @@ def main():
     byts = alg_bytes(N_, R_, M_, 1, T)
     t_call = value = achieved_tflops = float("nan")
     roof = None
+    decode_roof = None
     if want("prefill"):
         sec = time_calls(call256, args.steps, args.warmup)
         t_call = sec / args.steps
@@ -327,12 +415,17 @@ def main():
             t_ph[ph] = time_graph(phase_call(ph), 64, max(args.steps // 16, 4), 2)
         f_st = {"stage1": 2 * T * R_ * M_, "stage2": 2 * T * N_ * R_}
         dom = max(f_st, key=lambda k: t_ph[k])
-        ach = f_st[dom] / t_ph[dom] / 1e12
+        kname = {"stage1": "k_tile<1", "stage2": "k_tile<2"}[dom]
+        # the launch duration: the committed rocprof mean of this kernel when
+        # it was taken on the current source, else the live graph replay
+        prof_us = committed_mean_us(PREFILL_TRACE_MD, kname, GEMM_SRC)
+        dur_us = prof_us if prof_us is not None else t_ph[dom] * 1e6
+        ach = f_st[dom] / (dur_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": committed_traffic(dom[-1]),
-                "kernel": {"stage1": "k_tile<1, ...>", "stage2": "k_tile<2, ...>"}[dom]
-                          + f" ({dom} of the T=256 call)",
-                "launch_us": t_ph[dom] * 1e6, "alg_flops_per_launch": f_st[dom],
+                "kernel": kname + ", ...> (" + dom + " of the T=256 call)",
+                "launch_us": dur_us, "launch_us_source": "rocprof" if prof_us is not None else "live",
+                "launch_us_live": t_ph[dom] * 1e6, "alg_flops_per_launch": f_st[dom],
                 "phase_launch_us": {k: v * 1e6 for k, v in t_ph.items()}}
         log("phase launches: " + ", ".join(f"{k} {v * 1e6:.2f} us" for k, v in t_ph.items())
             + f"; dominant {dom}: {ach:.1f} TFLOP/s")
@@ -395,14 +488,28 @@ def main():
         errg_all = oracle.max_norm_error(yg_h, np.repeat(yref[:1], G, axis=0))
         ng = max(args.steps // 10, 10)
         tg_ = time_calls(callg, ng, 3) / ng
+        tgg = time_graph(callg, 8, max(args.steps // 40, 3), 2)
         bg = G * alg_bytes(N_, R_, M_, 1, 1, ids=True)
         out["grouped_decode_256_layers"] = {
             "layers": G, "T_per_layer": 1, "us_per_call": tg_ * 1e6, "tokens_per_s": G / tg_,
             "effective_GBs": bg / tg_ / 1e9, "hbm_frac": bg / tg_ / 1e9 / HBM_PEAK_GBS,
+            "us_per_call_graph": tgg * 1e6, "hbm_frac_graph": bg / tgg / 1e9 / HBM_PEAK_GBS,
             "alg_bytes_per_call": bg, "parity_err_token0": errg, "parity_err_all_rows": errg_all,
             "rows_bit_identical": rows_equal,
         }
-        log(f"grouped decode: {tg_ * 1e6:.1f} us/call, {bg / tg_ / 1e9:.1f} GB/s")
+        log(f"grouped decode: {tg_ * 1e6:.1f} us/call, {bg / tg_ / 1e9:.1f} GB/s; graph replay "
+            f"{tgg * 1e6:.1f} us/call, {bg / tgg / 1e9:.1f} GB/s")
+        # the decode-side roofline: the one k_gemv_fused launch of the call
+        prof_us = committed_mean_us(DECODE_TRACE_MD, "k_gemv_fused", GEMV_SRC)
+        dur_us = prof_us if prof_us is not None else tgg * 1e6
+        tr = committed_json(DECODE_TRAFFIC_MD, "traffic_json", GEMV_SRC)
+        decode_roof = {"bound": "hbm", "achieved": bg / (dur_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                       "unit": "GB/s", "frac": bg / (dur_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                       "traffic": tr["bytes_per_launch"] if tr else None,
+                       "kernel": "k_gemv_fused (256 one-token layers, one launch per call)",
+                       "launch_us": dur_us,
+                       "launch_us_source": "rocprof" if prof_us is not None else "live",
+                       "launch_us_live": tgg * 1e6, "alg_bytes_per_launch": bg}
 
     # ------------------------------------------ multi-adapter batch cfg5 --
     if want("multi"):
@@ -827,6 +934,7 @@ def main():
         "parity_err": err256,
         "achieved_TFLOPs_per_call": achieved_tflops,
         "roofline": roof,
+        "decode_roofline": decode_roof,
         "cpu_baseline": cpu,
         "cpu_context": cpu_ctx,
         "cases": out,

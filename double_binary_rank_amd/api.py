@@ -2,7 +2,9 @@
 
 Argument marshalling only: tensors supply device pointers, strides and the
 current HIP stream; every step of the product runs in the HIP library.
-Function names follow the C entry points.
+Function names follow the C entry points.  The offline planning of middle
+widths (sizes, importances, the channel gather) is host numpy code in
+``planner.py``; the methods here only move the factors to it and back.
 """
 from __future__ import annotations
 
@@ -13,6 +15,8 @@ import torch
 
 from . import _lib
 from ._lib import check, lib
+from . import planner
+from .planner import layer_bits, plan_channels, rank_for_bits  # noqa: F401  (re-exported)
 
 __all__ = [
     "dbf_abi_version",
@@ -360,47 +364,6 @@ def dbf_factorize(W: torch.Tensor, k: int, omega: torch.Tensor | None = None, *,
     return out
 
 
-def layer_bits(N: int, R: int, M: int, ell: int = 1) -> int:
-    """Storage of one layer: N*R + R*M sign bits and 16-bit alpha, beta,
-    gamma per term (DBF summary, Control Granular de Compresion)."""
-    return N * R + R * M + 16 * ell * (N + R + M)
-
-
-def rank_for_bits(N: int, M: int, bpw: float, ell: int = 1) -> int:
-    """Largest middle width k whose storage is at most bpw bits per entry of
-    the N x M matrix (fractional budgets allowed)."""
-    k = int((bpw * N * M - 16 * ell * (N + M)) // (N + M + 16 * ell))
-    while k > 0 and layer_bits(N, k, M, ell) > bpw * N * M:
-        k -= 1
-    while layer_bits(N, k + 1, M, ell) <= bpw * N * M:
-        k += 1
-    return max(k, 0)
-
-
-def plan_channels(shapes, importances, budget_bits: float):
-    """Non-uniform middle widths for a stack (DBF summary, section 3,
-    iterative non-uniform pruning, read without data): drop the globally
-    least important channel (ties: earlier layer, then lower index) until the
-    stack's storage fits budget_bits.  shapes: (N, R, M) per layer (ell = 1);
-    importances: host arrays of length R, e.g. ``PackedLayer.channel_importance``.
-    Returns the sorted kept channel indices of each layer (host int64 arrays;
-    a layer may keep none)."""
-    import numpy as np
-
-    total = sum(layer_bits(N, R, M) for (N, R, M) in shapes)
-    cand = sorted((float(v), li, r) for li, imp in enumerate(importances)
-                  for r, v in enumerate(np.asarray(imp, dtype=np.float64)))
-    dropped = [set() for _ in shapes]
-    for _, li, r in cand:
-        if total <= budget_bits:
-            break
-        N, _, M = shapes[li]
-        dropped[li].add(r)
-        total -= N + M + 16
-    return [np.array([r for r in range(R) if r not in d], dtype=np.int64)
-            for (_, R, _), d in zip(shapes, dropped)]
-
-
 def pointer_table(tensors, device) -> torch.Tensor:
     """Device int64 array of the tensors' device addresses."""
     return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
@@ -487,26 +450,26 @@ class PackedLayer:
                    f["gamma"], f["S1"].shape[0], f["S1"].shape[1], f["S2"].shape[1])
 
     def channel_importance(self):
-        """Per middle channel r (ell = 1): |beta_r| ||alpha|| ||gamma||, the
-        Frobenius norm of the channel's rank-1 term of the update; a host
-        float64 array."""
+        """Per middle channel r (ell = 1): |beta_r| ||alpha|| ||gamma|| (see
+        ``planner.channel_importance``), from host copies of the scales; a
+        host float64 array."""
         if self.ell != 1:
             raise ValueError("channel importance is defined for ell = 1")
-        a = self.alpha.double().norm()
-        g = self.gamma.double().norm()
-        return (self.beta[0].double().abs() * a * g).cpu().numpy()
+        return planner.channel_importance(self.alpha.cpu().numpy(), self.beta.cpu().numpy(),
+                                          self.gamma.cpu().numpy())
 
     def select_channels(self, keep) -> "PackedLayer":
         """The layer restricted to the middle channels ``keep`` (sorted
-        indices): columns of S1, rows of S2 and entries of beta.  Offline
-        re-packing (unpack, gather, pack on the device)."""
-        idx = torch.as_tensor(keep, dtype=torch.int64, device=self.B1.device)
-        if idx.numel() == 0:
-            raise ValueError("a layer needs at least one channel")
-        S1 = dbf_unpack_signs(self.B1, self.N, self.R)[:, idx].contiguous()
-        S2 = dbf_unpack_signs(self.B2, self.R, self.M)[idx].contiguous()
-        return PackedLayer(dbf_pack_signs(S1), dbf_pack_signs(S2), self.alpha,
-                           self.beta[:, idx].contiguous(), self.gamma, self.N, int(idx.numel()),
+        indices): the signs are unpacked by the library, gathered on the
+        host by ``planner.select_channels`` and packed again by the library
+        (offline)."""
+        S1 = dbf_unpack_signs(self.B1, self.N, self.R).cpu().numpy()
+        S2 = dbf_unpack_signs(self.B2, self.R, self.M).cpu().numpy()
+        S1k, S2k, bk = planner.select_channels(S1, S2, self.beta.cpu().numpy(), keep)
+        dev = self.B1.device
+        return PackedLayer(dbf_pack_signs(torch.from_numpy(S1k).to(dev)),
+                           dbf_pack_signs(torch.from_numpy(S2k).to(dev)), self.alpha,
+                           torch.from_numpy(bk).to(dev), self.gamma, self.N, S1k.shape[1],
                            self.M)
 
     def transposed_signs(self):

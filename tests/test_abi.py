@@ -313,6 +313,33 @@ def test_rank_and_plan_match_the_definition():
         assert all(np.array_equal(g, w) for g, w in zip(got, want))
 
 
+def test_planner_importance_and_gather():
+    """The host planner's channel importance equals the oracle's definition,
+    and its channel gather takes the kept columns of S1, rows of S2 and
+    entries of beta, rejecting unsorted, repeated or out-of-range indices."""
+    import numpy as np
+    import oracle
+    from double_binary_rank_amd import planner
+    rng = np.random.default_rng(61)
+    a, b, g = (rng.standard_normal((1, n)).astype(np.float16) for n in (37, 11, 23))
+    assert np.allclose(planner.channel_importance(a, b, g), oracle.channel_importance(a, b, g),
+                       rtol=1e-13, atol=0)
+    with pytest.raises(ValueError):
+        planner.channel_importance(np.ones((2, 37)), np.ones((2, 11)), np.ones((2, 23)))
+    S1 = rng.choice([-1, 1], size=(9, 11)).astype(np.int8)
+    S2 = rng.choice([-1, 1], size=(11, 7)).astype(np.int8)
+    beta = rng.standard_normal((2, 11)).astype(np.float16)
+    keep = np.array([0, 3, 4, 10])
+    S1k, S2k, bk = planner.select_channels(S1, S2, beta, keep)
+    for r_new, r in enumerate(keep):
+        assert np.array_equal(S1k[:, r_new], S1[:, r])
+        assert np.array_equal(S2k[r_new], S2[r])
+        assert np.array_equal(bk[:, r_new], beta[:, r])
+    for bad in ([], [3, 1], [2, 2], [-1, 4], [0, 11]):
+        with pytest.raises(ValueError):
+            planner.select_channels(S1, S2, beta, bad)
+
+
 def _fwd_na(**kw):
     a = dict(x=A, ldx=64, B1=A, B2=A, alpha=A, beta=A, gamma=A, N=32, R=16, M=64, ell=1, T=4,
              y=A, ldy=32, y_type=_lib.DBF_F16, flags=0, stream=None)
