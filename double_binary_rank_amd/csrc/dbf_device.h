@@ -192,6 +192,87 @@ __device__ inline int32_t segment_runs(const int32_t* __restrict__ ids, int32_t 
   return carry_cnt;
 }
 
+// As segment_runs for T <= 64 * NW * PER, in one pass: thread j takes the
+// PER consecutive tokens from PER * j, and every id is requested at once.
+// A token's run start is the last run start at or before it: within the
+// wave, the nearest lower lane with a run start (a ballot and one shuffle
+// that every lane takes part in);
+// across waves, the last run start of the waves before (LDS).  A thread's
+// block-start count (0..PER, under 16) goes to the other lanes bit by bit
+// through four ballots, and across waves through LDS.  Two barriers.
+template <int NW, int PER, typename OnStart, typename OnEnd>
+__device__ inline int32_t segment_runs_local(const int32_t* __restrict__ ids, int32_t T,
+                                             int32_t n_adapters, int32_t chunk,
+                                             OnStart&& on_start, OnEnd&& on_end) {
+  static_assert(PER < 16, "block-start counts in four bits");
+  __shared__ int32_t s_rs[NW];   // per wave: its last run start, -1 if none
+  __shared__ int32_t s_cnt[NW];  // per wave: its block starts
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int32_t tb = tid * PER;
+  int32_t raw[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) raw[k] = tb + k < T ? ids[tb + k] : -1;
+  const int32_t raw_prv = (tb >= 1 && tb - 1 < T) ? ids[tb - 1] : -1;
+  int32_t id[PER];
+  uint32_t rsb = 0;  // bit k: token tb + k starts a run
+  int32_t my_last = -1;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    id[k] = tb + k < T ? norm_id(raw[k], n_adapters) : -1;
+    const int32_t prv = k == 0 ? norm_id(raw_prv, n_adapters) : id[k - 1];
+    if (tb + k < T && (tb + k == 0 || prv != id[k])) {
+      rsb |= 1u << k;
+      my_last = tb + k;
+    }
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const uint64_t H = __ballot(my_last >= 0);
+  const int32_t wave_last = H ? __builtin_amdgcn_readlane(my_last, 63 - __clzll(H)) : -1;
+  if (lane == 0) s_rs[w] = wave_last;
+  __syncthreads();
+  int32_t carry_rs = -1;
+  for (int v = 0; v < w; ++v)
+    if (s_rs[v] >= 0) carry_rs = s_rs[v];
+  const uint64_t below = H & lt;
+  const int src = below ? 63 - __clzll(below) : lane;
+  const int32_t from_lane = __shfl(my_last, src);
+  int32_t rs = below ? from_lane : carry_rs;  // run start before this thread's first token
+  uint32_t bsb = 0;  // bit k: token tb + k starts a block
+  int32_t cnt = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if ((rsb >> k) & 1u) rs = tb + k;
+    if (tb + k < T && (tb + k - rs) % chunk == 0) {
+      bsb |= 1u << k;
+      ++cnt;
+    }
+  }
+  int32_t before = 0, wtot = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint64_t Bb = __ballot((cnt >> b) & 1);
+    before += __popcll(Bb & lt) << b;
+    wtot += __popcll(Bb) << b;
+  }
+  if (lane == 0) s_cnt[w] = wtot;
+  __syncthreads();
+  int32_t idx = before, total = 0;
+  for (int v = 0; v < NW; ++v) {
+    if (v < w) idx += s_cnt[v];
+    total += s_cnt[v];
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if ((bsb >> k) & 1u) {
+      on_start(idx, tb + k, id[k]);
+      if (idx > 0) on_end(idx - 1, tb + k);
+      ++idx;
+    }
+  }
+  if (tid == 0 && total > 0) on_end(total - 1, T);
+  return total;
+}
+
 // The column-block list in global memory (workgroup of 256 threads):
 // cbl[idx] = {t0, t1, adapter, 0}, hdr->n_colblocks = count.
 __device__ inline void segment_ids(const int32_t* __restrict__ ids, int32_t T, int32_t n_adapters,

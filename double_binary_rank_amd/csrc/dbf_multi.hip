@@ -71,6 +71,18 @@ struct MaParams {
 };
 
 typedef const DBF_GLOBAL half_t* ghp;
+// Reads through the constant address space with wave-uniform addresses are
+// scalar loads: waiting for them does not wait for the vector requests in
+// flight (the x rows of stage 1).  The block list, the count and the factor
+// pointer tables are not written during a launch that reads them.
+typedef const __attribute__((address_space(4))) int32_t* cip;
+typedef const __attribute__((address_space(4))) uint64_t* cu64p;
+
+// Entry a of a pointer table (a wave-uniform): one scalar load.
+template <class P>
+__device__ inline P table_ptr(const void* tab, int32_t a) {
+  return (P)(uintptr_t)((cu64p)tab)[a];
+}
 
 // The column blocks (runs of at most 16 tokens of one adapter, from the
 // segmentation launch) that workgroup slot `first` of `stride` takes:
@@ -79,26 +91,37 @@ typedef const DBF_GLOBAL half_t* ghp;
 // inside the list's storage.)
 template <class F>
 __device__ inline void for_each_block(const MaParams& p, int first, int stride, F&& f) {
-  const ColBlock c0 = p.cbl[first];
-  const int n = p.hdr->n_colblocks;
+  const cip c0 = (cip)(p.cbl + first);
+  const int t00 = c0[0], t10 = c0[1], a0 = c0[2];
+  const int n = *(cip)&p.hdr->n_colblocks;
   for (int cb = first; cb < n; cb += stride) {
-    const ColBlock c = cb == first ? c0 : p.cbl[cb];
-    f(c.t0, c.t1 - c.t0, c.adapter);
+    if (cb == first) {
+      f(t00, t10 - t00, a0);
+    } else {
+      const cip c = (cip)(p.cbl + cb);
+      const int t0 = c[0], t1 = c[1], a = c[2];
+      f(t0, t1 - t0, a);
+    }
   }
 }
 
-// The column-block list: one workgroup of 1024 threads (a pass over 1024
-// ids has two barriers, and the ids of the next pass are requested during
-// the current one).
+// The column-block list: one workgroup of 1024 threads.  Up to 4096 ids in
+// one pass (4 consecutive ids per thread, all requested at once, two
+// barriers); beyond, passes of 1024 ids (two barriers each, the ids of the
+// next pass requested during the current one).
+constexpr int kMaSegLocal = 4096;
+template <bool LOCAL>
 __global__ __launch_bounds__(1024) void k_ma_segment(MaParams p) {
-  const int32_t n = segment_runs<16>(
-      p.ids, p.T, p.num_adapters, kMaTok,
-      [&](int32_t idx, int32_t t, int32_t id) {
-        p.cbl_w[idx].t0 = t;
-        p.cbl_w[idx].adapter = id;
-        p.cbl_w[idx].pad = 0;
-      },
-      [&](int32_t idx, int32_t t1) { p.cbl_w[idx].t1 = t1; });
+  auto on_start = [&](int32_t idx, int32_t t, int32_t id) {
+    p.cbl_w[idx].t0 = t;
+    p.cbl_w[idx].adapter = id;
+    p.cbl_w[idx].pad = 0;
+  };
+  auto on_end = [&](int32_t idx, int32_t t1) { p.cbl_w[idx].t1 = t1; };
+  const int32_t n =
+      LOCAL ? segment_runs_local<16, kMaSegLocal / 1024>(p.ids, p.T, p.num_adapters, kMaTok,
+                                                         on_start, on_end)
+            : segment_runs<16>(p.ids, p.T, p.num_adapters, kMaTok, on_start, on_end);
   if (threadIdx.x == 0) p.hdr_w->n_colblocks = n;
 }
 
@@ -151,9 +174,9 @@ __global__ __launch_bounds__(64 * kMaW1) void k_ma_stage1(MaParams p) {
       }
     };
     dma_chunk(0);
-    const char* B2 = (const char*)p.B2s[a];
-    const half_t* beta = p.betas[a];
-    const half_t* gamma = p.gammas[a];
+    const char* B2 = table_ptr<const char*>(p.B2s, a);
+    const half_t* beta = table_ptr<const half_t*>(p.betas, a);
+    const half_t* gamma = table_ptr<const half_t*>(p.gammas, a);
     v4u w[kMaBlk];
     auto sign_chunk = [&](int kc) {
 #pragma unroll
@@ -292,8 +315,8 @@ __global__ __launch_bounds__(64 * kMaW2) void k_ma_stage2(MaParams p) {
       }
       return;
     }
-    const char* B1 = (const char*)p.B1s[a];
-    const half_t* alpha = p.alphas[a];
+    const char* B1 = table_ptr<const char*>(p.B1s, a);
+    const half_t* alpha = table_ptr<const half_t*>(p.alphas, a);
     const bool live = c16 < ntok;
     // requests: the z operands (term, step) of this lane's token, the sign
     // words of this wave's quads and the workgroup's alpha rows
@@ -441,7 +464,10 @@ __global__ __launch_bounds__(64 * kMaW2) void k_ma_stage2(MaParams p) {
 template <int ELL>
 hipError_t launch_ell(const MaParams& p, int phases, hipStream_t s) {
   if (phases & 1) {
-    hipLaunchKernelGGL(k_ma_segment, dim3(1), dim3(1024), 0, s, p);
+    if (p.T <= kMaSegLocal)
+      hipLaunchKernelGGL(k_ma_segment<true>, dim3(1), dim3(1024), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_ma_segment<false>, dim3(1), dim3(1024), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -115,12 +115,22 @@ def _ones(rng, shape):
     return np.ones(shape, dtype=np.float16)
 
 
+def _scale_pm12(rng, shape):  # uniform over {-2, -1, 1, 2}: products stay exact
+    return rng.choice(np.array([-2.0, -1.0, 1.0, 2.0]), size=shape).astype(np.float16)
+
+
+def _scale_pm1(rng, shape):  # uniform over {-1, 1}
+    return rng.choice(np.array([-1.0, 1.0]), size=shape).astype(np.float16)
+
+
 _SCALES = {
     "small_plus": _scale_small_plus,
     "abs002": _scale_abs002,
     "abs1": _scale_abs1,
     "lognormal": _scale_lognormal,
     "ones": _ones,
+    "pm12": _scale_pm12,
+    "pm1": _scale_pm1,
 }
 
 

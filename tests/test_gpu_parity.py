@@ -419,13 +419,14 @@ def test_multi_adapter_many_adapters(path):
 
 
 @pytest.mark.parametrize("shape", [(70, 20, 4104, 1, 40), (200, 64, 264, 2, 77),
-                                   (64, 33, 8, 2, 16)])
+                                   (64, 33, 8, 2, 16), (96, 48, 16384, 2, 33)])
 def test_multi_short_rank_kernel(shape):
-    """The one-launch kernel of several short-rank adapters (R <= 64, at most
-    two terms) on the large-T path: N not a multiple of 4 or of 64, one or
-    two MFMA steps of rank, a reduction of two chunks ending in a partial
-    block, a partial last token tile, unsorted ids with out-of-range ones;
-    exact on integers (fp32 output, also accumulating onto a base) and
+    """The tile kernels of several short-rank adapters (R <= 64, at most two
+    terms) on the large-T path: N not a multiple of 4 or of 64, one or two
+    MFMA steps of rank, the reduction over M split over 1 to 8 workgroups
+    per tile (the last one short, ending in a partial block), a partial last
+    token tile, unsorted ids (many adapters per tile) with out-of-range
+    ones; exact on integers (fp32 output, also accumulating onto a base) and
     within the bar on fp16 data."""
     N, R, M, ell, T = shape
     B = synth.make_multi_adapter(num_adapters=6, N=N, R=R, M=M, ell=ell, T=T, seed=61,
@@ -444,6 +445,17 @@ def test_multi_short_rank_kernel(shape):
     torch.cuda.synchronize()
     assert np.array_equal(y2.cpu().numpy().astype(np.float64),
                           _multi_ref(B, ids, y_old=base).astype(np.float32).astype(np.float64))
+    # scales of both signs that differ row by row (alpha is folded into the
+    # signs of stage 2 per row), still exact (|z| as with unit scales)
+    Bs = synth.make_multi_adapter(num_adapters=6, N=N, R=R, M=M, ell=ell, T=T, seed=63,
+                                  alpha="pm12", beta="pm1", gamma="pm1", x_kind="int3",
+                                  sort=False)
+    Ds = H().DeviceAdapters(Bs.adapters)
+    ys = Ds.forward(H().to_dev_rows(Bs.x), H().to_dev(Bs.ids), path="mfma",
+                    y=H().empty_rows(T, N, torch.float32))
+    torch.cuda.synchronize()
+    assert np.array_equal(ys.cpu().numpy().astype(np.float64),
+                          _multi_ref(Bs, Bs.ids).astype(np.float32).astype(np.float64))
     Bf = synth.make_multi_adapter(num_adapters=6, N=N, R=R, M=M, ell=ell, T=T, seed=62)
     Df = H().DeviceAdapters(Bf.adapters)
     yf = Df.forward(H().to_dev_rows(Bf.x), H().to_dev(Bf.ids), path="mfma",
@@ -616,18 +628,23 @@ def _ref_blocks(ids, n_adapters, chunk):
     return out
 
 
-@pytest.mark.parametrize("path,ell,chunk,R", [("gemv", 1, 5, 32), ("gemv", 2, 2, 32),
-                                               ("mfma", 2, 32, 80), ("mfma", 2, 16, 32)])
-def test_segmentation_blocks(path, ell, chunk, R):
+@pytest.mark.parametrize("path,ell,chunk,R,T", [("gemv", 1, 5, 32, 1000), ("gemv", 2, 2, 32, 1000),
+                                                 ("mfma", 2, 32, 80, 1000),
+                                                 ("mfma", 2, 16, 32, 1000),
+                                                 ("mfma", 2, 16, 32, 4096),
+                                                 ("mfma", 1, 16, 64, 5000)])
+def test_segmentation_blocks(path, ell, chunk, R, T):
     """The column-block list the prep launch writes into the workspace (its
     header and list sit at the library's internal offsets 0 and 256) equals
-    the list by definition: runs of 1..70 tokens over several 256-id passes,
-    equal neighbouring runs that merge, and out-of-range ids."""
+    the list by definition: runs of 1..70 tokens over several passes of ids
+    (or, for ranks up to 64 on the large-T path and up to 4096 ids, one
+    pass of 4 ids per thread: the largest such T and one past it), equal
+    neighbouring runs that merge, and out-of-range ids."""
     rng = np.random.default_rng(91)
     A, parts = 7, []
-    while sum(len(p) for p in parts) < 1000:
+    while sum(len(p) for p in parts) < T:
         parts.append(np.full(int(rng.integers(1, 71)), int(rng.integers(-3, A + 3)), np.int32))
-    ids = np.concatenate(parts)[:1000]
+    ids = np.concatenate(parts)[:T]
     ids[300:340] = 4  # a run across the first pass boundary
     ids[511:513] = -1
     # (on the large-T path, ranks up to 64 cut runs every 16 tokens)
