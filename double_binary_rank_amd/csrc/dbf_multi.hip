@@ -10,8 +10,8 @@
 // A one-workgroup launch cuts the ids into column blocks: runs of at most
 // 16 tokens of one adapter (any order of ids is accepted; sorted ids give
 // about T/16 + A blocks).  A block's tokens are one MFMA column each; the
-// other columns (tokens of neighbouring blocks) are computed and not
-// stored.
+// other columns (stage 1: whatever the LDS area holds, since only the
+// block's x rows are requested; stage 2: zero) are computed and not stored.
 //   stage 1 (R <= 64 rows: one row quad), 8 waves: wave w accumulates the
 //     128-blocks w, w + 8, ... of the reduction over M; each wave requests
 //     all of a chunk's x rows straight into its own LDS area (256
@@ -151,11 +151,11 @@ __global__ __launch_bounds__(64 * kMaW1) void k_ma_stage1(MaParams p) {
     if (npass++ > 0) __syncthreads();  // the previous adapter's readers of LDS are done
 
     // A chunk's requests: this wave's blocks kb = kc + wv + 8j (blocks past
-    // the last repeat it): their x rows (16 tokens x 256 B; rows past T
-    // repeat row T-1, entries past M the last 8) straight to the wave's LDS
-    // area, 256 contiguous bytes per 16 lanes, then their sign words to
-    // registers.  The x requests need only t0, so they go out while the
-    // adapter's factor pointers are still on their way.
+    // the last repeat it): the x rows of the block's tokens (256 B each;
+    // entries past M repeat the last 8) straight to the wave's LDS area, 256
+    // contiguous bytes per 16 lanes, then their sign words to registers.
+    // The x requests need only t0, so they go out while the adapter's factor
+    // pointers are still on their way.
     auto dma_chunk = [&](int kc) {
 #pragma unroll
       for (int j = 0; j < kMaBlk; ++j) {
@@ -163,13 +163,15 @@ __global__ __launch_bounds__(64 * kMaW1) void k_ma_stage1(MaParams p) {
         kb = kb < p.nkb1 ? kb : p.nkb1 - 1;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+          // (rows past the block's tokens are not requested: their columns
+          // are computed from whatever the area holds and never stored)
           const int r = 4 * u + (lane >> 4);
-          const int t = t0 + r < p.T ? t0 + r : p.T - 1;
           const int c = (lane & 15) ^ r;
           int k = kb * kColBlock + 8 * c;
           k = k < M - 8 ? k : M - 8;
-          dma16(p.x, (uint32_t)t * (uint32_t)p.ldx * 2u + (uint32_t)k * 2u,
-                sx0 + (uint32_t)((wv * kMaBlk + j) * 4096 + u * 1024));
+          if (r < ntok)
+            dma16(p.x, (uint32_t)(t0 + r) * (uint32_t)p.ldx * 2u + (uint32_t)k * 2u,
+                  sx0 + (uint32_t)((wv * kMaBlk + j) * 4096 + u * 1024));
         }
       }
     };
