@@ -21,7 +21,7 @@
 //     summed in wave order through LDS, scaled by beta_i in fp32 and rounded
 //     once to fp16: z [ell][T][ldz] in the workspace.  One workgroup per
 //     block.
-//   stage 2, 4 waves per (block, 16 row quads of the N outputs): the
+//   stage 2, 4 waves per (block, 8 row quads of the N outputs): the
 //     reduction over R is at most two MFMA steps per term; each term's tile
 //     is scaled by alpha_i in fp32 and the terms are added in ascending i;
 //     the tile goes through LDS so that each token's 64 outputs leave as one
@@ -38,7 +38,7 @@ constexpr int kMaTok = 16;           // tokens per column block
 constexpr int kMaW1 = 8;             // stage-1 waves per workgroup
 constexpr int kMaBlk = 4;            // 128-blocks per wave per chunk of stage 1
 constexpr int kMaW2 = 4;             // stage-2 waves per workgroup
-constexpr int kMaQw = 4;             // stage-2 row quads per wave
+constexpr int kMaQw = 2;             // stage-2 row quads per wave
 constexpr int kMaMaxEll = 2;         // terms
 constexpr int kMaGamHalfs = 8704;    // LDS halfs for gamma_i of every term, zero-padded
 constexpr int kMaStage = (kMaGamHalfs / 8 + 64 * kMaW1 - 1) / (64 * kMaW1);  // chunks per thread
@@ -285,7 +285,9 @@ __global__ __launch_bounds__(64 * kMaW1) void k_ma_stage1(MaParams p) {
 }
 
 template <int ELL>
-__global__ __launch_bounds__(64 * kMaW2) void k_ma_stage2(MaParams p) {
+// (at most 128 registers: four waves per SIMD, so the blocks' dependent
+// requests of more workgroups overlap)
+__global__ __launch_bounds__(64 * kMaW2, 4) void k_ma_stage2(MaParams p) {
   constexpr int kRowsWg = kMaW2 * kMaQw * 64;  // output rows of a workgroup
   __shared__ __attribute__((aligned(16))) float sts[kMaW2][kMaTok * 64];  // each wave's tile
   __shared__ __attribute__((aligned(16))) half_t sal[ELL][kRowsWg];       // alpha_i of the rows
