@@ -532,17 +532,25 @@ def main():
         torch.cuda.synchronize()
         errm = oracle.max_norm_error(ym.float().cpu().numpy(),
                                      oracle.forward_multi_adapter(B.x, B.ids, B.adapters))
+        y_eager = ym.clone()
         nm = max(args.steps // 2, 20)
         tm = time_calls(callm, nm, args.warmup) / nm
+        # the same call captured in a HIP graph (its three launches without
+        # the host's launch gaps); the replays must leave y bit for bit as
+        # the eager call did
+        tmg = time_graph(callm, 16, max(args.steps // 16, 4), 2)
+        graph_same = bool(torch.equal(ym, y_eager))
         bm = 64 * (-(-(2 * 4096 * 64) // 8) + 2 * 2 * (4096 + 64 + 4096)) + 2 * 4096 * Tm * 2 + 4 * Tm
         fm = alg_flops(4096, 64, 4096, 2, Tm)
         out["multi_adapter_64"] = {
             "T": Tm, "adapters": 64, "us_per_call": tm * 1e6, "tokens_per_s": Tm / tm,
             "effective_GBs": bm / tm / 1e9, "hbm_frac": bm / tm / 1e9 / HBM_PEAK_GBS,
             "mfma_frac": fm / tm / 1e12 / MFMA_F16_PEAK_TFLOPS, "alg_bytes_per_call": bm,
-            "parity_err": errm,
+            "us_per_call_graph": tmg * 1e6, "hbm_frac_graph": bm / tmg / 1e9 / HBM_PEAK_GBS,
+            "graph_bit_identical": graph_same, "parity_err": errm,
         }
-        log(f"multi-adapter: {tm * 1e6:.1f} us/call, {bm / tm / 1e9:.1f} GB/s")
+        log(f"multi-adapter: {tm * 1e6:.1f} us/call, {bm / tm / 1e9:.1f} GB/s; graph replay "
+            f"{tmg * 1e6:.1f} us/call")
 
     # ------------------------------- the other configurations, timed --
     if want("configs"):
