@@ -284,9 +284,9 @@ __global__ __launch_bounds__(64 * kMaW1) void k_ma_stage1(MaParams p) {
   });
 }
 
+// (At most 128 registers: four waves per SIMD, so the dependent requests of
+// more workgroups overlap.)
 template <int ELL>
-// (at most 128 registers: four waves per SIMD, so the blocks' dependent
-// requests of more workgroups overlap)
 __global__ __launch_bounds__(64 * kMaW2, 4) void k_ma_stage2(MaParams p) {
   constexpr int kRowsWg = kMaW2 * kMaQw * 64;  // output rows of a workgroup
   __shared__ __attribute__((aligned(16))) float sts[kMaW2][kMaTok * 64];  // each wave's tile
