@@ -233,6 +233,33 @@ def test_signed_scales(shape, path):
     assert np.array_equal(got, ref(Li).astype(np.float32).astype(np.float64))
 
 
+# Layer shapes (N, R, M, ell, T) at about 515 tokens whose stages take each
+# compiled token-tile shape (NC tiles of 16 tokens, W row quads, KS reduction
+# parts) under the launcher's cost model, every size ragged: stage 1 works
+# over R rows and M reduction entries, stage 2 over N rows and R entries.
+TILE_SHAPES = [
+    (66, 1999, 136, 1, 513),   # stage 1 (4, 4, 2), stage 2 (2, 1, 8)
+    (72, 2001, 264, 2, 517),   # stage 1 (4, 2, 4), stage 2 (2, 1, 8)
+    (1999, 130, 136, 2, 515),  # stage 1 (2, 2, 4), stage 2 (4, 4, 2)
+    (1999, 520, 136, 1, 515),  # stage 1 (2, 2, 4), stage 2 (4, 2, 4)
+]
+
+
+@pytest.mark.parametrize("shape", TILE_SHAPES)
+def test_tile_shapes_every_element(shape):
+    """Every output of the token-tile stages in each compiled tile shape,
+    with tails in rows, reduction and tokens: integer inputs bit for bit
+    (|z| <= 3M stays exact in fp16), fp16 inputs within the bar."""
+    N, R, M, ell, T = shape
+    Li = synth.make_layer(N, R, M, ell, T, seed=sum(shape), alpha="ones", beta="ones",
+                          gamma="ones", x_kind="int3")
+    got = H().run_layer(Li, path="mfma", y_dtype=torch.float32)
+    assert np.array_equal(got, ref(Li).astype(np.float32).astype(np.float64))
+    L = synth.make_layer(N, R, M, ell, T, seed=sum(shape) + 1)
+    err = oracle.max_norm_error(H().run_layer(L, path="mfma"), ref(L))
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("shape", [(136, 200, 520, 2, 70), (64, 130, 904, 1, 33),
                                    (40, 72, 264, 1, 5), (40, 8448, 520, 1, 70)])
 def test_stage1_x_in_place_and_operand_tiles(shape):
