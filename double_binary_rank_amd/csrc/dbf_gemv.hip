@@ -208,6 +208,11 @@ struct GemvParams {
   int64_t ldx;
   float* z;
   int64_t ldz, zstride;
+  // PIN decode stages: stage 1 splits its reduction into ksplit parts of
+  // kslice blocks, part s writing its partial z at z + s * zpart floats;
+  // stage 2 adds the ksplit partials (its ZS template argument) in order
+  int32_t ksplit, kslice;
+  int64_t zpart;
   void* y;
   int64_t ldy;
   int32_t y_f32, accumulate;
@@ -316,7 +321,11 @@ __device__ inline void gemv_epilogue(const GemvParams& p, float* zb, void* yb, c
 // of its own blocks from gamma_i * x (stage 1) or z (stage 2) with the prep
 // kernel's arithmetic (block_parts) into its LDS area, so the operands are
 // bit for bit those of the two-launch stage.  Every workgroup repeats this
-// for its blocks: worth it while a wave's chunk is a few blocks.
+// for its blocks: worth it while a wave's chunk is a few blocks.  Stage 1
+// may split its reduction into p.ksplit parts, one work item each, so that
+// a short stage fills the compute units: part s writes its partial z (beta
+// applied) to its own slice, and stage 2 adds the ZS partials in order as
+// it reads z.
 constexpr int kPinColTokens = 2;                // PIN: ell * tokens per column block
 constexpr int kPinCols = kParts * kPinColTokens;  // PIN: live operand columns
 
@@ -332,13 +341,14 @@ struct GemvLds {
 };
 
 // The work items it = first, first + stride, ... of one stage.
-template <int STAGE, int RTG, int KC, bool MULTI, bool PIN, int NW, bool GROUP>
+template <int STAGE, int RTG, int KC, bool MULTI, bool PIN, int NW, bool GROUP, int ZS>
 __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvParams& p,
                                                                      char* lds, int first,
                                                                      int stride) {
   static_assert(!PIN || !MULTI, "operand parts are built in place for one adapter");
   static_assert(!GROUP || PIN, "grouped layers take the parts-building stages");
   static_assert(!PIN || RTG <= NW, "each wave finishes at most one row tile");
+  static_assert(ZS == 1 || (PIN && STAGE == 2), "partial z sums are read by PIN stage 2");
   typedef GemvLds<RTG, KC, PIN, NW> Lds;
   auto red = reinterpret_cast<v4f (*)[RTG][64]>(lds);
   auto pin_b = reinterpret_cast<uint8_t (*)[Lds::pinb_bytes / NW]>(lds + Lds::red_bytes);
@@ -352,7 +362,10 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
   const int c = j / kParts, part = j - kParts * (j / kParts);
   // item counts fit 32 bits (the host checks)
   const int n_cb = MULTI ? p.hdr->n_colblocks : (int)p.n_cb_host;
-  const int n_per = n_cb * (int)p.n_rg;  // items of one layer
+  // a split stage-1 reduction: the part is the slowest index of an item
+  const int nsplit = (STAGE == 1 && PIN && p.ksplit > 1) ? p.ksplit : 1;
+  const int n_cbr = n_cb * (int)p.n_rg;
+  const int n_per = n_cbr * nsplit;  // items of one layer
   const int n_items = GROUP ? n_per * p.group : n_per;
 
   for (int it = first; it < n_items; it += stride) {
@@ -361,7 +374,17 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
       layer = it / n_per;
       itl = it - layer * n_per;
     }
+    int ks = 0;
+    if constexpr (STAGE == 1 && PIN) {
+      ks = itl / n_cbr;
+      itl -= ks * n_cbr;
+    }
     const int cb = itl / (int)p.n_rg, rg = itl - cb * (int)p.n_rg;
+    // the item's reduction blocks [kb_lo, kb_hi) (the host makes every part
+    // non-empty)
+    const int64_t kb_lo = nsplit > 1 ? (int64_t)ks * p.kslice : 0;
+    const int64_t kb_hi =
+        nsplit > 1 ? (kb_lo + p.kslice < p.nkb ? kb_lo + p.kslice : p.nkb) : p.nkb;
     float* const zl = (float*)((char*)p.z + (GROUP ? layer * p.layer_ws : 0));
     void* const yl = (char*)p.y + (GROUP ? layer * p.y_layer_bytes : 0);
     int64_t t0, t1;
@@ -425,9 +448,9 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
     const int64_t nrt_here = (p.nrt - tile0) < RTG ? (p.nrt - tile0) : RTG;
     const int nq_here = (int)((nrt_here + kQuad - 1) / kQuad);
     bool first_chunk = true;
-    for (int64_t kbase = 0; kbase < p.nkb; kbase += NW * KC) {
+    for (int64_t kbase = kb_lo; kbase < kb_hi; kbase += NW * KC) {
       const int64_t kw0 = kbase + wv * KC;
-      const int nk = (int)((p.nkb - kw0) < KC ? ((p.nkb - kw0) > 0 ? (p.nkb - kw0) : 0) : KC);
+      const int nk = (int)((kb_hi - kw0) < KC ? ((kb_hi - kw0) > 0 ? (kb_hi - kw0) : 0) : KC);
       // lane's 16 bytes of unit (quad, block): the A words of its 4 row tiles
       gv4up base = (gv4up)S + ((tile0 / kQuad) * p.nkb + kw0) * (kUnitWords / 4) + lane;
       v8i bop[KC];
@@ -435,16 +458,17 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
       v4u wd[RQ][KC];
       auto load_signs = [&]() {
         // every sign word of this round is requested before the first MFMA:
-        // RQ*KC 16-byte loads (16 KB per wave at RTG*KC = 64) in flight at once
+        // RQ*KC 16-byte loads (16 KB per wave at RTG*KC = 64) in flight at
+        // once, non-temporal (streamed; measured faster on the decode calls)
 #pragma unroll
         for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
           for (int kk = 0; kk < KC; ++kk)
-            wd[rq][kk] = (rq < nq_here && kk < nk) ? base[(rq * p.nkb + kk) * (kUnitWords / 4)]
-                                                   : v4u{0u, 0u, 0u, 0u};
+            wd[rq][kk] = (rq < nq_here && kk < nk)
+                             ? __builtin_nontemporal_load(base + (rq * p.nkb + kk) * (kUnitWords / 4))
+                             : v4u{0u, 0u, 0u, 0u};
       };
       if constexpr (PIN) {
-        if (nk > 0) load_signs();
         uint8_t* pb = pin_b[wv];
         uint8_t* ps = pin_s[wv];
         // lane l holds entries 2l, 2l+1 of the block; they meet adjacent
@@ -452,23 +476,26 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
         const int boff = fp8_operand_byte(operand_k_of_col(2 * lane));
         // every entry of the wave's blocks is requested before the first
         // part is built (column cc = term * ntok + token, ell * ntok <=
-        // kPinColTokens)
+        // kPinColTokens), and the sign words after them: requests return in
+        // order, so the parts are built while the signs arrive.
         // Entries k, k+1 (k even) of a row come as one 4-byte word (x, gamma)
         // or 8-byte pair (z), every load from an address inside the row
-        // (clamped) and the entries past K zeroed after: no branch between
-        // the requests, so all of them are in flight together.  Stage 1
-        // runs here only with K even and gamma 4-byte aligned (the host
-        // checks), so its pairs are aligned words.
+        // (clamped) and the entries past K zeroed after; columns and blocks
+        // the wave does not have are skipped on wave-uniform conditions.  No
+        // per-lane branch sits between the requests, so all of them are in
+        // flight together.  Stage 1 runs here only with K even and gamma
+        // 4-byte aligned (the host checks), so its pairs are aligned words.
         constexpr int NCC = kPinColTokens;
         const int ncc = p.ell * ntok;
         v2f ev[KC][NCC];
         {
           // row starts are wave-uniform; the lane's part is a 32-bit byte
-          // offset (a parts-building stage has K <= 32 * 128)
+          // offset (a parts-building stage has K <= 256 * 128: at most
+          // kMaxZParts parts of at most 32 blocks, or 2 of 64)
           const int kc = STAGE == 1 ? (int)p.K - 2 : (int)p.ldz - 2;
           typedef const DBF_GLOBAL char* gcp;
           uint32_t ea[KC][NCC], eb[KC][NCC];
-          v2f ez[KC][NCC];
+          v2f ez[ZS][KC][NCC];
 #pragma unroll
           for (int kk = 0; kk < KC; ++kk) {
             const int k = (int)(kw0 + kk) * kColBlock + 2 * lane;
@@ -477,14 +504,28 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
             for (int cc = 0; cc < NCC; ++cc) {
               const int q = cc / ntok, ci2 = q < p.ell ? q : p.ell - 1;
               const int64_t t = t0 + (cc - q * ntok);
-              if (STAGE == 1) {
+              if (cc >= ncc || kk >= nk) {
+                // nothing to request (zeroed again at the use)
+                if (STAGE == 1) {
+                  ea[kk][cc] = 0u;
+                  eb[kk][cc] = 0u;
+                } else {
+#pragma unroll
+                  for (int zs = 0; zs < ZS; ++zs) ez[zs][kk][cc] = v2f{0.f, 0.f};
+                }
+              } else if (STAGE == 1) {
                 ea[kk][cc] = *(const DBF_GLOBAL uint32_t*)((gcp)(f.gamma + ci2 * p.K) + off);
                 eb[kk][cc] = *(const DBF_GLOBAL uint32_t*)((gcp)(p.x + t * p.ldx) + off);
               } else {
-                ez[kk][cc] = *(const DBF_GLOBAL v2f*)((gcp)(zl + ci2 * p.zstride + t * p.ldz) + off);
+                // the ZS partial sums of z (one per part of stage 1)
+#pragma unroll
+                for (int zs = 0; zs < ZS; ++zs)
+                  ez[zs][kk][cc] = *(const DBF_GLOBAL v2f*)(
+                      (gcp)(zl + zs * p.zpart + ci2 * p.zstride + t * p.ldz) + off);
               }
             }
           }
+          if (nk > 0) load_signs();
 #pragma unroll
           for (int kk = 0; kk < KC; ++kk)
 #pragma unroll
@@ -498,8 +539,13 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
                 v0 = (float)ga[0] * (float)xb[0];
                 v1 = (float)ga[1] * (float)xb[1];
               } else {
-                v0 = ez[kk][cc][0];
-                v1 = ez[kk][cc][1];
+                v0 = ez[0][kk][cc][0];
+                v1 = ez[0][kk][cc][1];
+#pragma unroll
+                for (int zs = 1; zs < ZS; ++zs) {
+                  v0 += ez[zs][kk][cc][0];
+                  v1 += ez[zs][kk][cc][1];
+                }
               }
               ev[kk][cc] = v2f{on && k < p.K ? v0 : 0.0f, on && k + 1 < p.K ? v1 : 0.0f};
             }
@@ -576,17 +622,18 @@ __device__ __attribute__((always_inline)) inline void gemv_fp4_items(const GemvP
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         scg[v] = sc_r0 + v < p.rows ? __builtin_bit_cast(half_t, (uint16_t)scu[v]) : (half_t)0.0f;
-      gemv_epilogue<STAGE, PIN ? 2 : 0>(p, zl, yl, srow, sum, tile, lane, g, part, colv, ci, ct,
-                                        ntok, t0, scg);
+      gemv_epilogue<STAGE, PIN ? 2 : 0>(p, nsplit > 1 ? zl + ks * p.zpart : zl, yl, srow, sum,
+                                        tile, lane, g, part, colv, ci, ct, ntok, t0, scg);
     }
     __syncthreads();
   }
 }
 
-template <int STAGE, int RTG, int KC, bool MULTI, bool PIN = false, int NW = 4, bool GROUP = false>
+template <int STAGE, int RTG, int KC, bool MULTI, bool PIN = false, int NW = 4, bool GROUP = false,
+          int ZS = 1>
 __global__ __launch_bounds__(64 * NW) void k_gemv_fp4(GemvParams p) {
   __shared__ __attribute__((aligned(16))) char lds[GemvLds<RTG, KC, PIN, NW>::bytes];
-  gemv_fp4_items<STAGE, RTG, KC, MULTI, PIN, NW, GROUP>(p, lds, blockIdx.x, (int)p.grid);
+  gemv_fp4_items<STAGE, RTG, KC, MULTI, PIN, NW, GROUP, ZS>(p, lds, blockIdx.x, (int)p.grid);
 }
 
 // Stage the live B operand pieces of blocks [k0, k0 + nkc) of a column block
@@ -1269,29 +1316,62 @@ constexpr int64_t kFusedLdsMax = 160 * 1024;  // LDS budget: one workgroup per c
 constexpr int kStreamQPW = 2;  // row quads per wave and item
 constexpr int kStreamD = 8;    // sign loads in flight per lane
 constexpr int64_t kStreamLdsB = 32 * 1024;  // LDS budget for staged B operands
+constexpr int64_t kPinSplitWorkgroups = 256;  // split decode stage 1: one per compute unit
 
 // A stage that builds its own operand parts: 16 waves per workgroup, so a
 // wave's chunk is kc = 1, 2 or 4 blocks (4: one adapter, not grouped), one
-// quad of row tiles per item.
+// quad of row tiles per item (stage 1: per part of its reduction).
+template <int STAGE, int KC, bool GROUP, int ZS>
+static void launch_pin_k(const GemvParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, KC, false, true, 16, GROUP, ZS>), dim3((unsigned)p.grid),
+                     dim3(1024), 0, s, p);
+}
+
+template <int KC, bool GROUP>
+static hipError_t launch_pin_stage2(const GemvParams& p, int zs, hipStream_t s) {
+  // ZS * KC <= 8: at most 16 pairs of z entries per lane in flight
+  if (zs == 1) launch_pin_k<2, KC, GROUP, 1>(p, s);
+  else if (zs == 2) launch_pin_k<2, KC, GROUP, 2>(p, s);
+  else if constexpr (KC <= 2) {
+    if (zs == 4) launch_pin_k<2, KC, GROUP, 4>(p, s);
+    else if constexpr (KC == 1) {
+      if (zs == 8) launch_pin_k<2, KC, GROUP, 8>(p, s);
+      else return hipErrorInvalidValue;
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// zs: stage 1, the parts of its reduction (p.ksplit); stage 2, the partial
+// sums of z to add.
 template <int STAGE>
-static hipError_t launch_gemv_pin(GemvParams p, int kc, hipStream_t s) {
+static hipError_t launch_gemv_pin(GemvParams p, int kc, int zs, hipStream_t s) {
   p.nq = cdiv(p.nrt, kQuad);
   p.n_rg = cdiv(p.nrt, kQuad);
-  const int64_t grid = p.n_cb_host * p.n_rg * (p.group > 1 ? p.group : 1);
+  const int64_t grid =
+      p.n_cb_host * p.n_rg * (p.group > 1 ? p.group : 1) * (STAGE == 1 ? zs : 1);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   p.grid = grid;
-  const dim3 g((unsigned)grid), b(1024);
+  if (STAGE == 2) {
+    if (p.group > 1)
+      return kc == 1 ? launch_pin_stage2<1, true>(p, zs, s) : launch_pin_stage2<2, true>(p, zs, s);
+    return kc == 1 ? launch_pin_stage2<1, false>(p, zs, s)
+           : kc == 4 ? launch_pin_stage2<4, false>(p, zs, s)
+                     : launch_pin_stage2<2, false>(p, zs, s);
+  }
   if (p.group > 1) {
-    if (kc == 1)
-      hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 1, false, true, 16, true>), g, b, 0, s, p);
-    else
-      hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 2, false, true, 16, true>), g, b, 0, s, p);
+    if (kc == 1) launch_pin_k<1, 1, true, 1>(p, s);
+    else launch_pin_k<1, 2, true, 1>(p, s);
   } else if (kc == 1) {
-    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 1, false, true, 16>), g, b, 0, s, p);
+    launch_pin_k<1, 1, false, 1>(p, s);
   } else if (kc == 4) {
-    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 4, false, true, 16>), g, b, 0, s, p);
+    launch_pin_k<1, 4, false, 1>(p, s);
   } else {
-    hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, 2, false, true, 16>), g, b, 0, s, p);
+    launch_pin_k<1, 2, false, 1>(p, s);
   }
   return hipGetLastError();
 }
@@ -1474,7 +1554,35 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
   bool pairs1 = a.M % 2 == 0;
   for (int j = 0; j < (a.group > 1 ? a.group : 1); ++j)
     pairs1 = pairs1 && (((uintptr_t)(a.group > 1 ? a.grp[j].gamma : a.single.gamma)) & 3u) == 0;
-  const int kc1 = pairs1 ? pin_kc(g1.nkb) : 0, kc2 = pin_kc(g2.nkb);
+  const int kc2 = pin_kc(g2.nkb);
+  // With stage 2 building its parts from z, stage 1 splits its reduction
+  // into zs parts (a power of two, each non-empty, at most kMaxZParts / kc2
+  // so that stage 2's requests of the partial sums stay in registers): as
+  // many as keep one workgroup per compute unit, and at least enough for a
+  // part to build its own parts (32 blocks; 64 with one operand column when
+  // stage 2 takes 4 blocks per wave, which grouped calls never do; with two
+  // columns a 64-block part measured slower than the prep launch).  The
+  // choice does not depend on the number of grouped layers, so a grouped
+  // call's z is bit for bit that of the single calls.
+  int zs = 1;
+  if (pairs1 && kc2 > 0) {
+    const int smax = kMaxZParts / kc2;
+    const int64_t pin_cols = (int64_t)a.ell * (a.T < tcb ? a.T : tcb);
+    const int64_t lim = kc2 == 4 && pin_cols == 1 ? 64 : 32;
+    const int64_t items = n_cb_max * cdiv(g1.nrt, kQuad);
+    int sp = 1;
+    while (sp < smax && cdiv(g1.nkb, sp) > lim) sp *= 2;
+    if (cdiv(g1.nkb, sp) <= lim) {
+      while (2 * sp <= smax && 2 * sp <= g1.nkb && items * 2 * sp <= kPinSplitWorkgroups) sp *= 2;
+      while (sp > 1 && (sp - 1) * cdiv(g1.nkb, sp) >= g1.nkb) sp /= 2;
+      zs = sp;
+    }
+  }
+  const int64_t kslice = cdiv(g1.nkb, zs);
+  const int kc1 = pairs1 ? pin_kc(kslice) : 0;
+  g1.ksplit = zs;
+  g1.kslice = (int32_t)kslice;
+  g1.zpart = g2.zpart = (int64_t)a.ell * a.T * ldz;
   if (a.group > 1) {
     // one launch per stage for every layer when both stages build their own
     // parts; otherwise the caller runs the layers one by one (nothing has
@@ -1492,7 +1600,7 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
   if (kc1 > 0) {
     g1.x = a.x;
     g1.ldx = a.ldx;
-    if ((a.phases & 2) && (e = launch_gemv_pin<1>(g1, kc1, s)) != hipSuccess) return e;
+    if ((a.phases & 2) && (e = launch_gemv_pin<1>(g1, kc1, zs, s)) != hipSuccess) return e;
   } else {
     pp.K = a.M;
     pp.nkb = cdiv(a.M, kColBlock);
@@ -1513,7 +1621,7 @@ hipError_t launch_gemv(const ForwardArgs& a, hipStream_t s) {
       return e;
   }
   if (!(a.phases & 4)) return hipSuccess;
-  if (kc2 > 0) return launch_gemv_pin<2>(g2, kc2, s);
+  if (kc2 > 0) return launch_gemv_pin<2>(g2, kc2, zs, s);
 
   // stage 2: y = sum_i alpha_i * (S1 . z_i)
   pp.K = a.R;

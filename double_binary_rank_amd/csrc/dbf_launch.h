@@ -50,6 +50,9 @@ struct ForwardArgs {
 constexpr int64_t kGemvMaxT = 4096;
 // fp8 parts each activation is split into on the small-T path.
 constexpr int kParts = 3;
+// Largest number of parts a decode call's stage-1 reduction is split into
+// (each part writes its own partial z; stage 2 adds them in order).
+constexpr int kMaxZParts = 8;
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline int64_t ldz_of(int64_t R) { return cdiv(R, 8) * 8; }
@@ -78,8 +81,11 @@ inline WsLayout ws_layout(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t 
   w.cbl = off;
   off += align256((size_t)max_colblocks(T) * sizeof(ColBlock));
   w.z = off;
-  // fp32 [ell][T][ldz] on the small-T path, MFMA-tiled fp16 on the large-T path
-  const size_t z32 = (size_t)ell * T * ldz_of(R) * sizeof(float);
+  // fp32 [ell][T][ldz] on the small-T path (for ell * T <= 2, up to
+  // kMaxZParts partial sums of it, one per part of a split stage-1
+  // reduction), MFMA-tiled fp16 on the large-T path
+  const size_t z32 = (size_t)ell * T * ldz_of(R) * sizeof(float) *
+                     ((int64_t)ell * T <= 2 ? kMaxZParts : 1);
   const size_t z16 = (size_t)ell * zt_term_halfs(R, T) * sizeof(half_t);
   off += align256(z32 > z16 ? z32 : z16);
   // large-T path: v_i = gamma_i * x, fp16 tiles like z (16 tokens x 128 cols)

@@ -309,17 +309,22 @@ def odd_scales(pl):
 
 @pytest.mark.parametrize("shape", [(300, 130, 260, 1, 1), (4096, 2048, 4096, 1, 1),
                                    (96, 200, 8000, 1, 2), (72, 40, 136, 2, 1), (1, 1, 1, 1, 1),
-                                   (64, 37, 96, 1, 1), (64, 38, 97, 1, 1), (80, 37, 98, 2, 1)])
+                                   (64, 37, 96, 1, 1), (64, 38, 97, 1, 1), (80, 37, 98, 2, 1),
+                                   (300, 2100, 1000, 1, 1), (64, 4200, 8200, 1, 1)])
 def test_decode_stages_build_parts(shape):
     """With one adapter and ell * tokens <= 2 the small-T stages build their
     fp8 operand parts themselves, from gamma*x and from z, with no prep
-    launch (reductions of 1..32 blocks: 1 or 2 blocks per wave; the
-    63-block stage 1 of M = 8000 takes a prep launch, and so does stage 1
-    when M is odd or gamma is not 4-byte aligned).  Odd R puts the last
-    entry pair of stage 2 on the z row's padding.  Exact on integer inputs
-    with unit scales, also with 2-byte aligned scale vectors, within the bar
-    on fp16, and equal to the result of the adapter-table call, whose prep
-    launches build the same parts, on integers."""
+    launch, and stage 1 splits its reduction into 1, 2, 4 or 8 parts whose
+    partial z stage 2 adds: here 2 parts of 2 and 1 blocks (M = 260), 8 of
+    4 (the attention layer), 8 parts of the 63-block M = 8000 with two
+    tokens, 2 of one block each (ell = 2), 4 parts read by 2 blocks per
+    stage-2 wave (R = 2100), and 2 parts of 33 and 32 blocks read by 4
+    blocks per wave (R = 4200, M = 8200, a partial last block); M odd or
+    gamma not 4-byte aligned takes the prep launch unsplit.  Odd R puts the
+    last entry pair of stage 2 on the z row's padding.  Exact on integer
+    inputs with unit scales, also with 2-byte aligned scale vectors, within
+    the bar on fp16, and equal to the result of the adapter-table call,
+    whose prep launches build the same parts, on integers."""
     N, R, M, ell, T = shape
     Li = synth.make_layer(N, R, M, ell, T, seed=101, alpha="ones", beta="ones", gamma="ones",
                           x_kind="int3")
