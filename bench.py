@@ -309,6 +309,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of cases to run (profiling)")
+    ap.add_argument("--configs", default="",
+                    help="with the configs case: comma list of its entries to run, e.g. "
+                         "mlp_up_2bpw_T1 (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run a {COPY_MIB} MiB device copy (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -557,6 +560,9 @@ def main():
         cfgs = {}
         for cfg, Tc in ((1, 4), (2, 1), (2, 8), (4, 1), (4, 16), (4, 256), (40, 1), (40, 16),
                         (40, 256)):
+            name = f"{synth.CONFIGS[cfg].name}_T{Tc}"
+            if args.configs and name not in args.configs.split(","):
+                continue
             Lc = synth.make_config_layer(cfg, Tc)
             Nc, Rc, Mc = Lc.S1.shape[0], Lc.S1.shape[1], Lc.S2.shape[1]
             plc = dbf.PackedLayer.from_signs(Lc.S1, Lc.S2, Lc.alpha, Lc.beta, Lc.gamma,
@@ -593,7 +599,6 @@ def main():
             # call, free of the host's launch rate
             tg = time_graph(callc, 64, max(args.steps // 16, 4), 2)
             bc, fc = alg_bytes(Nc, Rc, Mc, 1, Tc), alg_flops(Nc, Rc, Mc, 1, Tc)
-            name = f"{synth.CONFIGS[cfg].name}_T{Tc}"
             cfgs[name] = {
                 "N": Nc, "R": Rc, "M": Mc, "T": Tc, "us_per_call": tc * 1e6,
                 "tokens_per_s": Tc / tc, "effective_GBs": bc / tc / 1e9,
