@@ -407,8 +407,8 @@ int lds_of(const TileChoice& c) {
 // of the MFMA time of a SIMD (its two waves' 16*NC MFMAs each, at the
 // issue rate measured with the expansion in the loop) and the LDS fill at
 // about 46 bytes per cycle and compute unit (measured); a fixed cost per
-// workgroup (argument loads, first requests, K-part sum, stores); and
-// rounds when there are more workgroups than fit at once.
+// workgroup (argument loads, first requests, stores) plus the sum of its
+// KS K-parts; and rounds when there are more workgroups than fit at once.
 double tile_cost(const TileChoice& c, int64_t nq, int64_t nkb, int64_t T) {
   const int64_t n_rg = cdiv(nq, c.w), n_tb = cdiv(T, 16 * c.nc);
   const int64_t wgs = n_rg * n_tb;
@@ -418,7 +418,7 @@ double tile_cost(const TileChoice& c, int64_t nq, int64_t nkb, int64_t T) {
   const double mfma = 2.0 * 16 * c.nc * cpm;
   const double fill = (c.ks * 16.0 * c.nc * 256 + 8 * 1024 + c.ks * 256) / 46.0;
   const double iter = mfma > fill ? mfma : fill;
-  return rounds * (cdiv(nkb, c.ks) * iter + 5800.0);
+  return rounds * (cdiv(nkb, c.ks) * iter + 4600.0 + 600.0 * c.ks);
 }
 
 template <int STAGE, int NC, int W, int KS>

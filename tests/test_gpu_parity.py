@@ -240,19 +240,23 @@ def test_signed_scales(shape, path):
 TILE_SHAPES = [
     (66, 1999, 136, 1, 513),   # stage 1 (4, 4, 2), stage 2 (2, 1, 8)
     (72, 2001, 264, 2, 517),   # stage 1 (4, 2, 4), stage 2 (2, 1, 8)
-    (1999, 130, 136, 2, 515),  # stage 1 (2, 2, 4), stage 2 (4, 4, 2)
-    (1999, 520, 136, 1, 515),  # stage 1 (2, 2, 4), stage 2 (4, 2, 4)
+    (1999, 130, 136, 2, 515),  # stage 1 (4, 4, 2), stage 2 (4, 4, 2)
+    (1999, 520, 136, 1, 515),  # stage 1 (4, 4, 2), stage 2 (4, 2, 4)
+    (77, 265, 264, 2, 45),     # stage 1 (2, 2, 4), stage 2 (2, 2, 4)
+    (72, 130, 2000, 1, 70),    # stage 1 (2, 1, 8), stage 2 (4, 4, 2)
 ]
 
 
 @pytest.mark.parametrize("shape", TILE_SHAPES)
 def test_tile_shapes_every_element(shape):
     """Every output of the token-tile stages in each compiled tile shape,
-    with tails in rows, reduction and tokens: integer inputs bit for bit
-    (|z| <= 3M stays exact in fp16), fp16 inputs within the bar."""
+    with tails in rows, reduction and tokens: integer inputs with unit
+    scales bit for bit (z = S2 x is held in fp16, exact while every |z| is
+    at most 2048: asserted), fp16 inputs within the bar."""
     N, R, M, ell, T = shape
     Li = synth.make_layer(N, R, M, ell, T, seed=sum(shape), alpha="ones", beta="ones",
                           gamma="ones", x_kind="int3")
+    assert np.abs(Li.S2.astype(np.float64) @ Li.x.T.astype(np.float64)).max() <= 2048
     got = H().run_layer(Li, path="mfma", y_dtype=torch.float32)
     assert np.array_equal(got, ref(Li).astype(np.float32).astype(np.float64))
     L = synth.make_layer(N, R, M, ell, T, seed=sum(shape) + 1)
