@@ -1320,22 +1320,25 @@ constexpr int64_t kPinSplitWorkgroups = 256;  // split decode stage 1: one per c
 
 // A stage that builds its own operand parts: 16 waves per workgroup, so a
 // wave's chunk is kc = 1, 2 or 4 blocks (4: one adapter, not grouped), one
-// quad of row tiles per item (stage 1: per part of its reduction).
-template <int STAGE, int KC, bool GROUP, int ZS>
+// quad of row tiles per item (stage 1: per part of its reduction).  An item
+// of at most 4 blocks runs 4 waves instead (one block each): 16 would leave
+// most waves idle, and the workgroup's barrier would still wait for the
+// last of them to be launched.
+template <int STAGE, int KC, bool GROUP, int ZS, int NW = 16>
 static void launch_pin_k(const GemvParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, KC, false, true, 16, GROUP, ZS>), dim3((unsigned)p.grid),
-                     dim3(1024), 0, s, p);
+  hipLaunchKernelGGL((k_gemv_fp4<STAGE, 4, KC, false, true, NW, GROUP, ZS>), dim3((unsigned)p.grid),
+                     dim3(64 * NW), 0, s, p);
 }
 
-template <int KC, bool GROUP>
+template <int KC, bool GROUP, int NW>
 static hipError_t launch_pin_stage2(const GemvParams& p, int zs, hipStream_t s) {
   // ZS * KC <= 8: at most 16 pairs of z entries per lane in flight
-  if (zs == 1) launch_pin_k<2, KC, GROUP, 1>(p, s);
-  else if (zs == 2) launch_pin_k<2, KC, GROUP, 2>(p, s);
+  if (zs == 1) launch_pin_k<2, KC, GROUP, 1, NW>(p, s);
+  else if (zs == 2) launch_pin_k<2, KC, GROUP, 2, NW>(p, s);
   else if constexpr (KC <= 2) {
-    if (zs == 4) launch_pin_k<2, KC, GROUP, 4>(p, s);
+    if (zs == 4) launch_pin_k<2, KC, GROUP, 4, NW>(p, s);
     else if constexpr (KC == 1) {
-      if (zs == 8) launch_pin_k<2, KC, GROUP, 8>(p, s);
+      if (zs == 8) launch_pin_k<2, KC, GROUP, 8, NW>(p, s);
       else return hipErrorInvalidValue;
     } else {
       return hipErrorInvalidValue;
@@ -1356,16 +1359,26 @@ static hipError_t launch_gemv_pin(GemvParams p, int kc, int zs, hipStream_t s) {
       p.n_cb_host * p.n_rg * (p.group > 1 ? p.group : 1) * (STAGE == 1 ? zs : 1);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   p.grid = grid;
+  // blocks of one item
+  const int64_t nbk = STAGE == 1 && zs > 1 ? p.kslice : p.nkb;
+  const bool nw4 = nbk <= 4;
   if (STAGE == 2) {
-    if (p.group > 1)
-      return kc == 1 ? launch_pin_stage2<1, true>(p, zs, s) : launch_pin_stage2<2, true>(p, zs, s);
-    return kc == 1 ? launch_pin_stage2<1, false>(p, zs, s)
-           : kc == 4 ? launch_pin_stage2<4, false>(p, zs, s)
-                     : launch_pin_stage2<2, false>(p, zs, s);
+    if (p.group > 1) {
+      if (nw4) return launch_pin_stage2<1, true, 4>(p, zs, s);
+      return kc == 1 ? launch_pin_stage2<1, true, 16>(p, zs, s)
+                     : launch_pin_stage2<2, true, 16>(p, zs, s);
+    }
+    if (nw4) return launch_pin_stage2<1, false, 4>(p, zs, s);
+    return kc == 1 ? launch_pin_stage2<1, false, 16>(p, zs, s)
+           : kc == 4 ? launch_pin_stage2<4, false, 16>(p, zs, s)
+                     : launch_pin_stage2<2, false, 16>(p, zs, s);
   }
   if (p.group > 1) {
-    if (kc == 1) launch_pin_k<1, 1, true, 1>(p, s);
+    if (nw4) launch_pin_k<1, 1, true, 1, 4>(p, s);
+    else if (kc == 1) launch_pin_k<1, 1, true, 1>(p, s);
     else launch_pin_k<1, 2, true, 1>(p, s);
+  } else if (nw4) {
+    launch_pin_k<1, 1, false, 1, 4>(p, s);
   } else if (kc == 1) {
     launch_pin_k<1, 1, false, 1>(p, s);
   } else if (kc == 4) {
