@@ -23,6 +23,9 @@
 //   6. dS1, dS2 as dense fp16 matrix-core contractions over the tokens of
 //      all terms (k_dense_tn) from feature-major tiles (k_tiles_fm), with the
 //      straight-through slope applied in the same epilogue.
+// Independent launches of one kernel (the two k_tiles_f32, the three column
+// dot products and their sums, the four k_tiles_fm, the two k_dense_tn) run
+// as one launch over a task list: 12 launches per call instead of 21.
 // Every matrix-core operand is rounded to fp16 once from its exact fp32
 // value, as on the forward large-T path; accumulation is fp32.
 #include "dbf_device.h"
@@ -33,6 +36,38 @@ namespace dbf {
 namespace {
 
 typedef const DBF_GLOBAL v8h* gv8hp;
+
+// Up to kMaxTasks independent launches of one kernel as one launch: task j
+// takes the workgroups [first[j], first[j + 1]).
+constexpr int kMaxTasks = 4;
+template <class P>
+struct Tasks {
+  P p[kMaxTasks];
+  int64_t first[kMaxTasks + 1];
+  int32_t n;
+};
+
+// The task of workgroup b (wave-uniform); b becomes the workgroup's index
+// within its task.
+template <class P>
+__device__ inline const P& task_of(const Tasks<P>& t, int64_t& b) {
+  int j = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxTasks; ++k) j += (k < t.n && b >= t.first[k]) ? 1 : 0;
+  b -= t.first[j];
+  return t.p[j];
+}
+
+template <class P>
+struct TaskList {
+  Tasks<P> t{};
+  void add(const P& p, int64_t blocks) {
+    t.p[t.n] = p;
+    t.first[t.n + 1] = t.first[t.n] + blocks;
+    ++t.n;
+  }
+  int64_t blocks() const { return t.first[t.n]; }
+};
 
 // Token-major tiles (16 tokens x 128 reduction entries; entry (t, k) at
 // half ((t/16 * nkb + k/128) * 4 + (k%128)/32) * 512 + (16 * (k/8 % 4) +
@@ -49,9 +84,11 @@ struct TilesF32Params {
   int64_t out_term;
 };
 
-__global__ __launch_bounds__(256) void k_tiles_f32(TilesF32Params p) {
+__global__ __launch_bounds__(256) void k_tiles_f32(Tasks<TilesF32Params> tasks) {
+  int64_t b = blockIdx.x;
+  const TilesF32Params& p = task_of(tasks, b);
   const int lane = threadIdx.x & 63;
-  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t u = b * 4 + (threadIdx.x >> 6);
   if (u >= p.n_units) return;
   const int kb = (int)(u % p.nkb);
   const int64_t r = u / p.nkb;
@@ -89,8 +126,10 @@ struct TilesFmParams {
   half_t* out;
 };
 
-__global__ __launch_bounds__(256) void k_tiles_fm(TilesFmParams p) {
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(256) void k_tiles_fm(Tasks<TilesFmParams> tasks) {
+  int64_t b = blockIdx.x;
+  const TilesFmParams& p = task_of(tasks, b);
+  const int64_t id = b * blockDim.x + threadIdx.x;
   if (id >= p.n_threads) return;
   const int lane = (int)(id & 63), s = (int)((id >> 6) & 3);
   const int64_t blk = id >> 8;  // tile-major: (feature tile, 128-block)
@@ -132,11 +171,14 @@ struct ColdotParams {
   float* d;                 // [ell][C]
 };
 
-__global__ __launch_bounds__(256) void k_coldot(ColdotParams p) {
+__global__ __launch_bounds__(256) void k_coldot(Tasks<ColdotParams> tasks) {
   __shared__ float red[4][64];
+  int64_t b = blockIdx.x;
+  const ColdotParams& p = task_of(tasks, b);
+  const int blk = (int)b;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int cg = blockIdx.x % p.n_cg, i = (blockIdx.x / p.n_cg) % p.ell;
-  const int chunk = blockIdx.x / (p.n_cg * p.ell);
+  const int cg = blk % p.n_cg, i = (blk / p.n_cg) % p.ell;
+  const int chunk = blk / (p.n_cg * p.ell);
   const int c = cg * 64 + lane;
   float acc = 0.0f;
   if (c < p.C) {
@@ -159,13 +201,21 @@ __global__ __launch_bounds__(256) void k_coldot(ColdotParams p) {
         ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
-__global__ __launch_bounds__(256) void k_colsum(const float* part, int32_t n_chunks, int64_t n,
-                                                float* d) {
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= n) return;
+struct ColsumParams {
+  const float* part;  // [n_chunks][n]
+  int32_t n_chunks;
+  int64_t n;
+  float* d;
+};
+
+__global__ __launch_bounds__(256) void k_colsum(Tasks<ColsumParams> tasks) {
+  int64_t b = blockIdx.x;
+  const ColsumParams& p = task_of(tasks, b);
+  const int64_t id = b * blockDim.x + threadIdx.x;
+  if (id >= p.n) return;
   float acc = 0.0f;
-  for (int k = 0; k < n_chunks; ++k) acc += part[(int64_t)k * n + id];
-  d[id] = acc;
+  for (int k = 0; k < p.n_chunks; ++k) acc += p.part[(int64_t)k * p.n + id];
+  p.d[id] = acc;
 }
 
 // dx[t][m] = sum_i gamma_i[m] * Q_i[t][m] (terms ascending), stored as fp16
@@ -220,11 +270,14 @@ struct DenseParams {
 };
 
 template <bool OUT, bool STE>
-__global__ __launch_bounds__(256) void k_dense_tn(DenseParams p) {
+__global__ __launch_bounds__(256) void k_dense_tn(Tasks<DenseParams> tasks) {
+  int64_t b = blockIdx.x;
+  const DenseParams& p = task_of(tasks, b);
+  const int blk = (int)b;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
-  const int ga = blockIdx.x % p.n_ga, gb = blockIdx.x / p.n_ga;
+  const int ga = blk % p.n_ga, gb = blk / p.n_ga;
   const int ta0 = (ga * 2 + (wv & 1)) * 4, tb0 = (gb * 2 + (wv >> 1)) * 4;
   float* __restrict__ out = p.out;
   float* __restrict__ dH = p.dH;
@@ -306,8 +359,8 @@ __global__ __launch_bounds__(256) void k_dense_tn(DenseParams p) {
     }
 }
 
-hipError_t launch_tiles_f32(const float* src, int64_t ld, int64_t src_term, int64_t T, int64_t K,
-                            int32_t ell, const half_t* scale, half_t* out, hipStream_t s) {
+TilesF32Params tiles_f32(const float* src, int64_t ld, int64_t src_term, int64_t T, int64_t K,
+                         int32_t ell, const half_t* scale, half_t* out) {
   TilesF32Params p{};
   p.src = src;
   p.ld = ld;
@@ -320,13 +373,11 @@ hipError_t launch_tiles_f32(const float* src, int64_t ld, int64_t src_term, int6
   p.scale = scale;
   p.out = out;
   p.out_term = zt_term_halfs(K, T);
-  hipLaunchKernelGGL(k_tiles_f32, dim3((unsigned)cdiv(p.n_units, 4)), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return p;
 }
 
-hipError_t launch_tiles_fm(const half_t* src16, const float* src32, int64_t ld, int64_t src_term,
-                           int64_t T, int64_t C, int32_t ell, const half_t* scale, half_t* out,
-                           hipStream_t s) {
+TilesFmParams tiles_fm(const half_t* src16, const float* src32, int64_t ld, int64_t src_term,
+                       int64_t T, int64_t C, int32_t ell, const half_t* scale, half_t* out) {
   TilesFmParams p{};
   p.src16 = src16;
   p.src32 = src32;
@@ -339,30 +390,11 @@ hipError_t launch_tiles_fm(const half_t* src16, const float* src32, int64_t ld, 
   p.n_threads = cdiv(C, 16) * p.nkb * 256;
   p.scale = scale;
   p.out = out;
-  hipLaunchKernelGGL(k_tiles_fm, dim3((unsigned)cdiv(p.n_threads, 256)), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return p;
 }
 
-hipError_t launch_coldot(const half_t* a16, const float* a32, int64_t lda, int64_t a_term,
-                         const float* b, int64_t ldb, int64_t b_term, int64_t T, int64_t C,
-                         int32_t ell, float* part, float* d, hipStream_t s) {
-  const int32_t n_cg = (int32_t)cdiv(C, 64);
-  const int64_t n_chunks = cdiv(T, kColdotChunk);
-  ColdotParams p{a16, a32, lda, a_term, b, ldb, b_term, (int32_t)T, (int32_t)C, ell, n_cg, part, d};
-  const int64_t grid = (int64_t)n_cg * ell * n_chunks;
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_coldot, dim3((unsigned)grid), dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)ell * C;
-  hipLaunchKernelGGL(k_colsum, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, (const float*)part,
-                     (int32_t)n_chunks, n, d);
-  return hipGetLastError();
-}
-
-hipError_t launch_dense(const half_t* A, const half_t* B, int64_t rows_a, int64_t rows_b,
-                        int64_t kf, float* out, const float* H, float tau, float* dH,
-                        hipStream_t s) {
+DenseParams dense(const half_t* A, const half_t* B, int64_t rows_a, int64_t rows_b, int64_t kf,
+                  float* out, const float* H, float tau, float* dH) {
   DenseParams p{};
   p.A = A;
   p.B = B;
@@ -376,15 +408,30 @@ hipError_t launch_dense(const half_t* A, const half_t* B, int64_t rows_a, int64_
   p.H = H;
   p.inv_tau = H != nullptr ? 1.0f / tau : 0.0f;
   p.dH = dH;
-  const int64_t grid = (int64_t)p.n_ga * cdiv(rows_b, 128);
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
-  if (out != nullptr && H != nullptr)
-    hipLaunchKernelGGL((k_dense_tn<true, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
-  else if (out != nullptr)
-    hipLaunchKernelGGL((k_dense_tn<true, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((k_dense_tn<false, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return p;
+}
+
+int64_t dense_blocks(const DenseParams& p) { return (int64_t)p.n_ga * cdiv(p.rows_b, 128); }
+
+template <class P>
+bool grid_ok(const TaskList<P>& l) {
+  return l.t.n > 0 && l.blocks() <= INT32_MAX;
+}
+
+// The task list of one dense launch: out and dH select the epilogue, the
+// same for every task.
+template <bool OUT, bool STE>
+hipError_t launch_dense(const TaskList<DenseParams>& l, hipStream_t s) {
+  if (!grid_ok(l)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_dense_tn<OUT, STE>), dim3((unsigned)l.blocks()), dim3(256), 0, s, l.t);
   return hipGetLastError();
+}
+
+hipError_t launch_dense_list(const TaskList<DenseParams>& l, hipStream_t s) {
+  const bool out = l.t.p[0].out != nullptr, ste = l.t.p[0].H != nullptr;
+  if (out && ste) return launch_dense<true, true>(l, s);
+  if (out) return launch_dense<true, false>(l, s);
+  return launch_dense<false, true>(l, s);
 }
 
 }  // namespace
@@ -412,15 +459,43 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   DBF_TRY(launch_tiles_f16(a.g, a.ldg, T, N, ell, a.alpha, gt, s));
   DBF_TRY(launch_sign_product(a.B1t, R, N, ell, T, gt, pp, lr, s));
   // 3-4: W_i = S1 (beta_i U_i), Q_i = S2^T (beta_i P_i)
-  DBF_TRY(launch_tiles_f32(u, lr, T * lr, T, R, ell, a.beta, zt, s));
-  DBF_TRY(launch_tiles_f32(pp, lr, T * lr, T, R, ell, a.beta, pt, s));
+  {
+    TaskList<TilesF32Params> l;
+    for (const TilesF32Params& q : {tiles_f32(u, lr, T * lr, T, R, ell, a.beta, zt),
+                                    tiles_f32(pp, lr, T * lr, T, R, ell, a.beta, pt)})
+      l.add(q, cdiv(q.n_units, 4));
+    if (!grid_ok(l)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_tiles_f32, dim3((unsigned)l.blocks()), dim3(256), 0, s, l.t);
+    DBF_TRY(hipGetLastError());
+  }
   DBF_TRY(launch_sign_product(a.B1, N, R, ell, T, zt, w, ln, s));
   DBF_TRY(launch_sign_product(a.B2t, M, R, ell, T, pt, q, lm, s));
-  // 5: scale gradients and dx
-  float* part = (float*)(ws + L.part);
-  DBF_TRY(launch_coldot(a.g, nullptr, a.ldg, 0, w, ln, T * ln, T, N, ell, part, a.dalpha, s));
-  DBF_TRY(launch_coldot(nullptr, u, lr, T * lr, pp, lr, T * lr, T, R, ell, part, a.dbeta, s));
-  DBF_TRY(launch_coldot(a.x, nullptr, a.ldx, 0, q, lm, T * lm, T, M, ell, part, a.dgamma, s));
+  // 5: scale gradients and dx; the three dot products keep their per-chunk
+  // partial sums in separate thirds of the part region
+  {
+    float* part = (float*)(ws + L.part);
+    const int64_t n_chunks = cdiv(T, kColdotChunk);
+    const int64_t third = n_chunks * ell * bwd_colmax(N, R, M);
+    const ColdotParams cd[3] = {
+        {a.g, nullptr, a.ldg, 0, w, ln, T * ln, (int32_t)T, (int32_t)N, ell,
+         (int32_t)cdiv(N, 64), part, a.dalpha},
+        {nullptr, u, lr, T * lr, pp, lr, T * lr, (int32_t)T, (int32_t)R, ell,
+         (int32_t)cdiv(R, 64), part + third, a.dbeta},
+        {a.x, nullptr, a.ldx, 0, q, lm, T * lm, (int32_t)T, (int32_t)M, ell,
+         (int32_t)cdiv(M, 64), part + 2 * third, a.dgamma}};
+    TaskList<ColdotParams> ld;
+    TaskList<ColsumParams> ls;
+    for (const ColdotParams& c : cd) {
+      ld.add(c, (int64_t)c.n_cg * ell * n_chunks);
+      const int64_t n = (int64_t)ell * c.C;
+      ls.add(ColsumParams{c.part, (int32_t)n_chunks, n, c.d}, cdiv(n, 256));
+    }
+    if (!grid_ok(ld) || !grid_ok(ls)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_coldot, dim3((unsigned)ld.blocks()), dim3(256), 0, s, ld.t);
+    DBF_TRY(hipGetLastError());
+    hipLaunchKernelGGL(k_colsum, dim3((unsigned)ls.blocks()), dim3(256), 0, s, ls.t);
+    DBF_TRY(hipGetLastError());
+  }
   {
     DxParams p{q, lm, T * lm, a.gamma, (int32_t)T, (int32_t)M, ell, a.dx, a.lddx, a.dx_f32 ? 1 : 0};
     hipLaunchKernelGGL(k_dx, dim3((unsigned)cdiv(T * M, 256)), dim3(256), 0, s, p);
@@ -428,19 +503,49 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   }
   // 6: sign gradients over the tokens of every term
   const int64_t kf = bwd_kf(ell, T);
-  if (a.dS1 != nullptr || a.dH1 != nullptr) {
-    half_t* gf = (half_t*)(ws + L.gf);
-    half_t* zf = (half_t*)(ws + L.zf);
-    DBF_TRY(launch_tiles_fm(a.g, nullptr, a.ldg, 0, T, N, ell, a.alpha, gf, s));
-    DBF_TRY(launch_tiles_fm(nullptr, u, lr, T * lr, T, R, ell, a.beta, zf, s));
-    DBF_TRY(launch_dense(gf, zf, N, R, kf, a.dS1, a.H1, a.tau, a.dH1, s));
+  const bool want1 = a.dS1 != nullptr || a.dH1 != nullptr;
+  const bool want2 = a.dS2 != nullptr || a.dH2 != nullptr;
+  if (!want1 && !want2) return hipSuccess;
+  half_t* gf = (half_t*)(ws + L.gf);
+  half_t* zf = (half_t*)(ws + L.zf);
+  half_t* pf = (half_t*)(ws + L.pf);
+  half_t* vf = (half_t*)(ws + L.vf);
+  {
+    TaskList<TilesFmParams> l;
+    auto add = [&](const TilesFmParams& q) { l.add(q, cdiv(q.n_threads, 256)); };
+    if (want1) {
+      add(tiles_fm(a.g, nullptr, a.ldg, 0, T, N, ell, a.alpha, gf));
+      add(tiles_fm(nullptr, u, lr, T * lr, T, R, ell, a.beta, zf));
+    }
+    if (want2) {
+      add(tiles_fm(nullptr, pp, lr, T * lr, T, R, ell, a.beta, pf));
+      add(tiles_fm(a.x, nullptr, a.ldx, 0, T, M, ell, a.gamma, vf));
+    }
+    if (!grid_ok(l)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_tiles_fm, dim3((unsigned)l.blocks()), dim3(256), 0, s, l.t);
+    DBF_TRY(hipGetLastError());
   }
-  if (a.dS2 != nullptr || a.dH2 != nullptr) {
-    half_t* pf = (half_t*)(ws + L.pf);
-    half_t* vf = (half_t*)(ws + L.vf);
-    DBF_TRY(launch_tiles_fm(nullptr, pp, lr, T * lr, T, R, ell, a.beta, pf, s));
-    DBF_TRY(launch_tiles_fm(a.x, nullptr, a.ldx, 0, T, M, ell, a.gamma, vf, s));
-    DBF_TRY(launch_dense(pf, vf, R, M, kf, a.dS2, a.H2, a.tau, a.dH2, s));
+  const DenseParams d1 = dense(gf, zf, N, R, kf, a.dS1, a.H1, a.tau, a.dH1);
+  const DenseParams d2 = dense(pf, vf, R, M, kf, a.dS2, a.H2, a.tau, a.dH2);
+  // one launch when both products take the same epilogue
+  const bool same = want1 && want2 && (a.dS1 != nullptr) == (a.dS2 != nullptr) &&
+                    (a.H1 != nullptr) == (a.H2 != nullptr);
+  if (same) {
+    TaskList<DenseParams> l;
+    l.add(d1, dense_blocks(d1));
+    l.add(d2, dense_blocks(d2));
+    DBF_TRY(launch_dense_list(l, s));
+  } else {
+    if (want1) {
+      TaskList<DenseParams> l;
+      l.add(d1, dense_blocks(d1));
+      DBF_TRY(launch_dense_list(l, s));
+    }
+    if (want2) {
+      TaskList<DenseParams> l;
+      l.add(d2, dense_blocks(d2));
+      DBF_TRY(launch_dense_list(l, s));
+    }
   }
 #undef DBF_TRY
   return hipSuccess;

@@ -181,6 +181,10 @@ inline int64_t bwd_kf(int32_t ell, int64_t T) { return (int64_t)ell * cdiv(T, 12
 // a multiple of 4 floats, for the 16-byte stores of the sign-product kernel.
 inline int64_t bwd_ld(int64_t cols) { return cdiv(cols, 4) * 4; }
 
+inline int64_t bwd_colmax(int64_t N, int64_t R, int64_t M) {
+  return N > R ? (N > M ? N : M) : (R > M ? R : M);
+}
+
 inline BwdLayout bwd_layout(int64_t N, int64_t R, int64_t M, int32_t ell, int64_t T) {
   BwdLayout L{};
   size_t off = 0;
@@ -202,8 +206,9 @@ inline BwdLayout bwd_layout(int64_t N, int64_t R, int64_t M, int32_t ell, int64_
   L.zf = take((size_t)cdiv(R, 16) * kf * 16 * sizeof(half_t));
   L.pf = take((size_t)cdiv(R, 16) * kf * 16 * sizeof(half_t));
   L.vf = take((size_t)cdiv(M, 16) * kf * 16 * sizeof(half_t));
-  const int64_t cmax = N > R ? (N > M ? N : M) : (R > M ? R : M);
-  L.part = take((size_t)cdiv(T, kColdotChunk) * ell * cmax * sizeof(float));
+  // per-chunk partial sums of the three column dot products (dalpha,
+  // dbeta, dgamma), one third each
+  L.part = take((size_t)3 * cdiv(T, kColdotChunk) * ell * bwd_colmax(N, R, M) * sizeof(float));
   L.total = off;
   return L;
 }

@@ -805,6 +805,37 @@ def test_backward_fp16(shape):
             assert err <= TOL, (k, err)
 
 
+@pytest.mark.parametrize("sign_grads,which", [(True, "H1"), (False, "H2"), (True, None)])
+def test_backward_partial_sign_grads(sign_grads, which):
+    """Sign gradients with only some outputs requested: dS1 and dS2 with the
+    straight-through dH1 alone (the two dense products then take different
+    epilogues), dH2 alone without dS, and dS alone; each requested output
+    within the bar, the others absent."""
+    N, R, M, ell, T = 96, 200, 136, 2, 40
+    L = synth.make_layer(N, R, M, ell, T, seed=215)
+    rng = np.random.default_rng(216)
+    G = oracle.fp16_rne(rng.standard_normal((T, N)))
+    H1 = rng.standard_normal((N, R)).astype(np.float32)
+    H2 = rng.standard_normal((R, M)).astype(np.float32)
+    want = _bwd_ref(L, G, H1=H1, H2=H2, tau=0.5)
+    pl = H().upload(L)
+    kw = {}
+    if which == "H1":
+        kw = dict(H1=torch.as_tensor(H1).cuda(), tau=0.5)
+    elif which == "H2":
+        kw = dict(H2=torch.as_tensor(H2).cuda(), tau=0.5)
+    out = pl.backward(H().to_dev_rows(L.x), H().to_dev_rows(np.asarray(G, np.float16)),
+                      dx_dtype=torch.float32, sign_grads=sign_grads, **kw)
+    torch.cuda.synchronize()
+    expect = {"dx", "dalpha", "dbeta", "dgamma"}
+    expect |= {"dS1", "dS2"} if sign_grads else set()
+    expect |= {"d" + which} if which else set()
+    assert set(out) == expect
+    for k in sorted(expect):
+        err = oracle.max_norm_error(out[k].float().cpu().numpy().astype(np.float64), want[k])
+        assert err <= TOL, (k, err)
+
+
 def test_backward_attention_layer():
     """The attention projection (4096 x 4096, R = 2048, log-normal scales) at
     T = 64 tokens: every gradient within the bar."""
