@@ -19,13 +19,15 @@
 //      packing of S1;
 //   3. tiles of Z_i = beta_i.U_i and of beta_i.P_i (k_tiles_f32);
 //   4. W_i = S1 Z_i and Q_i = S2^T (beta_i.P_i), again stage 3;
-//   5. the column dot products (k_coldot, k_colsum) and dx (k_dx);
+//   5. the column dot products (coldot_block, colsum_block) and dx
+//      (dx_block);
 //   6. dS1, dS2 as dense fp16 matrix-core contractions over the tokens of
-//      all terms (k_dense_tn) from feature-major tiles (k_tiles_fm), with the
-//      straight-through slope applied in the same epilogue.
-// Independent launches of one kernel (the two k_tiles_f32, the three column
-// dot products and their sums, the four k_tiles_fm, the two k_dense_tn) run
-// as one launch over a task list: 12 launches per call instead of 21.
+//      all terms (dense_block) from feature-major tiles (tiles_fm_block),
+//      with the straight-through slope applied in the same epilogue.
+// Independent work in one launch over task lists: the two k_tiles_f32; the
+// three column dot products, dx and the four feature-major tiles
+// (k_bwd_mid); the sums of the dot products' chunks and the two dense
+// products (k_bwd_end): 9 launches per call instead of 21.
 // Every matrix-core operand is rounded to fp16 once from its exact fp32
 // value, as on the forward large-T path; accumulation is fp32.
 #include "dbf_device.h"
@@ -126,9 +128,7 @@ struct TilesFmParams {
   half_t* out;
 };
 
-__global__ __launch_bounds__(256) void k_tiles_fm(Tasks<TilesFmParams> tasks) {
-  int64_t b = blockIdx.x;
-  const TilesFmParams& p = task_of(tasks, b);
+__device__ inline void tiles_fm_block(const TilesFmParams& p, int64_t b) {
   const int64_t id = b * blockDim.x + threadIdx.x;
   if (id >= p.n_threads) return;
   const int lane = (int)(id & 63), s = (int)((id >> 6) & 3);
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void k_tiles_fm(Tasks<TilesFmParams> tasks) {
 // d_i[c] = sum_t a_i[t][c] * b_i[t][c] in fp32, deterministic: workgroup
 // (column group of 64, token chunk of kColdotChunk) has 4 waves, wave w
 // summing tokens w, w+4, ... of the chunk for 64 columns; the 4 partials are
-// added in wave order and stored per chunk, and k_colsum adds the chunks in
+// added in wave order and stored per chunk, and colsum_block adds the chunks in
 // ascending order.  a is fp16 [T][lda] shared by the terms (a16) or fp32 per
 // term (a32); b is fp32 [ell][T][ldb].
 struct ColdotParams {
@@ -171,11 +171,8 @@ struct ColdotParams {
   float* d;                 // [ell][C]
 };
 
-__global__ __launch_bounds__(256) void k_coldot(Tasks<ColdotParams> tasks) {
+__device__ inline void coldot_block(const ColdotParams& p, int blk) {
   __shared__ float red[4][64];
-  int64_t b = blockIdx.x;
-  const ColdotParams& p = task_of(tasks, b);
-  const int blk = (int)b;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int cg = blk % p.n_cg, i = (blk / p.n_cg) % p.ell;
   const int chunk = blk / (p.n_cg * p.ell);
@@ -208,9 +205,7 @@ struct ColsumParams {
   float* d;
 };
 
-__global__ __launch_bounds__(256) void k_colsum(Tasks<ColsumParams> tasks) {
-  int64_t b = blockIdx.x;
-  const ColsumParams& p = task_of(tasks, b);
+__device__ inline void colsum_block(const ColsumParams& p, int64_t b) {
   const int64_t id = b * blockDim.x + threadIdx.x;
   if (id >= p.n) return;
   float acc = 0.0f;
@@ -230,8 +225,8 @@ struct DxParams {
   int32_t f32;
 };
 
-__global__ __launch_bounds__(256) void k_dx(DxParams p) {
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__device__ inline void dx_block(const DxParams& p, int64_t b) {
+  const int64_t id = b * blockDim.x + threadIdx.x;
   if (id >= (int64_t)p.T * p.M) return;
   const int64_t t = id / p.M, m = id - t * p.M;
   float acc = 0.0f;
@@ -270,10 +265,7 @@ struct DenseParams {
 };
 
 template <bool OUT, bool STE>
-__global__ __launch_bounds__(256) void k_dense_tn(Tasks<DenseParams> tasks) {
-  int64_t b = blockIdx.x;
-  const DenseParams& p = task_of(tasks, b);
-  const int blk = (int)b;
+__device__ inline void dense_block(const DenseParams& p, int blk) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
@@ -359,6 +351,52 @@ __global__ __launch_bounds__(256) void k_dense_tn(Tasks<DenseParams> tasks) {
     }
 }
 
+// The launch after the sign products W and Q: the three column dot
+// products (workgroups [0, cd_end)), dx ([cd_end, dx_end)) and the
+// feature-major tiles of the sign gradients ([dx_end, ...)).  They read only
+// what earlier launches wrote.
+struct MidParams {
+  Tasks<ColdotParams> cd;
+  DxParams dx;
+  Tasks<TilesFmParams> fm;
+  int64_t cd_end, dx_end;
+};
+
+__global__ __launch_bounds__(256) void k_bwd_mid(MidParams m) {
+  int64_t b = blockIdx.x;
+  if (b < m.cd_end) {
+    const ColdotParams& p = task_of(m.cd, b);
+    coldot_block(p, (int)b);
+  } else if (b < m.dx_end) {
+    dx_block(m.dx, b - m.cd_end);
+  } else {
+    b -= m.dx_end;
+    const TilesFmParams& p = task_of(m.fm, b);
+    tiles_fm_block(p, b);
+  }
+}
+
+// The last launch: the sums of the dot products' chunks (workgroups [0,
+// cs_end)) and the sign-gradient products with one epilogue.
+struct EndParams {
+  Tasks<ColsumParams> cs;
+  Tasks<DenseParams> dn;
+  int64_t cs_end;
+};
+
+template <bool OUT, bool STE>
+__global__ __launch_bounds__(256) void k_bwd_end(EndParams e) {
+  int64_t b = blockIdx.x;
+  if (b < e.cs_end) {
+    const ColsumParams& p = task_of(e.cs, b);
+    colsum_block(p, b);
+  } else {
+    b -= e.cs_end;
+    const DenseParams& p = task_of(e.dn, b);
+    dense_block<OUT, STE>(p, (int)b);
+  }
+}
+
 TilesF32Params tiles_f32(const float* src, int64_t ld, int64_t src_term, int64_t T, int64_t K,
                          int32_t ell, const half_t* scale, half_t* out) {
   TilesF32Params p{};
@@ -418,20 +456,28 @@ bool grid_ok(const TaskList<P>& l) {
   return l.t.n > 0 && l.blocks() <= INT32_MAX;
 }
 
-// The task list of one dense launch: out and dH select the epilogue, the
-// same for every task.
-template <bool OUT, bool STE>
-hipError_t launch_dense(const TaskList<DenseParams>& l, hipStream_t s) {
-  if (!grid_ok(l)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_dense_tn<OUT, STE>), dim3((unsigned)l.blocks()), dim3(256), 0, s, l.t);
+// One k_bwd_end launch: the column sums in `cs` (may be empty) and the dense
+// products in `dn` (may be empty), which share one epilogue: out and dH of
+// the first select it.
+hipError_t launch_end(const TaskList<ColsumParams>& cs, const TaskList<DenseParams>& dn,
+                      hipStream_t s) {
+  EndParams e{};
+  e.cs = cs.t;
+  e.dn = dn.t;
+  e.cs_end = cs.blocks();
+  const int64_t grid = cs.blocks() + dn.blocks();
+  if (grid <= 0) return hipSuccess;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  const bool out = dn.t.n == 0 || dn.t.p[0].out != nullptr;
+  const bool ste = dn.t.n > 0 && dn.t.p[0].H != nullptr;
+  const dim3 g((unsigned)grid), b(256);
+  if (out && ste)
+    hipLaunchKernelGGL((k_bwd_end<true, true>), g, b, 0, s, e);
+  else if (out)
+    hipLaunchKernelGGL((k_bwd_end<true, false>), g, b, 0, s, e);
+  else
+    hipLaunchKernelGGL((k_bwd_end<false, true>), g, b, 0, s, e);
   return hipGetLastError();
-}
-
-hipError_t launch_dense_list(const TaskList<DenseParams>& l, hipStream_t s) {
-  const bool out = l.t.p[0].out != nullptr, ste = l.t.p[0].H != nullptr;
-  if (out && ste) return launch_dense<true, true>(l, s);
-  if (out) return launch_dense<true, false>(l, s);
-  return launch_dense<false, true>(l, s);
 }
 
 }  // namespace
@@ -470,49 +516,38 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   }
   DBF_TRY(launch_sign_product(a.B1, N, R, ell, T, zt, w, ln, s));
   DBF_TRY(launch_sign_product(a.B2t, M, R, ell, T, pt, q, lm, s));
-  // 5: scale gradients and dx; the three dot products keep their per-chunk
-  // partial sums in separate thirds of the part region
-  {
-    float* part = (float*)(ws + L.part);
-    const int64_t n_chunks = cdiv(T, kColdotChunk);
-    const int64_t third = n_chunks * ell * bwd_colmax(N, R, M);
-    const ColdotParams cd[3] = {
-        {a.g, nullptr, a.ldg, 0, w, ln, T * ln, (int32_t)T, (int32_t)N, ell,
-         (int32_t)cdiv(N, 64), part, a.dalpha},
-        {nullptr, u, lr, T * lr, pp, lr, T * lr, (int32_t)T, (int32_t)R, ell,
-         (int32_t)cdiv(R, 64), part + third, a.dbeta},
-        {a.x, nullptr, a.ldx, 0, q, lm, T * lm, (int32_t)T, (int32_t)M, ell,
-         (int32_t)cdiv(M, 64), part + 2 * third, a.dgamma}};
-    TaskList<ColdotParams> ld;
-    TaskList<ColsumParams> ls;
-    for (const ColdotParams& c : cd) {
-      ld.add(c, (int64_t)c.n_cg * ell * n_chunks);
-      const int64_t n = (int64_t)ell * c.C;
-      ls.add(ColsumParams{c.part, (int32_t)n_chunks, n, c.d}, cdiv(n, 256));
-    }
-    if (!grid_ok(ld) || !grid_ok(ls)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_coldot, dim3((unsigned)ld.blocks()), dim3(256), 0, s, ld.t);
-    DBF_TRY(hipGetLastError());
-    hipLaunchKernelGGL(k_colsum, dim3((unsigned)ls.blocks()), dim3(256), 0, s, ls.t);
-    DBF_TRY(hipGetLastError());
+  // 5-6: the scale gradients, dx and the sign gradients in two launches: the
+  // column dot products, dx and the feature-major tiles, then the sums of
+  // the dot products' chunks and the dense sign-gradient products.  The
+  // three dot products keep their per-chunk partial sums in separate thirds
+  // of the part region.
+  float* part = (float*)(ws + L.part);
+  const int64_t n_chunks = cdiv(T, kColdotChunk);
+  const int64_t third = n_chunks * ell * bwd_colmax(N, R, M);
+  const ColdotParams cd[3] = {
+      {a.g, nullptr, a.ldg, 0, w, ln, T * ln, (int32_t)T, (int32_t)N, ell, (int32_t)cdiv(N, 64),
+       part, a.dalpha},
+      {nullptr, u, lr, T * lr, pp, lr, T * lr, (int32_t)T, (int32_t)R, ell, (int32_t)cdiv(R, 64),
+       part + third, a.dbeta},
+      {a.x, nullptr, a.ldx, 0, q, lm, T * lm, (int32_t)T, (int32_t)M, ell, (int32_t)cdiv(M, 64),
+       part + 2 * third, a.dgamma}};
+  TaskList<ColdotParams> lcd;
+  TaskList<ColsumParams> lcs;
+  for (const ColdotParams& c : cd) {
+    lcd.add(c, (int64_t)c.n_cg * ell * n_chunks);
+    const int64_t n = (int64_t)ell * c.C;
+    lcs.add(ColsumParams{c.part, (int32_t)n_chunks, n, c.d}, cdiv(n, 256));
   }
-  {
-    DxParams p{q, lm, T * lm, a.gamma, (int32_t)T, (int32_t)M, ell, a.dx, a.lddx, a.dx_f32 ? 1 : 0};
-    hipLaunchKernelGGL(k_dx, dim3((unsigned)cdiv(T * M, 256)), dim3(256), 0, s, p);
-    DBF_TRY(hipGetLastError());
-  }
-  // 6: sign gradients over the tokens of every term
   const int64_t kf = bwd_kf(ell, T);
   const bool want1 = a.dS1 != nullptr || a.dH1 != nullptr;
   const bool want2 = a.dS2 != nullptr || a.dH2 != nullptr;
-  if (!want1 && !want2) return hipSuccess;
   half_t* gf = (half_t*)(ws + L.gf);
   half_t* zf = (half_t*)(ws + L.zf);
   half_t* pf = (half_t*)(ws + L.pf);
   half_t* vf = (half_t*)(ws + L.vf);
+  TaskList<TilesFmParams> lfm;
   {
-    TaskList<TilesFmParams> l;
-    auto add = [&](const TilesFmParams& q) { l.add(q, cdiv(q.n_threads, 256)); };
+    auto add = [&](const TilesFmParams& f) { lfm.add(f, cdiv(f.n_threads, 256)); };
     if (want1) {
       add(tiles_fm(a.g, nullptr, a.ldg, 0, T, N, ell, a.alpha, gf));
       add(tiles_fm(nullptr, u, lr, T * lr, T, R, ell, a.beta, zf));
@@ -521,31 +556,34 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
       add(tiles_fm(nullptr, pp, lr, T * lr, T, R, ell, a.beta, pf));
       add(tiles_fm(a.x, nullptr, a.ldx, 0, T, M, ell, a.gamma, vf));
     }
-    if (!grid_ok(l)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_tiles_fm, dim3((unsigned)l.blocks()), dim3(256), 0, s, l.t);
+  }
+  {
+    MidParams m{};
+    m.cd = lcd.t;
+    m.dx = DxParams{q, lm, T * lm, a.gamma, (int32_t)T, (int32_t)M, ell, a.dx, a.lddx,
+                    a.dx_f32 ? 1 : 0};
+    m.fm = lfm.t;
+    m.cd_end = lcd.blocks();
+    m.dx_end = m.cd_end + cdiv(T * M, 256);
+    const int64_t grid = m.dx_end + lfm.blocks();
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_bwd_mid, dim3((unsigned)grid), dim3(256), 0, s, m);
     DBF_TRY(hipGetLastError());
   }
   const DenseParams d1 = dense(gf, zf, N, R, kf, a.dS1, a.H1, a.tau, a.dH1);
   const DenseParams d2 = dense(pf, vf, R, M, kf, a.dS2, a.H2, a.tau, a.dH2);
-  // one launch when both products take the same epilogue
+  // both products with the column sums when they take the same epilogue
   const bool same = want1 && want2 && (a.dS1 != nullptr) == (a.dS2 != nullptr) &&
                     (a.H1 != nullptr) == (a.H2 != nullptr);
-  if (same) {
-    TaskList<DenseParams> l;
-    l.add(d1, dense_blocks(d1));
-    l.add(d2, dense_blocks(d2));
-    DBF_TRY(launch_dense_list(l, s));
-  } else {
-    if (want1) {
-      TaskList<DenseParams> l;
-      l.add(d1, dense_blocks(d1));
-      DBF_TRY(launch_dense_list(l, s));
-    }
-    if (want2) {
-      TaskList<DenseParams> l;
-      l.add(d2, dense_blocks(d2));
-      DBF_TRY(launch_dense_list(l, s));
-    }
+  TaskList<DenseParams> ldn;
+  if (want1) ldn.add(d1, dense_blocks(d1));
+  if (want2 && (same || !want1)) ldn.add(d2, dense_blocks(d2));
+  DBF_TRY(launch_end(lcs, ldn, s));
+  if (want1 && want2 && !same) {
+    TaskList<ColsumParams> none;
+    TaskList<DenseParams> l2;
+    l2.add(d2, dense_blocks(d2));
+    DBF_TRY(launch_end(none, l2, s));
   }
 #undef DBF_TRY
   return hipSuccess;
