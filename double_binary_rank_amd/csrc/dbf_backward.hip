@@ -13,7 +13,7 @@
 //   dH = dS * (1 - tanh(H/tau)^2) / tau  (soft sign tanh(h/tau)).
 //
 // Launch sequence (one stream):
-//   1. fp16 operand tiles of V_i and of G.alpha_i (k_prep_v);
+//   1. fp16 operand tiles of V_i and of G.alpha_i (k_prep_v2, one launch);
 //   2. U_i = S2 V_i and P_i = S1^T (G.alpha_i): the large-T sign-product
 //      kernel with raw fp32 output (k_gemm stage 3), P from the transposed
 //      packing of S1;
@@ -27,7 +27,8 @@
 // Independent work in one launch over task lists: the two k_tiles_f32; the
 // three column dot products, dx and the four feature-major tiles
 // (k_bwd_mid); the sums of the dot products' chunks and the two dense
-// products (k_bwd_end): 9 launches per call instead of 21.
+// products (k_bwd_end); the two fp16 tile builds (k_prep_v2): 8 launches per
+// call instead of 21.
 // Every matrix-core operand is rounded to fp16 once from its exact fp32
 // value, as on the forward large-T path; accumulation is fp32.
 #include "dbf_device.h"
@@ -500,9 +501,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   if ((e = (x)) != hipSuccess) return e
   const int64_t lr = bwd_ld(R), ln = bwd_ld(N), lm = bwd_ld(M);
   // 1-2: U_i = S2 (gamma_i x), P_i = S1^T (alpha_i G)
-  DBF_TRY(launch_tiles_f16(a.x, a.ldx, T, M, ell, a.gamma, vt, s));
+  DBF_TRY(launch_tiles_f16_pair(TilesF16{a.x, a.ldx, M, a.gamma, vt},
+                                TilesF16{a.g, a.ldg, N, a.alpha, gt}, T, ell, s));
   DBF_TRY(launch_sign_product(a.B2, R, M, ell, T, vt, u, lr, s));
-  DBF_TRY(launch_tiles_f16(a.g, a.ldg, T, N, ell, a.alpha, gt, s));
   DBF_TRY(launch_sign_product(a.B1t, R, N, ell, T, gt, pp, lr, s));
   // 3-4: W_i = S1 (beta_i U_i), Q_i = S2^T (beta_i P_i)
   {

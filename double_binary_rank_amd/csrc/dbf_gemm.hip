@@ -241,14 +241,10 @@ struct PrepVParams {
 // past T and tokens whose adapter id is out of range are zero.  One fp16
 // rounding of the exact product.
 template <bool MULTI>
-__global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
-  if (MULTI && p.seg_cbl != nullptr && blockIdx.x == 0) {
-    segment_ids(p.ids, p.T, p.num_adapters, p.seg_chunk, p.seg_cbl, p.seg_hdr);
-    return;
-  }
+__device__ inline void prep_v_block(const PrepVParams& p, int blk) {
   const int lane = threadIdx.x & 63;
   // unit counts fit 32 bits (the workspace bounds them; the host checks)
-  const int u = ((int)blockIdx.x - (MULTI && p.seg_cbl != nullptr ? 1 : 0)) * 4 + (threadIdx.x >> 6);
+  const int u = blk * 4 + (threadIdx.x >> 6);
   if (u >= (int)p.n_units) return;  // uniform per wave
   const int r = u / p.nkb, kb = u - r * p.nkb;
   const int ntt = (p.T + 15) >> 4;
@@ -285,6 +281,25 @@ __global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
     }
     *(v8h*)(out + s * 512) = o;
   }
+}
+
+template <bool MULTI>
+__global__ __launch_bounds__(256) void k_prep_v(PrepVParams p) {
+  if (MULTI && p.seg_cbl != nullptr && blockIdx.x == 0) {
+    segment_ids(p.ids, p.T, p.num_adapters, p.seg_chunk, p.seg_cbl, p.seg_hdr);
+    return;
+  }
+  prep_v_block<MULTI>(p, (int)blockIdx.x - (MULTI && p.seg_cbl != nullptr ? 1 : 0));
+}
+
+// Two independent one-adapter tile builds in one launch: workgroups [0, n0)
+// build p0's tiles, the rest p1's.
+__global__ __launch_bounds__(256) void k_prep_v2(PrepVParams p0, PrepVParams p1, int32_t n0) {
+  const int b = (int)blockIdx.x;
+  if (b < n0)
+    prep_v_block<false>(p0, b);
+  else
+    prep_v_block<false>(p1, b - n0);
 }
 
 // Several adapters: the first column block of a workgroup and, for up to
@@ -833,21 +848,29 @@ hipError_t launch_stage(GemmParams p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_tiles_f16(const half_t* src, int64_t ld, int64_t T, int64_t K, int32_t ell,
-                            const half_t* scale, half_t* out, hipStream_t s) {
-  PrepVParams pv{};
-  pv.x = src;
-  pv.ldx = ld;
-  pv.T = (int32_t)T;
-  pv.M = (int32_t)K;
-  pv.ell = ell;
-  pv.nkb = (int32_t)cdiv(K, kColBlock);
-  pv.n_units = (int64_t)ell * cdiv(T, 16) * pv.nkb;
-  pv.gamma = scale;
-  pv.v = out;
-  pv.v_term = zt_term_halfs(K, T);
-  if (pv.n_units > INT32_MAX - 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_prep_v<false>, dim3((unsigned)cdiv(pv.n_units, 4)), dim3(256), 0, s, pv);
+hipError_t launch_tiles_f16_pair(const TilesF16& a, const TilesF16& b, int64_t T, int32_t ell,
+                                 hipStream_t s) {
+  PrepVParams pv[2]{};
+  int64_t blocks[2];
+  for (int j = 0; j < 2; ++j) {
+    const TilesF16& t = j == 0 ? a : b;
+    PrepVParams& q = pv[j];
+    q.x = t.src;
+    q.ldx = t.ld;
+    q.T = (int32_t)T;
+    q.M = (int32_t)t.K;
+    q.ell = ell;
+    q.nkb = (int32_t)cdiv(t.K, kColBlock);
+    q.n_units = (int64_t)ell * cdiv(T, 16) * q.nkb;
+    q.gamma = t.scale;
+    q.v = t.out;
+    q.v_term = zt_term_halfs(t.K, T);
+    if (q.n_units > INT32_MAX - 4) return hipErrorInvalidValue;
+    blocks[j] = cdiv(q.n_units, 4);
+  }
+  if (blocks[0] + blocks[1] > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_prep_v2, dim3((unsigned)(blocks[0] + blocks[1])), dim3(256), 0, s, pv[0],
+                     pv[1], (int32_t)blocks[0]);
   return hipGetLastError();
 }
 

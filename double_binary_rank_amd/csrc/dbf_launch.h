@@ -126,9 +126,16 @@ hipError_t launch_gemm(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_tile_forward(const ForwardArgs& a, hipStream_t s);
 bool tile_path_fits(const ForwardArgs& a);
 // Token-major fp16 operand tiles (the large-T layout above) of
-// scale_i[k] * src[t][k] for each of ell terms (src fp16 [T][ld], shared).
-hipError_t launch_tiles_f16(const half_t* src, int64_t ld, int64_t T, int64_t K, int32_t ell,
-                            const half_t* scale, half_t* out, hipStream_t s);
+// scale_i[k] * src[t][k] for each of ell terms (src fp16 [T][ld], shared),
+// for two sources in one launch.
+struct TilesF16 {
+  const half_t* src;
+  int64_t ld, K;
+  const half_t* scale;  // [ell][K]
+  half_t* out;
+};
+hipError_t launch_tiles_f16_pair(const TilesF16& a, const TilesF16& b, int64_t T, int32_t ell,
+                                 hipStream_t s);
 // Raw per-term sign products out[i][t][r] = sum_k S[r][k] * tiles_i[t][k]
 // (fp32, [ell][T][ldo]); S is a packed rows x K sign matrix.
 hipError_t launch_sign_product(const uint32_t* S, int64_t rows, int64_t K, int32_t ell, int64_t T,
