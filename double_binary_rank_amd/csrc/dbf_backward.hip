@@ -27,8 +27,9 @@
 // Independent work in one launch over task lists: the two k_tiles_f32; the
 // three column dot products, dx and the four feature-major tiles
 // (k_bwd_mid); the sums of the dot products' chunks and the two dense
-// products (k_bwd_end); the two fp16 tile builds (k_prep_v2): 8 launches per
-// call instead of 21.
+// products (k_bwd_end); the two fp16 tile builds (k_prep_v2); with M = N
+// the sign products two by two (grouped stage 3): 6 launches per call
+// instead of 21 (8 with M != N).
 // Every matrix-core operand is rounded to fp16 once from its exact fp32
 // value, as on the forward large-T path; accumulation is fp32.
 #include "dbf_device.h"
@@ -503,8 +504,14 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   // 1-2: U_i = S2 (gamma_i x), P_i = S1^T (alpha_i G)
   DBF_TRY(launch_tiles_f16_pair(TilesF16{a.x, a.ldx, M, a.gamma, vt},
                                 TilesF16{a.g, a.ldg, N, a.alpha, gt}, T, ell, s));
-  DBF_TRY(launch_sign_product(a.B2, R, M, ell, T, vt, u, lr, s));
-  DBF_TRY(launch_sign_product(a.B1t, R, N, ell, T, gt, pp, lr, s));
+  // with M = N the two products have one shape: one grouped launch
+  const bool square = M == N;
+  if (square) {
+    DBF_TRY(launch_sign_product_pair(a.B2, a.B1t, R, M, ell, T, vt, gt, u, pp, lr, s));
+  } else {
+    DBF_TRY(launch_sign_product(a.B2, R, M, ell, T, vt, u, lr, s));
+    DBF_TRY(launch_sign_product(a.B1t, R, N, ell, T, gt, pp, lr, s));
+  }
   // 3-4: W_i = S1 (beta_i U_i), Q_i = S2^T (beta_i P_i)
   {
     TaskList<TilesF32Params> l;
@@ -515,8 +522,12 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_tiles_f32, dim3((unsigned)l.blocks()), dim3(256), 0, s, l.t);
     DBF_TRY(hipGetLastError());
   }
-  DBF_TRY(launch_sign_product(a.B1, N, R, ell, T, zt, w, ln, s));
-  DBF_TRY(launch_sign_product(a.B2t, M, R, ell, T, pt, q, lm, s));
+  if (square) {
+    DBF_TRY(launch_sign_product_pair(a.B1, a.B2t, N, R, ell, T, zt, pt, w, q, ln, s));
+  } else {
+    DBF_TRY(launch_sign_product(a.B1, N, R, ell, T, zt, w, ln, s));
+    DBF_TRY(launch_sign_product(a.B2t, M, R, ell, T, pt, q, lm, s));
+  }
   // 5-6: the scale gradients, dx and the sign gradients in two launches: the
   // column dot products, dx and the feature-major tiles, then the sums of
   // the dot products' chunks and the dense sign-gradient products.  The

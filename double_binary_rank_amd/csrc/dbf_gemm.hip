@@ -345,7 +345,7 @@ __device__ inline void factors_of(const GemmParams& p, const FactorTab<kLdsAdapt
 template <int STAGE, int NC, bool SPLITK, bool MULTI, bool XIN, int NWV, bool GROUP>
 __global__ __launch_bounds__(64 * NWV) void k_gemm(GemmParams p) {
   static_assert(!XIN || (STAGE == 1 && !MULTI), "x is read in place by single-adapter stage 1");
-  static_assert(!GROUP || (!MULTI && STAGE != 3), "grouped layers take the single-adapter stages");
+  static_assert(!GROUP || !MULTI, "grouped layers take the single-adapter stages");
   static_assert(NWV == 4 || (SPLITK && NC == 2 && NWV == 8), "8 waves only split a reduction");
   constexpr int D = 2;  // operand buffers per wave (deeper rings measured slower)
   constexpr int TPW = 4 * NC / NWV;  // SPLITK: output tiles each wave finishes
@@ -809,7 +809,7 @@ hipError_t launch_one(GemmParams p, hipStream_t s) {
   const bool wide = eight_waves(p);
   if (p.multi) return launch_k<STAGE, NC, SPLITK, true, false, false>(p, grid, false, s);
   if (p.group > 1) {
-    if constexpr (STAGE == 2) return launch_k<2, NC, SPLITK, false, false, true>(p, grid, wide, s);
+    if constexpr (STAGE >= 2) return launch_k<STAGE, NC, SPLITK, false, false, true>(p, grid, wide, s);
     if constexpr (STAGE == 1 && NC == 2) {
       if (p.x != nullptr) return launch_k<1, NC, SPLITK, false, true, true>(p, grid, wide, s);
     }
@@ -874,8 +874,9 @@ hipError_t launch_tiles_f16_pair(const TilesF16& a, const TilesF16& b, int64_t T
   return hipGetLastError();
 }
 
-hipError_t launch_sign_product(const uint32_t* S, int64_t rows, int64_t K, int32_t ell, int64_t T,
-                               const half_t* tiles, float* out, int64_t ldo, hipStream_t s) {
+namespace {
+GemmParams sign_product_params(int64_t rows, int64_t K, int32_t ell, int64_t T, float* out,
+                               int64_t ldo) {
   GemmParams p{};
   p.rows = (int32_t)rows;
   p.K = (int32_t)K;
@@ -889,10 +890,33 @@ hipError_t launch_sign_product(const uint32_t* S, int64_t rows, int64_t K, int32
   p.y = out;
   p.ldy = ldo;
   p.y_term = T * ldo;
-  p.single.B1 = S;
-  p.opnd = tiles;
   p.opnd_term = zt_term_halfs(K, T);
   p.opnd_nkb = p.nkb;
+  return p;
+}
+}  // namespace
+
+hipError_t launch_sign_product(const uint32_t* S, int64_t rows, int64_t K, int32_t ell, int64_t T,
+                               const half_t* tiles, float* out, int64_t ldo, hipStream_t s) {
+  GemmParams p = sign_product_params(rows, K, ell, T, out, ldo);
+  p.single.B1 = S;
+  p.opnd = tiles;
+  return launch_stage<3>(p, s);
+}
+
+hipError_t launch_sign_product_pair(const uint32_t* S0, const uint32_t* S1, int64_t rows,
+                                    int64_t K, int32_t ell, int64_t T, const half_t* tiles0,
+                                    const half_t* tiles1, float* out0, float* out1, int64_t ldo,
+                                    hipStream_t s) {
+  GemmParams p = sign_product_params(rows, K, ell, T, out0, ldo);
+  // the second product as layer 1 of a grouped launch: its operand tiles
+  // and its output at fixed byte offsets from the first's
+  p.group = 2;
+  p.grp[0].B1 = S0;
+  p.grp[1].B1 = S1;
+  p.opnd = tiles0;
+  p.layer_ws = (int64_t)((const char*)tiles1 - (const char*)tiles0);
+  p.y_layer_bytes = (int64_t)((const char*)out1 - (const char*)out0);
   return launch_stage<3>(p, s);
 }
 

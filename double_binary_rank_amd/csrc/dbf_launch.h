@@ -140,6 +140,12 @@ hipError_t launch_tiles_f16_pair(const TilesF16& a, const TilesF16& b, int64_t T
 // (fp32, [ell][T][ldo]); S is a packed rows x K sign matrix.
 hipError_t launch_sign_product(const uint32_t* S, int64_t rows, int64_t K, int32_t ell, int64_t T,
                                const half_t* tiles, float* out, int64_t ldo, hipStream_t s);
+// Two such products of one shape in one launch (S0 with tiles0 into out0, S1
+// with tiles1 into out1).
+hipError_t launch_sign_product_pair(const uint32_t* S0, const uint32_t* S1, int64_t rows,
+                                    int64_t K, int32_t ell, int64_t T, const half_t* tiles0,
+                                    const half_t* tiles1, float* out0, float* out1, int64_t ldo,
+                                    hipStream_t s);
 
 // ------------------------------------------------------------ backward ----
 struct BackwardArgs {

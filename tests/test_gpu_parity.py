@@ -764,7 +764,8 @@ def _run_bwd(L, G, dx_dtype=torch.float32, H1=None, H2=None, tau=None):
 # every reduction's worst case stays below 2^24 and every fp16 operand value
 # below 2048 (x, g in -3..3, unit scales), so the exact result is an fp32 value
 BWD_INT_SHAPES = [(40, 24, 72, 1, 5), (300, 130, 260, 2, 9), (17, 129, 127, 2, 5),
-                  (64, 16, 8, 3, 70), (1, 1, 1, 1, 1), (96, 200, 136, 1, 40), (24, 16, 40, 2, 200)]
+                  (64, 16, 8, 3, 70), (1, 1, 1, 1, 1), (96, 200, 136, 1, 40), (24, 16, 40, 2, 200),
+                  (72, 40, 72, 2, 37), (40, 24, 40, 1, 130)]  # M = N: sign products in pairs
 
 
 @pytest.mark.parametrize("shape", BWD_INT_SHAPES)
@@ -783,7 +784,7 @@ def test_backward_integer_bitexact(shape):
 
 
 BWD_FP_SHAPES = [(300, 130, 260, 2, 37), (64, 16, 8, 3, 70), (96, 200, 136, 1, 300),
-                 (520, 256, 384, 1, 129)]
+                 (520, 256, 384, 1, 129), (264, 130, 264, 2, 45)]
 
 
 @pytest.mark.parametrize("shape", BWD_FP_SHAPES)
