@@ -435,9 +435,11 @@ __global__ __launch_bounds__(64 * kMaW2, 4) void k_ma_stage2(MaParams p) {
           if (p.accumulate)
             for (int v = 0; v < nv; ++v) o[v] += yp[v];
           if (nv == 16) {
+            // y is written once and not read again here: non-temporal
+            // (streamed) stores, measured faster on the 64-adapter batch
 #pragma unroll
             for (int v = 0; v < 16; v += 4)
-              *(v4f*)(yp + v) = v4f{o[v], o[v + 1], o[v + 2], o[v + 3]};
+              __builtin_nontemporal_store(v4f{o[v], o[v + 1], o[v + 2], o[v + 3]}, (v4f*)(yp + v));
           } else {
             for (int v = 0; v < nv; ++v) yp[v] = o[v];
           }
@@ -452,8 +454,8 @@ __global__ __launch_bounds__(64 * kMaW2, 4) void k_ma_stage2(MaParams p) {
               h0[v] = (half_t)o[v];
               h1[v] = (half_t)o[v + 8];
             }
-            *(v8h*)yp = h0;
-            *(v8h*)(yp + 8) = h1;
+            __builtin_nontemporal_store(h0, (v8h*)yp);
+            __builtin_nontemporal_store(h1, (v8h*)(yp + 8));
           } else {
             for (int v = 0; v < nv; ++v) yp[v] = (half_t)o[v];
           }
