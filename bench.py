@@ -880,6 +880,59 @@ def main():
         log(f"device copy {COPY_MIB} MiB: {2 * n / sec / 1e9:.0f} GB/s read + write")
         del src, dst
 
+    # ---- the vendor library's fp16 products on this machine (context only) --
+    # torch's fp16 linear (hipBLASLt): a large square product for the matrix
+    # cores' achievable rate, the dense fp16 layer the factorisation replaces
+    # (4096 x 4096 at T = 256 and T = 1) and a dense product of one stage's
+    # shape (T = 256, 2048 x 4096, i.e. the signs stored as fp16).  Weights
+    # rotate over copies that exceed twice the Infinity Cache, as above.
+    if want("vendor"):
+        F = torch.nn.functional
+        ven = {}
+
+        def linear_case(name, T_, rows, cols, n_copies, calls):
+            g = torch.Generator(device=dev)
+            g.manual_seed(7)
+            a = torch.randn(T_, cols, device=dev, dtype=torch.float16, generator=g)
+            ws_ = [torch.randn(rows, cols, device=dev, dtype=torch.float16, generator=g)
+                   for _ in range(n_copies)]
+            o = torch.empty(T_, rows, device=dev, dtype=torch.float16)
+
+            def f(i):
+                torch.matmul(a, ws_[i % n_copies].t(), out=o)
+
+            sec_eager = time_calls(f, calls, 5) / calls
+            f(n_copies - 1)
+            torch.cuda.synchronize()
+            want_o = o.clone()
+            o.zero_()
+            # the same calls replayed from a HIP graph (free of the host's
+            # launch rate); the last replayed call's result must equal the
+            # eager one
+            try:
+                sec_graph = time_graph(f, n_copies, max(calls // n_copies, 2), 1)
+                same = bool(torch.equal(o, want_o))
+            except RuntimeError as exc:  # capture refused: keep the eager figure
+                log(f"vendor fp16 {name}: no graph replay ({exc})")
+                sec_graph, same = None, False
+            sec = sec_graph if same else sec_eager
+            fl = 2.0 * T_ * rows * cols
+            by = 2.0 * (T_ * cols + rows * cols + T_ * rows)
+            ven[name] = {"T": T_, "rows": rows, "cols": cols, "us_per_call": sec * 1e6,
+                         "us_per_call_eager": sec_eager * 1e6, "graph_replay": same,
+                         "TFLOPs": fl / sec / 1e12, "mfma_frac": fl / sec / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                         "GBs": by / sec / 1e9, "hbm_frac": by / sec / 1e9 / HBM_PEAK_GBS,
+                         "weight_copies": n_copies}
+            log(f"vendor fp16 {name}: {sec * 1e6:.2f} us/call ({'graph' if same else 'eager'}; "
+                f"eager {sec_eager * 1e6:.2f}), {fl / sec / 1e12:.0f} TFLOP/s, {by / sec / 1e9:.0f} GB/s")
+            del a, ws_, o
+
+        linear_case("square_8192", 8192, 8192, 8192, 1, 20)
+        linear_case("dense_layer_4096_T256", 256, 4096, 4096, 16, 64)
+        linear_case("dense_layer_4096_T1", 1, 4096, 4096, 16, 256)
+        linear_case("stage1_shape_dense_T256", 256, 2048, 4096, 32, 64)
+        out["vendor_fp16_linear"] = ven
+
     # ------------------------------------------------------ CPU oracle --
     cpu = None
     cpu_ctx = None
