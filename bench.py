@@ -433,6 +433,49 @@ def main():
         log("phase launches: " + ", ".join(f"{k} {v * 1e6:.2f} us" for k, v in t_ph.items())
             + f"; dominant {dom}: {ach:.1f} TFLOP/s")
 
+    # ---------------- the same layer at longer prefills (T = 1024, 4096) --
+    # calls and each stage alone replayed from HIP graphs over the cold
+    # copies of the signs; parity on a sample of token rows
+    if want("sweep"):
+        sweep = {}
+        for Ts in (1024, 4096):
+            gx = torch.Generator(device=dev)
+            gx.manual_seed(3000 + Ts)
+            xT = torch.randn(Ts, M_, device=dev, dtype=torch.float16, generator=gx)
+            yT = torch.empty((Ts, N_), dtype=torch.float16, device=dev)
+            wsT = torch.empty(dbf.dbf_workspace_bytes(N_, R_, M_, 1, Ts), dtype=torch.uint8,
+                              device=dev)
+
+            def callT(i, ph=None):
+                k = i % n_inst
+                dbf.dbf_forward(xT, B1s[k], B2s[k], pl.alpha, pl.beta, pl.gamma, N_, R_, M_, y=yT,
+                                ws=wsT, phases=ph)
+
+            callT(0)
+            torch.cuda.synchronize()
+            rows = np.linspace(0, Ts - 1, 8).astype(np.int64)
+            xs_h = xT[torch.as_tensor(rows, device=dev)].cpu().numpy()
+            ys_h = yT[torch.as_tensor(rows, device=dev)].float().cpu().numpy()
+            errT = oracle.max_norm_error(ys_h, oracle.forward(xs_h, L.S1, L.S2, L.alpha, L.beta,
+                                                              L.gamma))
+            tT = time_graph(callT, 16, 4, 1)
+            fT = alg_flops(N_, R_, M_, 1, Ts)
+            st = {}
+            for ph in ("stage1", "stage2"):
+                tp = time_graph(lambda i, ph=ph: callT(i, ph), 16, 4, 1)
+                fs = 2.0 * Ts * R_ * (M_ if ph == "stage1" else N_)
+                st[ph] = {"us": tp * 1e6, "TFLOPs": fs / tp / 1e12,
+                          "mfma_frac": fs / tp / 1e12 / MFMA_F16_PEAK_TFLOPS}
+            sweep[f"T{Ts}"] = {"us_per_call_graph": tT * 1e6, "tokens_per_s": Ts / tT,
+                               "TFLOPs": fT / tT / 1e12,
+                               "mfma_frac": fT / tT / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                               "stages": st, "parity_err_8_rows": errT}
+            log(f"prefill T={Ts}: {tT * 1e6:.1f} us/call (graph), {fT / tT / 1e12:.0f} TFLOP/s; "
+                + ", ".join(f"{k} {v['us']:.1f} us = {100 * v['mfma_frac']:.1f} %"
+                            for k, v in st.items()) + f"; err {errT:.2e}")
+            del xT, yT, wsT
+        out["prefill_T_sweep"] = sweep
+
     # ------------------------------------------------------ decode T=1 --
     if want("decode"):
         x1 = x256[:1].contiguous()
@@ -930,6 +973,7 @@ def main():
         linear_case("square_8192", 8192, 8192, 8192, 1, 20)
         linear_case("dense_layer_4096_T256", 256, 4096, 4096, 16, 64)
         linear_case("dense_layer_4096_T1", 1, 4096, 4096, 16, 256)
+        linear_case("dense_layer_4096_T4096", 4096, 4096, 4096, 16, 32)
         linear_case("stage1_shape_dense_T256", 256, 2048, 4096, 32, 64)
         out["vendor_fp16_linear"] = ven
 
