@@ -45,13 +45,23 @@ __all__ = [
 _DTYPE = {torch.int8: _lib.DBF_I8, torch.float16: _lib.DBF_F16, torch.float32: _lib.DBF_F32}
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
-def _ptr(t) -> ctypes.c_void_p:
-    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+def _stream(stream, device: int | None = None) -> int:
+    """The HIP stream handle: the given stream's, else the current stream of
+    ``device`` (the current device when None).  Per call this is the host's
+    hottest step, so the current stream is read as a raw handle without
+    building a Stream object where torch offers that."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device() if device is None else device)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
 
 
 def _row_major(t: torch.Tensor, name: str) -> int:
@@ -116,6 +126,8 @@ _PHASE = {"prep": 8, "stage1": 16, "stage2": 32}
 
 
 def _flags(accumulate: bool, path: str | None, phases=None) -> int:
+    if path is None and phases is None:
+        return _lib.DBF_ACCUMULATE if accumulate else 0
     f = _lib.DBF_ACCUMULATE if accumulate else 0
     if path == "gemv":
         f |= _lib.DBF_PATH_GEMV
@@ -143,9 +155,10 @@ def _out(y, T, N, y_dtype, device):
 
 
 def _ws(ws, N, R, M, ell, T, device):
-    need = dbf_workspace_bytes(N, R, M, ell, T)
+    # (the library checks a given workspace's size itself)
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(dbf_workspace_bytes(N, R, M, ell, T), 16), dtype=torch.uint8,
+                         device=device)
     return ws
 
 
@@ -154,7 +167,7 @@ def _need(t, name, dtype, contiguous=False):
     layout it would misread."""
     if t is None:
         raise ValueError(f"{name} is required")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -177,7 +190,7 @@ def _keep_alive(stream, *tensors):
     """Buffers made here for work on another stream than the current one:
     tell the caching allocator that stream uses them, so their memory is not
     reused before that work has run."""
-    if stream is None or stream == torch.cuda.current_stream():
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
         return
     for t in tensors:
         if t is not None:
@@ -209,7 +222,8 @@ def dbf_forward(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor, alpha: torc
     yt = _DTYPE[y.dtype]
     check(lib.dbf_forward(_ptr(x), ldx, _ptr(B1), _ptr(B2), _ptr(alpha), _ptr(beta), _ptr(gamma),
                           N, R, M, ell, T, _ptr(y), ldy, yt, _flags(accumulate, path, phases), _ptr(ws),
-                          ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward")
+                          ws.nbytes, _stream(stream, x.get_device())),
+          "dbf_forward")
     _keep_alive(stream, y if made_y else None, ws if made_ws else None)
     return y
 
@@ -231,7 +245,7 @@ def dbf_forward_no_alloc(x: torch.Tensor, B1: torch.Tensor, B2: torch.Tensor,
     ldx, ldy = _row_major(x, "x"), _row_major(y, "y")
     check(lib.dbf_forward_no_alloc(_ptr(x), ldx, _ptr(B1), _ptr(B2), _ptr(alpha), _ptr(beta),
                                    _ptr(gamma), N, R, M, ell, T, _ptr(y), ldy, _DTYPE[y.dtype],
-                                   _flags(accumulate, path), _stream(stream)),
+                                   _flags(accumulate, path), _stream(stream, x.get_device())),
           "dbf_forward_no_alloc")
     return y
 
@@ -269,7 +283,7 @@ def dbf_forward_grouped(x: torch.Tensor, layers, *, y: torch.Tensor | None = Non
         _ptr(x), ldx, T, J, arr([p.B1 for p in layers]), arr([p.B2 for p in layers]),
         arr([p.alpha for p in layers]), arr([p.beta for p in layers]),
         arr([p.gamma for p in layers]), N, R, M, ell, _ptr(y), ldy, ys, _DTYPE[y.dtype],
-        _flags(accumulate, path, phases), _ptr(ws), ws.numel() * ws.element_size(),
+        _flags(accumulate, path, phases), _ptr(ws), ws.nbytes,
         _stream(stream)), "dbf_forward_grouped")
     _keep_alive(stream, y if made_y else None, ws if made_ws else None)
     return y
@@ -319,7 +333,7 @@ def dbf_backward(x: torch.Tensor, g: torch.Tensor, B1: torch.Tensor, B2: torch.T
         _ptr(beta), _ptr(gamma), N, R, M, ell, T, _ptr(dx), M, _DTYPE[dx_dtype],
         _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dgamma"]), _ptr(out.get("dS1")),
         _ptr(out.get("dS2")), _ptr(H1), _ptr(H2), 0.0 if tau is None else float(tau),
-        _ptr(out.get("dH1")), _ptr(out.get("dH2")), _ptr(ws), ws.numel() * ws.element_size(),
+        _ptr(out.get("dH1")), _ptr(out.get("dH2")), _ptr(ws), ws.nbytes,
         _stream(stream)), "dbf_backward")
     _keep_alive(stream, *out.values(), ws if made_ws else None)
     return out
@@ -358,7 +372,7 @@ def dbf_factorize(W: torch.Tensor, k: int, omega: torch.Tensor | None = None, *,
     check(lib.dbf_factorize(
         _ptr(W), N, M, ldw, k, _ptr(omega), _ptr(X0), _ptr(Y0), outer, admm_iters, power_iters,
         float(rho0), _ptr(out["S1"]), _ptr(out["S2"]), _ptr(out["alpha"]), _ptr(out["beta"]),
-        _ptr(out["gamma"]), _ptr(out["rel_err"]), _ptr(ws), ws.numel() * ws.element_size(),
+        _ptr(out["gamma"]), _ptr(out["rel_err"]), _ptr(ws), ws.nbytes,
         _stream(stream)), "dbf_factorize")
     _keep_alive(stream, *out.values(), ws if made_ws else None, X0, Y0)
     return out
@@ -397,7 +411,7 @@ def dbf_forward_multi_adapter(x: torch.Tensor, ids: torch.Tensor, B1s: torch.Ten
     check(lib.dbf_forward_multi_adapter(
         _ptr(x), ldx, T, _ptr(ids), num_adapters, _ptr(B1s), _ptr(B2s), _ptr(alphas), _ptr(betas),
         _ptr(gammas), N, R, M, ell, _ptr(y), ldy, yt, _flags(accumulate, path, phases), _ptr(ws),
-        ws.numel() * ws.element_size(), _stream(stream)), "dbf_forward_multi_adapter")
+        ws.nbytes, _stream(stream)), "dbf_forward_multi_adapter")
     _keep_alive(stream, y if made_y else None, ws if made_ws else None)
     return y
 
