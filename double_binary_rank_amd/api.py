@@ -66,9 +66,10 @@ def _ptr(t) -> int:
 
 def _row_major(t: torch.Tensor, name: str) -> int:
     # a size-1 inner dimension may carry any stride
-    if t.dim() != 2 or (t.stride(1) != 1 and t.size(1) != 1):
+    sh, st = t.shape, t.stride()
+    if len(sh) != 2 or (st[1] != 1 and sh[1] != 1):
         raise ValueError(f"{name} must be 2-D with unit inner stride")
-    return max(t.stride(0), t.size(1)) if t.size(0) == 1 else t.stride(0)
+    return max(st[0], sh[1]) if sh[0] == 1 else st[0]
 
 
 def dbf_abi_version() -> int:
@@ -177,8 +178,9 @@ def _need(t, name, dtype, contiguous=False):
 
 
 def _check_scales(alpha, beta, gamma):
-    for name, t in (("alpha", alpha), ("beta", beta), ("gamma", gamma)):
-        _need(t, name, torch.float16, contiguous=True)
+    _need(alpha, "alpha", torch.float16, contiguous=True)
+    _need(beta, "beta", torch.float16, contiguous=True)
+    _need(gamma, "gamma", torch.float16, contiguous=True)
 
 
 def _check_out(y):

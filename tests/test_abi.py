@@ -375,3 +375,31 @@ def test_no_alloc_limit_matches_header():
                   (4096, 6368, 14336, 1, 256), (4096, 64, 4096, 1, 8)):
         assert L.dbf_workspace_bytes(*shape, ctypes.byref(ctypes.c_size_t())) == 0
         assert _lib.workspace_bytes(*shape) <= _lib.NO_ALLOC_SCRATCH_BYTES
+
+
+def test_binding_row_major_and_checks():
+    """The binding's layout and argument checks (host logic, no device)."""
+    import torch
+    from double_binary_rank_amd import api
+    x = torch.zeros(5, 12, dtype=torch.float16)
+    assert api._row_major(x, "x") == 12
+    assert api._row_major(torch.zeros(5, 16)[:, :12], "x") == 16      # padded rows
+    assert api._row_major(torch.zeros(1, 12)[:, :12], "x") == 12
+    assert api._row_major(torch.zeros(4, 16)[1:2, :8], "x") == 16     # one row
+    assert api._row_major(torch.zeros(8).as_strided((1, 8), (1, 1)), "x") == 8  # any row stride
+    assert api._row_major(torch.zeros(3, 8)[:, :1], "x") == 8        # one column: any inner stride
+    with pytest.raises(ValueError):
+        api._row_major(torch.zeros(8, 3).t(), "x")                     # inner stride 3
+    with pytest.raises(ValueError):
+        api._row_major(torch.zeros(2, 3, 4), "x")
+    with pytest.raises(ValueError):
+        api._need(x, "x", torch.float16)                               # not a device tensor
+    with pytest.raises(ValueError):
+        api._need(None, "x", torch.float16)
+    assert api._flags(False, None) == 0
+    assert api._flags(True, None) == 1
+    assert api._flags(False, "gemv", ["prep", "stage2"]) == 2 | 8 | 32
+    with pytest.raises(ValueError):
+        api._flags(False, "nope")
+    with pytest.raises(ValueError):
+        api._flags(False, None, "stage3")
