@@ -927,19 +927,22 @@ def main():
     # torch's fp16 linear (hipBLASLt): a large square product for the matrix
     # cores' achievable rate, the dense fp16 layer the factorisation replaces
     # (4096 x 4096 at T = 256 and T = 1) and a dense product of one stage's
-    # shape (T = 256, 2048 x 4096, i.e. the signs stored as fp16).  Weights
-    # rotate over copies that exceed twice the Infinity Cache, as above.
+    # shape (T = 256, 2048 x 4096, i.e. the signs stored as fp16); and one
+    # fp32 product of the factorisation's size (2048^3).  Weights rotate over
+    # copies that exceed twice the Infinity Cache, as above.
     if want("vendor"):
         F = torch.nn.functional
         ven = {}
 
-        def linear_case(name, T_, rows, cols, n_copies, calls):
+        def linear_case(name, T_, rows, cols, n_copies, calls, dtype=torch.float16):
             g = torch.Generator(device=dev)
             g.manual_seed(7)
-            a = torch.randn(T_, cols, device=dev, dtype=torch.float16, generator=g)
-            ws_ = [torch.randn(rows, cols, device=dev, dtype=torch.float16, generator=g)
+            a = torch.randn(T_, cols, device=dev, dtype=dtype, generator=g)
+            ws_ = [torch.randn(rows, cols, device=dev, dtype=dtype, generator=g)
                    for _ in range(n_copies)]
-            o = torch.empty(T_, rows, device=dev, dtype=torch.float16)
+            o = torch.empty(T_, rows, device=dev, dtype=dtype)
+            esz = a.element_size()
+            peak = MFMA_F16_PEAK_TFLOPS if dtype == torch.float16 else FP32_PEAK_TFLOPS
 
             def f(i):
                 torch.matmul(a, ws_[i % n_copies].t(), out=o)
@@ -956,17 +959,18 @@ def main():
                 sec_graph = time_graph(f, n_copies, max(calls // n_copies, 2), 1)
                 same = bool(torch.equal(o, want_o))
             except RuntimeError as exc:  # capture refused: keep the eager figure
-                log(f"vendor fp16 {name}: no graph replay ({exc})")
+                log(f"vendor {name}: no graph replay ({exc})")
                 sec_graph, same = None, False
             sec = sec_graph if same else sec_eager
             fl = 2.0 * T_ * rows * cols
-            by = 2.0 * (T_ * cols + rows * cols + T_ * rows)
-            ven[name] = {"T": T_, "rows": rows, "cols": cols, "us_per_call": sec * 1e6,
+            by = esz * (T_ * cols + rows * cols + T_ * rows)
+            ven[name] = {"T": T_, "rows": rows, "cols": cols, "dtype": str(dtype).split(".")[-1],
+                         "us_per_call": sec * 1e6,
                          "us_per_call_eager": sec_eager * 1e6, "graph_replay": same,
-                         "TFLOPs": fl / sec / 1e12, "mfma_frac": fl / sec / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                         "TFLOPs": fl / sec / 1e12, "mfma_frac": fl / sec / 1e12 / peak,
                          "GBs": by / sec / 1e9, "hbm_frac": by / sec / 1e9 / HBM_PEAK_GBS,
                          "weight_copies": n_copies}
-            log(f"vendor fp16 {name}: {sec * 1e6:.2f} us/call ({'graph' if same else 'eager'}; "
+            log(f"vendor {name}: {sec * 1e6:.2f} us/call ({'graph' if same else 'eager'}; "
                 f"eager {sec_eager * 1e6:.2f}), {fl / sec / 1e12:.0f} TFLOP/s, {by / sec / 1e9:.0f} GB/s")
             del a, ws_, o
 
@@ -975,6 +979,11 @@ def main():
         linear_case("dense_layer_4096_T1", 1, 4096, 4096, 16, 256)
         linear_case("dense_layer_4096_T4096", 4096, 4096, 4096, 16, 32)
         linear_case("stage1_shape_dense_T256", 256, 2048, 4096, 32, 64)
+        # fp32: the factorisation's products (2048^3, against the fp32 matrix peak)
+        tf32 = torch.backends.cuda.matmul.allow_tf32
+        torch.backends.cuda.matmul.allow_tf32 = False  # full fp32 products
+        linear_case("sgemm_2048_fp32", 2048, 2048, 2048, 1, 20, torch.float32)
+        torch.backends.cuda.matmul.allow_tf32 = tf32
         out["vendor_fp16_linear"] = ven
 
     # ------------------------------------------------------ CPU oracle --
