@@ -31,41 +31,45 @@ namespace {
 // C[m][n] = sum_k A(m,k) B(k,n); A(m,k) = A[m*lda + k] (TA: A[k*lda + m]),
 // B(k,n) = B[k*ldb + n] (TB: B[n*ldb + k]).  fp32 in, fp32 accumulate, on
 // the matrix core (v_mfma_f32_16x16x4_f32: twice the unpacked vector FMA
-// rate).  A workgroup of 4 waves owns a 128 x 128 tile of C, each wave a
-// 64 x 64 quarter as 4 x 4 MFMA tiles.  kMK-deep slices of A and B go
+// rate).  A workgroup of 4 waves owns an MT x MT tile of C (MT = 128 or
+// 64), each wave an MT/2 x MT/2 quarter as 16 x 16 MFMA tiles.  kMK-deep
+// slices of A and B go
 // through LDS, rows padded by 16 floats so that the 4 rows x 16 columns a
 // wave reads per operand hit 64 distinct banks; the next slice is read from
 // memory into registers while the current one is multiplied.
 // MFMA lane layout (16 x 16 x 4): lane l holds A(l % 16, l / 16) and
 // B(l / 16, l % 16); output register r of lane l is C(4 (l / 16) + r, l % 16).
-constexpr int kMT = 128, kMK = 16, kMP = kMT + 16;
-constexpr int kME = kMT * kMK / 256;  // entries of each operand per thread and slice
+constexpr int kMK = 16;
 
-template <bool TA, bool TB>
+template <bool TA, bool TB, int MT>
 __global__ __launch_bounds__(256) void k_sgemm(const float* __restrict__ A, int64_t lda,
                                                const float* __restrict__ B, int64_t ldb,
                                                float* __restrict__ C, int64_t ldc, int32_t Mr,
                                                int32_t Nc, int32_t K) {
-  __shared__ float As[kMK][kMP];  // As[k][m]
-  __shared__ float Bs[kMK][kMP];  // Bs[k][n]
+  constexpr int MP = MT + 16;          // padded LDS row
+  constexpr int ME = MT * kMK / 256;   // entries of each operand per thread and slice
+  constexpr int WT = MT / 2;           // wave tile (2 x 2 waves)
+  constexpr int NI = WT / 16;          // MFMA tiles per wave and dimension
+  __shared__ float As[kMK][MP];  // As[k][m]
+  __shared__ float Bs[kMK][MP];  // Bs[k][n]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n_tn = (Nc + kMT - 1) / kMT;
-  const int m0 = (int)(blockIdx.x / n_tn) * kMT, n0 = (int)(blockIdx.x % n_tn) * kMT;
-  const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
+  const int n_tn = (Nc + MT - 1) / MT;
+  const int m0 = (int)(blockIdx.x / n_tn) * MT, n0 = (int)(blockIdx.x % n_tn) * MT;
+  const int wm = (wv >> 1) * WT, wn = (wv & 1) * WT;
   // entry e of this thread in a slice: consecutive threads take
   // consecutive addresses of the source
   auto a_pos = [&](int e, int& m, int& k) {
     const int id = tid + 256 * e;
-    if (TA) { k = id / kMT; m = id % kMT; } else { m = id / kMK; k = id % kMK; }
+    if (TA) { k = id / MT; m = id % MT; } else { m = id / kMK; k = id % kMK; }
   };
   auto b_pos = [&](int e, int& k, int& n) {
     const int id = tid + 256 * e;
-    if (TB) { n = id / kMK; k = id % kMK; } else { k = id / kMT; n = id % kMT; }
+    if (TB) { n = id / kMK; k = id % kMK; } else { k = id / MT; n = id % MT; }
   };
-  float ra[kME], rb[kME];
+  float ra[ME], rb[ME];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int e = 0; e < kME; ++e) {
+    for (int e = 0; e < ME; ++e) {
       int m, k, kb, n;
       a_pos(e, m, k);
       b_pos(e, kb, n);
@@ -74,16 +78,16 @@ __global__ __launch_bounds__(256) void k_sgemm(const float* __restrict__ A, int6
       rb[e] = (gn < Nc && gkb < K) ? (TB ? B[(int64_t)gn * ldb + gkb] : B[(int64_t)gkb * ldb + gn]) : 0.0f;
     }
   };
-  v4f acc[4][4];
+  v4f acc[NI][NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   fetch(0);
   for (int k0 = 0; k0 < K; k0 += kMK) {
     __syncthreads();  // the previous slice's readers are done
 #pragma unroll
-    for (int e = 0; e < kME; ++e) {
+    for (int e = 0; e < ME; ++e) {
       int m, k, kb, n;
       a_pos(e, m, k);
       b_pos(e, kb, n);
@@ -95,22 +99,22 @@ __global__ __launch_bounds__(256) void k_sgemm(const float* __restrict__ A, int6
 #pragma unroll
     for (int k4 = 0; k4 < kMK / 4; ++k4) {
       const int kk = 4 * k4 + (lane >> 4), c = lane & 15;
-      float a[4], b[4];
+      float a[NI], b[NI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][wm + 16 * i + c];
+      for (int i = 0; i < NI; ++i) a[i] = As[kk][wm + 16 * i + c];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][wn + 16 * j + c];
+      for (int j = 0; j < NI; ++j) b[j] = Bs[kk][wn + 16 * j + c];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NI; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NI; ++j) {
       const int gn = n0 + wn + 16 * j + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -120,13 +124,22 @@ __global__ __launch_bounds__(256) void k_sgemm(const float* __restrict__ A, int6
     }
 }
 
+// 128 x 128 tiles (64 x 64 per wave) when they give at least two workgroups
+// per compute unit; 64 x 64 tiles otherwise, so that a product of a few
+// hundred large tiles still keeps several waves on every SIMD.
 template <bool TA, bool TB>
 hipError_t sgemm(const float* A, int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
                  int64_t Mr, int64_t Nc, int64_t K, hipStream_t s) {
-  const int64_t grid = cdiv(Mr, kMT) * cdiv(Nc, kMT);
+  const int64_t big = cdiv(Mr, 128) * cdiv(Nc, 128);
+  const bool small = big < 2 * 256;
+  const int64_t grid = small ? cdiv(Mr, 64) * cdiv(Nc, 64) : big;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_sgemm<TA, TB>), dim3((unsigned)grid), dim3(256), 0, s, A, lda, B, ldb, C,
-                     ldc, (int32_t)Mr, (int32_t)Nc, (int32_t)K);
+  if (small)
+    hipLaunchKernelGGL((k_sgemm<TA, TB, 64>), dim3((unsigned)grid), dim3(256), 0, s, A, lda, B, ldb,
+                       C, ldc, (int32_t)Mr, (int32_t)Nc, (int32_t)K);
+  else
+    hipLaunchKernelGGL((k_sgemm<TA, TB, 128>), dim3((unsigned)grid), dim3(256), 0, s, A, lda, B,
+                       ldb, C, ldc, (int32_t)Mr, (int32_t)Nc, (int32_t)K);
   return hipGetLastError();
 }
 
